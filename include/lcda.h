@@ -1,0 +1,156 @@
+/* lcda.h - decode-time attention of a few queries against a large cached K/V,
+ * on AMD Instinct MI355X (gfx950).  C ABI of liblcda.so.
+ *
+ * Two paths:
+ *   dense:  cached_attn_lse   - A(q) and alpha(q) against all cached tokens
+ *           lse_merge_local   - exact merge of (A, alpha) with local tokens
+ *   sparse: sig_score_topk    - HashAttention SCORE + TOPK over 32-bit codes
+ *           gather_attn       - attention renormalised over the selected rows
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array pointer is a DEVICE pointer (HIP device memory) unless the
+ *   argument says otherwise.  The caller owns every buffer, including the
+ *   workspace; the library never allocates, frees or synchronises.
+ * - Every call only validates its arguments and enqueues kernels on `stream`
+ *   (a hipStream_t; NULL = the default stream); it returns before the work
+ *   completes.  A device fault surfaces at the caller's next synchronisation.
+ * - Validation happens before any HIP call, so a non-OK status means nothing
+ *   was enqueued (except LCDA_EHIP, reported by the launch itself).
+ * - Buffers must not alias each other.  Array pointers must be 16-byte
+ *   aligned.  Arrays are dense row-major with the shapes given.
+ * - Head dimension d must be 128.  Query head hq reads KV head
+ *   hq / (Hq / Hkv): query heads form contiguous groups of G = Hq / Hkv.
+ * - Scores are s_j = q . k_j / sqrt(d); alpha is a natural logarithm.
+ *   The scale is fixed by the method; there is no scale argument.
+ * - Outputs and alphas are fp32.  q, K and V share one storage type: fp32 or
+ *   bf16 (accumulation is fp32 either way).
+ * - Empty sets (n = 0, count = 0, n_loc = 0 with alpha = -inf) give out = 0
+ *   and alpha = -inf, never NaN.
+ * - The status is an int: LCDA_OK or one of the LCDA_E* codes below; the text
+ *   of the last failure on the calling thread is lcda_last_error().
+ */
+#ifndef LCDA_H
+#define LCDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LCDA_F32 = 0, LCDA_BF16 = 1 } lcda_dtype;
+
+enum {
+    LCDA_OK = 0,
+    LCDA_EINVAL = 1,       /* null required pointer, bad shape, misaligned pointer, cap too small */
+    LCDA_EUNSUPPORTED = 2, /* d != 128, n > INT32_MAX, dtype not fp32/bf16 */
+    LCDA_EWORKSPACE = 3,   /* ws_bytes smaller than the matching lcda_ws_bytes_* */
+    LCDA_EHIP = 4          /* a HIP launch reported an error */
+};
+
+/* Dense attention with log-normalizer.
+ *
+ * Defines, for each batch item b and query head hq with KV head h:
+ *   alpha(q) = log sum_j e^{s_j},   A(q) = sum_j e^{s_j} v_j / sum_j e^{s_j}
+ * over all n cached tokens ("Nectar: Neural Estimation of Cached-Token
+ * Attention via Regression", slide "Two functions separate retrieved content
+ * from mass", Eq. (3.1)).  The sum is split over token ranges and the
+ * partial results combined exactly through their log-normalizers (the
+ * sequence-parallel decode the HashAttention slides compare against).
+ *
+ *   q      [B, Hq, d]                       dtype
+ *   k, v   element (b, h, j, c) at b*kv_batch_stride + (h*n + j)*d + c   dtype
+ *          kv_batch_stride (elements): 0 = one document shared by all B
+ *          items, else >= Hkv*n*d
+ *   out    [B, Hq, d] fp32    A(q)
+ *   alpha  [B, Hq]    fp32    alpha(q)
+ *   ws     workspace of at least lcda_ws_bytes_cached_attn_lse(...) bytes
+ */
+int cached_attn_lse(const void* q, const void* k, const void* v,
+                    int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride,
+                    int dtype, float* out, float* alpha,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Exact merge with the visible local tokens.
+ *
+ * With Z_loc = sum_i e^{s_i} and N_loc = sum_i e^{s_i} v_i over the local
+ * tokens i < n_loc[b]:
+ *   out = (e^alpha A + N_loc) / (e^alpha + Z_loc),  alpha_out = log(e^alpha + Z_loc)
+ * ("Nectar ...", slide "The score makes exact local attention composable",
+ * Eq. (3.4)).  All n_loc[b] local tokens are visible (no mask).
+ *
+ *   q              [B, Hq, d]                 dtype
+ *   a_in, alpha_in [B, Hq, d], [B, Hq]        fp32 (e.g. from cached_attn_lse;
+ *                                             alpha_in = -inf: empty cached part)
+ *   k_loc, v_loc   [B, Hkv, n_loc_max, d]     dtype (private per batch item)
+ *   n_loc          [B] int32, 0 <= n_loc[b] <= n_loc_max; NULL = all n_loc_max
+ *   out            [B, Hq, d] fp32
+ *   alpha_out      [B, Hq] fp32, or NULL
+ * out may not alias a_in.
+ */
+int lse_merge_local(const void* q, const float* a_in, const float* alpha_in,
+                    const void* k_loc, const void* v_loc, const int32_t* n_loc,
+                    int64_t n_loc_max, int B, int Hq, int Hkv, int d, int dtype,
+                    float* out, float* alpha_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* HashAttention SCORE + TOPK.
+ *
+ * SCORE(k_i, q) = -popcount(h_i XOR h_q) over 32-bit codes ("HashAttention:
+ * Semantic Sparsity for Faster Inference", slide "A 32-bit signature makes
+ * scoring cheap", Eq. (2)).  TOPK picks the m positions of highest score
+ * (smallest distance) over all n positions, ties to the lower position, and
+ * unites them with the fixed windows [0, n_sink) and [n - n_recent, n)
+ * (slides "Only selection is approximate; selected KV stay in full form" and
+ * "Token-level sparsity still needs a careful kernel").  Each query head has
+ * its own code and its own selected set I; the G query heads of a group read
+ * the key codes of their KV head once.
+ *
+ *   key_sigs  [B, Hkv, n] uint32
+ *   q_sigs    [B, Hq]     uint32
+ *   idx       [B, Hq, cap] int32: I in ascending order, then -1 up to cap
+ *   cap       >= min(n, m + n_sink + n_recent)
+ *   count     [B, Hq] int32: |I|
+ *   scores    [B, Hq, n] int8 = -distance, or NULL (not needed by the path)
+ */
+int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs,
+                   int B, int Hq, int Hkv, int64_t n, int64_t m, int64_t n_sink,
+                   int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                   int8_t* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* GATHER-ATT: attention over the selected rows only, renormalised over I:
+ *   out = sum_{i in I} e^{s_i} v_i / sum_{j in I} e^{s_j},  alpha = log sum_{j in I} e^{s_j}
+ * ("HashAttention ...", slide "Only selection is approximate; selected KV
+ * stay in full form").  Rows are read straight from the cache by position
+ * (page size 1, no gathered copy).
+ *
+ *   q, k, v, kv_batch_stride   as in cached_attn_lse (n cached tokens)
+ *   idx    [B, Hq, cap] int32, the first count[b,hq] entries in [0, n)
+ *   count  [B, Hq] int32, 0 <= count <= cap
+ *   out    [B, Hq, d] fp32;  alpha [B, Hq] fp32 or NULL
+ * Entries of idx are trusted: positions outside [0, n) are undefined behaviour.
+ */
+int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_stride,
+                const int32_t* idx, const int32_t* count, int64_t cap,
+                int B, int Hq, int Hkv, int d, int64_t n, int dtype,
+                float* out, float* alpha, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes each call needs for the given shapes (0 on invalid shapes). */
+size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n,
+                                     int64_t kv_batch_stride);
+size_t lcda_ws_bytes_lse_merge_local(int B, int Hq, int Hkv, int d, int64_t n_loc_max);
+size_t lcda_ws_bytes_sig_score_topk(int B, int Hq, int Hkv, int64_t n);
+size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap);
+
+/* Text of the last non-OK status returned on the calling thread. */
+const char* lcda_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* lcda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCDA_H */

@@ -1,0 +1,424 @@
+// api.hip - the C ABI of liblcda: argument validation, workspace layout, launch
+// planning and kernel launches on the caller's stream.  Validation finishes
+// before any HIP call.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/lcda.h"
+#include "common.h"
+#include "internal.h"
+
+namespace lcda {
+
+hipError_t launch_split_mfma(const SplitPlan& p, const SplitArgs& a, hipStream_t st);
+hipError_t launch_split_valu(const SplitPlan& p, const SplitArgs& a, int dtype, bool gather, hipStream_t st);
+int valu_step_tokens();
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t elem_bytes(int dtype) { return dtype == LCDA_F32 ? 4 : 2; }
+
+// Shape checks shared by the attention calls.
+int check_heads(const char* fn, int B, int Hq, int Hkv, int d) {
+    if (d != kD) return fail(LCDA_EUNSUPPORTED, "%s: d = %d, only d = 128 is supported", fn, d);
+    if (B < 0) return fail(LCDA_EINVAL, "%s: B = %d < 0", fn, B);
+    if (Hq <= 0 || Hkv <= 0) return fail(LCDA_EINVAL, "%s: Hq = %d, Hkv = %d must be positive", fn, Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(LCDA_EINVAL, "%s: Hq = %d is not a multiple of Hkv = %d", fn, Hq, Hkv);
+    return LCDA_OK;
+}
+
+int check_dtype(const char* fn, int dtype) {
+    if (dtype != LCDA_F32 && dtype != LCDA_BF16)
+        return fail(LCDA_EUNSUPPORTED, "%s: dtype %d is neither LCDA_F32 nor LCDA_BF16", fn, dtype);
+    return LCDA_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, bool required) {
+    if (!p) return required ? fail(LCDA_EINVAL, "%s: %s is NULL", fn, name) : LCDA_OK;
+    if (!aligned16(p)) return fail(LCDA_EINVAL, "%s: %s is not 16-byte aligned", fn, name);
+    return LCDA_OK;
+}
+
+int check_n(const char* fn, const char* name, int64_t n) {
+    if (n < 0) return fail(LCDA_EINVAL, "%s: %s = %lld < 0", fn, name, (long long)n);
+    if (n > INT32_MAX) return fail(LCDA_EUNSUPPORTED, "%s: %s = %lld exceeds INT32_MAX", fn, name, (long long)n);
+    return LCDA_OK;
+}
+
+int check_kv_stride(const char* fn, int64_t stride, int Hkv, int64_t n, int dtype) {
+    if (stride < 0) return fail(LCDA_EINVAL, "%s: kv_batch_stride < 0", fn);
+    if (stride != 0 && stride < (int64_t)Hkv * n * kD)
+        return fail(LCDA_EINVAL, "%s: kv_batch_stride %lld < Hkv*n*d = %lld", fn, (long long)stride,
+                    (long long)((int64_t)Hkv * n * kD));
+    if ((stride * (int64_t)elem_bytes(dtype)) % 16 != 0)
+        return fail(LCDA_EINVAL, "%s: kv_batch_stride*element size is not a multiple of 16 bytes", fn);
+    return LCDA_OK;
+}
+
+struct PartialLayout {
+    size_t ml_off, acc_off, bytes;
+};
+
+PartialLayout partial_layout(int B, int Hq, int splits) {
+    PartialLayout l;
+    const size_t slots = (size_t)B * Hq * splits;
+    l.ml_off = 0;
+    l.acc_off = round_up(slots * sizeof(float2));
+    l.bytes = l.acc_off + round_up(slots * kD * sizeof(float));
+    return l;
+}
+
+#define RETURN_IF(x)          \
+    do {                      \
+        int _s = (x);         \
+        if (_s != LCDA_OK) return _s; \
+    } while (0)
+
+int hip_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(LCDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return LCDA_OK;
+}
+
+struct TopkLayout {
+    int chunks;
+    size_t hist_off, chunk_off, head_off, bytes;
+};
+
+TopkLayout topk_layout(int B, int Hq, int64_t n) {
+    TopkLayout l;
+    const int cl = topk_chunk_len(n);
+    l.chunks = (int)ceil_div(n, cl);
+    const size_t rows = (size_t)B * Hq;
+    l.hist_off = 0;
+    l.chunk_off = round_up(rows * l.chunks * 33 * sizeof(uint32_t));
+    l.head_off = l.chunk_off + round_up(rows * l.chunks * sizeof(int32_t));
+    l.bytes = l.head_off + round_up(rows * sizeof(uint64_t));
+    return l;
+}
+
+}  // namespace
+
+SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared) {
+    SplitPlan p{};
+    const int G = Hq / Hkv;
+    const int rows = shared ? B * G : G;
+    const int bkv = shared ? 1 : B;
+    int units, target;
+    p.waves = 4;
+    if (gather) {
+        p.kernel = kValu;
+        p.nt = 1;
+        p.rows_per_group = 1;
+        p.row_groups = 1;
+        p.block = valu_step_tokens();
+        units = B * Hq;
+        target = 2048;
+        p.grid_y = Hq;
+        p.grid_z = B;
+    } else if (dtype == LCDA_BF16) {
+        p.kernel = kMfma16;
+        p.nt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+        p.rows_per_group = 16 * p.nt;
+        p.row_groups = (int)ceil_div(rows, p.rows_per_group);
+        p.block = 32;
+        units = bkv * Hkv * p.row_groups;
+        target = p.nt == 4 ? 256 : 512;
+        p.grid_y = Hkv;
+        p.grid_z = bkv * p.row_groups;
+    } else {
+        p.kernel = kValu;
+        p.rows_per_group = rows >= 3 ? 4 : rows;
+        p.nt = p.rows_per_group;
+        p.row_groups = (int)ceil_div(rows, p.rows_per_group);
+        p.block = valu_step_tokens();
+        units = bkv * Hkv * p.row_groups;
+        target = 512;
+        p.grid_y = Hkv;
+        p.grid_z = bkv * p.row_groups;
+    }
+    const int64_t nblocks = n_tokens > 0 ? ceil_div(n_tokens, p.block) : 0;
+    const int64_t max_splits = nblocks > 0 ? ceil_div(nblocks, p.waves) : 1;
+    int64_t splits = ceil_div(target, units > 0 ? units : 1);
+    splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+    const int64_t bps = nblocks > 0 ? ceil_div(nblocks, splits) : 1;
+    splits = nblocks > 0 ? ceil_div(nblocks, bps) : 1;
+    p.splits = (int)splits;
+    p.blocks_per_split = (int)bps;
+    p.grid_x = p.splits;
+    return p;
+}
+
+hipError_t launch_split(const SplitPlan& p, const SplitArgs& a, int dtype, hipStream_t st) {
+    if (p.grid_x <= 0 || p.grid_y <= 0 || p.grid_z <= 0) return hipSuccess;
+    if (p.kernel == kMfma16) return launch_split_mfma(p, a, st);
+    return launch_split_valu(p, a, dtype, a.idx != nullptr, st);
+}
+
+}  // namespace lcda
+
+using namespace lcda;
+
+extern "C" {
+
+const char* lcda_last_error(void) { return g_err; }
+
+const char* lcda_version(void) { return "0.1.0"; }
+
+size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride) {
+    if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX) return 0;
+    const SplitPlan p = plan_split(LCDA_BF16, false, B, Hq, Hkv, n, kv_batch_stride == 0);
+    const SplitPlan p32 = plan_split(LCDA_F32, false, B, Hq, Hkv, n, kv_batch_stride == 0);
+    const int s = p.splits > p32.splits ? p.splits : p32.splits;
+    return partial_layout(B, Hq, s).bytes;
+}
+
+size_t lcda_ws_bytes_lse_merge_local(int B, int Hq, int Hkv, int d, int64_t n_loc_max) {
+    return lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n_loc_max, 1);
+}
+
+size_t lcda_ws_bytes_sig_score_topk(int B, int Hq, int Hkv, int64_t n) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX) return 0;
+    return topk_layout(B, Hq, n).bytes;
+}
+
+size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap) {
+    if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || cap < 0 || cap > INT32_MAX) return 0;
+    const SplitPlan p = plan_split(LCDA_BF16, true, B, Hq, Hkv, cap, false);
+    return partial_layout(B, Hq, p.splits).bytes;
+}
+
+int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int d, int64_t n,
+                    int64_t kv_batch_stride, int dtype, float* out, float* alpha, void* ws, size_t ws_bytes,
+                    void* stream) {
+    static const char* fn = "cached_attn_lse";
+    RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
+    RETURN_IF(check_dtype(fn, dtype));
+    RETURN_IF(check_n(fn, "n", n));
+    RETURN_IF(check_kv_stride(fn, kv_batch_stride, Hkv, n, dtype));
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "q", q, work));
+    RETURN_IF(check_ptr(fn, "k", k, work && n > 0));
+    RETURN_IF(check_ptr(fn, "v", v, work && n > 0));
+    RETURN_IF(check_ptr(fn, "out", out, work));
+    RETURN_IF(check_ptr(fn, "alpha", alpha, work));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    const bool shared = kv_batch_stride == 0;
+    const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n, shared);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    if (!work) return LCDA_OK;
+    if (!ws || ws_bytes < lay.bytes)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
+
+    SplitArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kv_batch_stride = kv_batch_stride;
+    a.n = n;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.shared = shared ? 1 : 0;
+    a.rows = shared ? B * a.G : a.G;
+    a.row_groups = p.row_groups;
+    a.splits = p.splits;
+    a.blocks_per_split = p.blocks_per_split;
+    a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
+    a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.scale_log2 = kLog2e / sqrtf((float)kD);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
+    CombineArgs c{};
+    c.ml = a.ml;
+    c.acc = a.acc;
+    c.slots = p.splits;
+    c.rows = B * Hq;
+    c.out = out;
+    c.alpha = alpha;
+    return hip_status(fn, launch_combine(c, st));
+}
+
+int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, const void* k_loc,
+                    const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq, int Hkv, int d,
+                    int dtype, float* out, float* alpha_out, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "lse_merge_local";
+    RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
+    RETURN_IF(check_dtype(fn, dtype));
+    RETURN_IF(check_n(fn, "n_loc_max", n_loc_max));
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "q", q, work));
+    RETURN_IF(check_ptr(fn, "a_in", a_in, work));
+    RETURN_IF(check_ptr(fn, "alpha_in", alpha_in, work));
+    RETURN_IF(check_ptr(fn, "k_loc", k_loc, work && n_loc_max > 0));
+    RETURN_IF(check_ptr(fn, "v_loc", v_loc, work && n_loc_max > 0));
+    RETURN_IF(check_ptr(fn, "n_loc", n_loc, false));
+    RETURN_IF(check_ptr(fn, "out", out, work));
+    RETURN_IF(check_ptr(fn, "alpha_out", alpha_out, false));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    if (work && (const void*)out == (const void*)a_in) return fail(LCDA_EINVAL, "%s: out aliases a_in", fn);
+    const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n_loc_max, false);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    if (!work) return LCDA_OK;
+    if (!ws || ws_bytes < lay.bytes)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
+
+    SplitArgs a{};
+    a.q = q;
+    a.k = k_loc;
+    a.v = v_loc;
+    a.kv_batch_stride = (int64_t)Hkv * n_loc_max * kD;
+    a.n = n_loc_max;
+    a.n_b = n_loc;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.shared = 0;
+    a.rows = a.G;
+    a.row_groups = p.row_groups;
+    a.splits = p.splits;
+    a.blocks_per_split = p.blocks_per_split;
+    a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
+    a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.scale_log2 = kLog2e / sqrtf((float)kD);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
+    CombineArgs c{};
+    c.ml = a.ml;
+    c.acc = a.acc;
+    c.slots = p.splits;
+    c.rows = B * Hq;
+    c.a_in = a_in;
+    c.alpha_in = alpha_in;
+    c.out = out;
+    c.alpha = alpha_out;
+    return hip_status(fn, launch_combine(c, st));
+}
+
+int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int Hq, int Hkv, int64_t n,
+                   int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                   int8_t* scores, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "sig_score_topk";
+    if (B < 0) return fail(LCDA_EINVAL, "%s: B = %d < 0", fn, B);
+    if (Hq <= 0 || Hkv <= 0) return fail(LCDA_EINVAL, "%s: Hq = %d, Hkv = %d must be positive", fn, Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(LCDA_EINVAL, "%s: Hq = %d is not a multiple of Hkv = %d", fn, Hq, Hkv);
+    if (Hq / Hkv > 8) return fail(LCDA_EUNSUPPORTED, "%s: more than 8 query heads per KV head", fn);
+    RETURN_IF(check_n(fn, "n", n));
+    if (m < 0 || n_sink < 0 || n_recent < 0)
+        return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be >= 0", fn);
+    if (cap < 0 || cap > INT32_MAX) return fail(LCDA_EINVAL, "%s: cap = %lld out of range", fn, (long long)cap);
+    const int64_t need = (m + n_sink + n_recent < n) ? m + n_sink + n_recent : n;
+    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX || cap < need)
+        return fail(LCDA_EINVAL, "%s: cap = %lld < min(n, m + n_sink + n_recent) = %lld", fn, (long long)cap,
+                    (long long)need);
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "key_sigs", key_sigs, work && n > 0));
+    RETURN_IF(check_ptr(fn, "q_sigs", q_sigs, work));
+    RETURN_IF(check_ptr(fn, "idx", idx, work && cap > 0));
+    RETURN_IF(check_ptr(fn, "count", count, work));
+    RETURN_IF(check_ptr(fn, "scores", scores, false));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    const TopkLayout lay = topk_layout(B, Hq, n);
+    if (!work) return LCDA_OK;
+    if (!ws || ws_bytes < lay.bytes)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
+    TopkArgs a{};
+    a.key_sigs = key_sigs;
+    a.q_sigs = q_sigs;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.n = n;
+    a.m = m;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.cap = cap;
+    a.idx = idx;
+    a.count = count;
+    a.scores = scores;
+    a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.hist_off);
+    a.chunk_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.chunk_off);
+    a.head_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.head_off);
+    a.chunks = lay.chunks;
+    a.chunk_len = topk_chunk_len(n);
+    return hip_status(fn, launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_stride, const int32_t* idx,
+                const int32_t* count, int64_t cap, int B, int Hq, int Hkv, int d, int64_t n, int dtype, float* out,
+                float* alpha, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "gather_attn";
+    RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
+    RETURN_IF(check_dtype(fn, dtype));
+    RETURN_IF(check_n(fn, "n", n));
+    RETURN_IF(check_n(fn, "cap", cap));
+    RETURN_IF(check_kv_stride(fn, kv_batch_stride, Hkv, n, dtype));
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "q", q, work));
+    RETURN_IF(check_ptr(fn, "k", k, work && n > 0));
+    RETURN_IF(check_ptr(fn, "v", v, work && n > 0));
+    RETURN_IF(check_ptr(fn, "idx", idx, work && cap > 0));
+    RETURN_IF(check_ptr(fn, "count", count, work));
+    RETURN_IF(check_ptr(fn, "out", out, work));
+    RETURN_IF(check_ptr(fn, "alpha", alpha, false));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    const SplitPlan p = plan_split(dtype, true, B, Hq, Hkv, cap, false);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    if (!work) return LCDA_OK;
+    if (!ws || ws_bytes < lay.bytes)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
+    SplitArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kv_batch_stride = kv_batch_stride;
+    a.n = n;
+    a.idx = idx;
+    a.count = count;
+    a.cap = cap;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.shared = kv_batch_stride == 0 ? 1 : 0;
+    a.rows = 1;
+    a.row_groups = 1;
+    a.splits = p.splits;
+    a.blocks_per_split = p.blocks_per_split;
+    a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
+    a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.scale_log2 = kLog2e / sqrtf((float)kD);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (cap == 0 || n == 0) {
+        // Nothing can be selected: every slot is written empty by a zero-length split.
+        a.blocks_per_split = 1;
+    }
+    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
+    CombineArgs c{};
+    c.ml = a.ml;
+    c.acc = a.acc;
+    c.slots = p.splits;
+    c.rows = B * Hq;
+    c.out = out;
+    c.alpha = alpha;
+    return hip_status(fn, launch_combine(c, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// internal.h - host-side launch interfaces between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcda {
+
+// Split attention over token ranges (or over a list of selected positions).
+// Work unit = (KV batch item bkv, KV head h, row group rg); each unit owns
+// `rows` query rows and reads one KV head.  Each unit's tokens are cut into
+// `splits` ranges of `blocks_per_split` blocks; each (unit, split) writes one
+// partial state per row into slot `split` of that row.
+struct SplitArgs {
+    const void* q;              // [B, Hq, d]
+    const void* k;              // cache, element (bkv, h, j, c) at bkv*kv_batch_stride + (h*n + j)*d + c
+    const void* v;
+    int64_t kv_batch_stride;    // elements; 0 = one shared document
+    int64_t n;                  // tokens per KV head in the cache layout
+    const int32_t* n_b;         // per batch item valid length (<= n) or null
+    const int32_t* idx;         // gather mode: [B, Hq, cap] positions; null = dense
+    const int32_t* count;       // gather mode: [B, Hq]
+    int64_t cap;
+    int B, Hq, Hkv, G;
+    int shared;                 // rows of a unit are (b, g) pairs over all b
+    int rows;                   // query rows per (bkv, h)
+    int row_groups;             // ceil(rows / rows_per_group)
+    int splits;                 // slots per query row
+    int blocks_per_split;       // split length in blocks of `block` tokens
+    float2* ml;                 // partial states (see Partials)
+    float* acc;
+    float scale_log2;           // log2(e) / sqrt(d)
+};
+
+// Kernel variants for the split partial.
+enum SplitKernel { kMfma16 = 0, kValu = 1 };
+
+struct SplitPlan {
+    int kernel;       // SplitKernel
+    int nt;           // MFMA: 16-row tiles per wave (1, 2, 4); VALU: rows per group
+    int waves;        // waves per workgroup
+    int block;        // tokens per block (loop step of one wave)
+    int rows_per_group;
+    int row_groups;
+    int splits;
+    int blocks_per_split;
+    int grid_x, grid_y, grid_z;
+};
+
+// Plan for a dense split over a cache of n tokens (gather: over cap positions).
+SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens,
+                     bool shared);
+
+hipError_t launch_split(const SplitPlan& p, const SplitArgs& a, int dtype, hipStream_t st);
+
+// LSE combine of `slots` partial states per row (+ an optional virtual pair
+// (a_in, alpha_in) per row) into out [rows, d] and alpha [rows].
+struct CombineArgs {
+    const float2* ml;
+    const float* acc;
+    int slots;
+    int rows;
+    const float* a_in;       // [rows, d] or null
+    const float* alpha_in;   // [rows] natural log, or null
+    float* out;
+    float* alpha;            // may be null
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// Signature top-k.
+struct TopkArgs {
+    const uint32_t* key_sigs;   // [B, Hkv, n]
+    const uint32_t* q_sigs;     // [B, Hq]
+    int B, Hq, Hkv, G;
+    int64_t n, m, n_sink, n_recent, cap;
+    int32_t* idx;               // [B, Hq, cap]
+    int32_t* count;             // [B, Hq]
+    int8_t* scores;             // [B, Hq, n] or null
+    uint32_t* hist;             // ws: [B, Hq, chunks, 33]
+    int32_t* chunk_info;        // ws: [B, Hq, chunks, 2] (take, offset)
+    int32_t* head_info;         // ws: [B, Hq, 4] (t, ...)
+    int chunks;
+    int chunk_len;
+};
+int topk_chunk_len(int64_t n);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+}  // namespace lcda

@@ -1,0 +1,261 @@
+// split_valu.hip - split attention partials on the vector ALUs, for fp32 or
+// bf16 K/V, over a token range (dense) or over a list of selected positions
+// (GATHER-ATT of "HashAttention: Semantic Sparsity for Faster Inference",
+// slide "Only selection is approximate; selected KV stay in full form":
+// softmax renormalised over the selected set, rows read straight from the
+// cache by position, page size 1, no gathered copy).
+//
+// Partial state per row and slot as in split_mfma.hip (base-2 units).
+//
+// Mapping: 16 lanes share one K/V row, each lane holding 8 consecutive d
+// values (16 B for bf16, 32 B for fp32), so one load instruction reads 4 whole
+// rows; the 4 lane groups of a wave walk interleaved token subsequences, each
+// with its own online softmax, and are merged by cross-lane shuffles at the
+// end.  Dot products are reduced over the 16 lanes of a row by butterflies.
+// Each lane group takes U rows per step and rescales once per step.
+
+#include "common.h"
+#include "internal.h"
+
+namespace lcda {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <typename T>
+struct Row8;
+
+template <>
+struct Row8<float> {
+    u32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = ld16(p);
+        b = ld16(p + 4);
+    }
+    __device__ __forceinline__ void to_float(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = __uint_as_float(a[e]);
+            x[4 + e] = __uint_as_float(b[e]);
+        }
+    }
+};
+
+template <>
+struct Row8<uint16_t> {
+    u32x4 a;
+    __device__ __forceinline__ void load(const uint16_t* p) { a = ld16(p); }
+    __device__ __forceinline__ void to_float(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16_lo(a[e]);
+            x[2 * e + 1] = bf16_hi(a[e]);
+        }
+    }
+};
+
+template <typename T, int R>
+struct ValuSmem {
+    float o[kWaves][R][kD];
+    float2 ml[kWaves][R];
+};
+
+// R: query rows per unit (dense) - 1 in gather mode.  U: rows per lane group per step.
+template <typename T, int R, int U, bool GATHER>
+__global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
+    __shared__ ValuSmem<T, R> sm;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j = lane >> 4, c16 = lane & 15;
+    const int split = blockIdx.x;
+    constexpr int kStep = 4 * U;  // tokens per wave step
+
+    // Unit: dense (bkv, h, rg) over grid (split, h, bkv*row_groups + rg);
+    //       gather (b, hq) over grid (split, hq, b).
+    int bkv, h, rows_base, n_rows;
+    int64_t n_tok;
+    const int32_t* list = nullptr;
+    if (GATHER) {
+        const int hq = blockIdx.y, b = blockIdx.z;
+        h = hq / a.G;
+        bkv = a.shared ? 0 : b;
+        rows_base = 0;
+        n_rows = 1;
+        n_tok = a.count[(int64_t)b * a.Hq + hq];
+        list = a.idx + ((int64_t)b * a.Hq + hq) * a.cap;
+    } else {
+        h = blockIdx.y;
+        bkv = blockIdx.z / a.row_groups;
+        rows_base = (blockIdx.z % a.row_groups) * R;
+        n_rows = min(R, a.rows - rows_base);
+        n_tok = a.n;
+        if (a.n_b) n_tok = min((int64_t)a.n_b[bkv], a.n);
+    }
+    const int64_t head_off = (int64_t)bkv * a.kv_batch_stride + (int64_t)h * a.n * kD;
+    const T* kh = static_cast<const T*>(a.k) + head_off + 8 * c16;
+    const T* vh = static_cast<const T*>(a.v) + head_off + 8 * c16;
+
+    // Query rows of this unit -> (b, hq).
+    auto row_bhq = [&](int r, int& b, int& hq) {
+        if (GATHER) {
+            b = blockIdx.z;
+            hq = blockIdx.y;
+        } else {
+            const int rr = rows_base + r;
+            b = a.shared ? rr / a.G : bkv;
+            hq = h * a.G + (a.shared ? rr % a.G : rr);
+        }
+    };
+
+    float qv[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < n_rows) {
+            int b, hq;
+            row_bhq(r, b, hq);
+            Row8<T> x;
+            x.load(static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + hq) * kD + 8 * c16);
+            x.to_float(qv[r]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[r][e] = 0.f;
+        }
+    }
+
+    float m[R], l[R], acc[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        m[r] = kNoMax;
+        l[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+    }
+
+    const int64_t t_begin = (int64_t)split * a.blocks_per_split * kStep;
+    const int64_t t_end = min(n_tok, t_begin + (int64_t)a.blocks_per_split * kStep);
+
+    for (int64_t t0 = t_begin + (int64_t)w * kStep; t0 < t_end; t0 += (int64_t)kWaves * kStep) {
+        Row8<T> kr[U], vr[U];
+        bool valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = t0 + 4 * u + j;
+            valid[u] = t < t_end;
+            int64_t pos;
+            if (GATHER) pos = valid[u] ? (int64_t)list[t] : (int64_t)list[t0];
+            else pos = valid[u] ? t : t0;
+            kr[u].load(kh + pos * kD);
+            vr[u].load(vh + pos * kD);
+        }
+        float s[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[8];
+            kr[u].to_float(kf);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = fmaf(qv[r][e], kf[e], d);
+                d = sum16(d) * a.scale_log2;
+                s[u][r] = valid[u] ? d : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float bm = s[0][r];
+#pragma unroll
+            for (int u = 1; u < U; ++u) bm = fmaxf(bm, s[u][r]);
+            const float mnew = fmaxf(m[r], bm);
+            const float alpha = fast_exp2(m[r] - mnew);
+            m[r] = mnew;
+            l[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+            vr[u].to_float(vf);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float p = fast_exp2(s[u][r] - m[r]);
+                l[r] += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, vf[e], acc[r][e]);
+            }
+        }
+    }
+
+    // Merge the 4 lane groups of the wave (lanes c16, c16+16, c16+32, c16+48).
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float M = fmaxf(m[r], __shfl_xor(m[r], 16, 64));
+        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        const float wt = fast_exp2(m[r] - M);
+        float L = l[r] * wt;
+        L += __shfl_xor(L, 16, 64);
+        L += __shfl_xor(L, 32, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[r][e] * wt;
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            acc[r][e] = x;
+        }
+        if (j == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.o[w][r][8 * c16 + e] = acc[r][e];
+            if (c16 == 0) sm.ml[w][r] = make_float2(M, L);
+        }
+    }
+    __syncthreads();
+
+    for (int e = threadIdx.x; e < R * kD; e += 64 * kWaves) {
+        const int r = e / kD, c = e % kD;
+        if (r >= n_rows) continue;
+        float M = sm.ml[0][r].x;
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.ml[ww][r].x);
+        float L = 0.f, x = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float wt = fast_exp2(sm.ml[ww][r].x - M);
+            L += wt * sm.ml[ww][r].y;
+            x += wt * sm.o[ww][r][c];
+        }
+        int b, hq;
+        row_bhq(r, b, hq);
+        const int64_t slot = ((int64_t)b * a.Hq + hq) * a.splits + split;
+        a.acc[slot * kD + c] = x;
+        if (c == 0) a.ml[slot] = make_float2(M, L);
+    }
+}
+
+template <typename T, bool GATHER>
+hipError_t launch_t(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
+    dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
+    constexpr int U = 4;
+    if (GATHER) {
+        hipLaunchKernelGGL((k_split_valu<T, 1, U, true>), grid, block, 0, st, a);
+    } else {
+        switch (p.rows_per_group) {
+            case 1: hipLaunchKernelGGL((k_split_valu<T, 1, U, false>), grid, block, 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_split_valu<T, 2, U, false>), grid, block, 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_split_valu<T, 4, U, false>), grid, block, 0, st, a); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int valu_step_tokens() { return 4 * 4; }
+
+hipError_t launch_split_valu(const SplitPlan& p, const SplitArgs& a, int dtype, bool gather, hipStream_t st) {
+    if (dtype == 0) return gather ? launch_t<float, true>(p, a, st) : launch_t<float, false>(p, a, st);
+    return gather ? launch_t<uint16_t, true>(p, a, st) : launch_t<uint16_t, false>(p, a, st);
+}
+
+}  // namespace lcda

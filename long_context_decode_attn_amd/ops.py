@@ -1,0 +1,230 @@
+"""Python binding of liblcda (ctypes): the four C-ABI calls under the same names.
+
+Only argument marshalling happens here: shapes and dtypes are checked, outputs
+and the workspace are allocated with torch on the tensors' device, and the
+call is enqueued on torch's current HIP stream.  Every step of the path runs in
+the HIP kernels of liblcda.so; there is no fallback of any kind: if the library
+is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblcda.so")
+
+LCDA_F32, LCDA_BF16 = 0, 1
+STATUS = {0: "LCDA_OK", 1: "LCDA_EINVAL", 2: "LCDA_EUNSUPPORTED", 3: "LCDA_EWORKSPACE", 4: "LCDA_EHIP"}
+
+# Every symbol include/lcda.h declares.
+EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn",
+           "lcda_ws_bytes_cached_attn_lse", "lcda_ws_bytes_lse_merge_local",
+           "lcda_ws_bytes_sig_score_topk", "lcda_ws_bytes_gather_attn",
+           "lcda_last_error", "lcda_version")
+
+_lib = None
+
+
+class LcdaError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__("%s failed: %s: %s" % (fn, STATUS.get(status, status), text))
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Open liblcda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("liblcda.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m long_context_decode_attn_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.cached_attn_lse.argtypes = [P, P, P, i32, i32, i32, i32, i64, i64, i32, P, P, P, sz, P]
+    lib.lse_merge_local.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, sz, P]
+    lib.sig_score_topk.argtypes = [P, P, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P, P, sz, P]
+    lib.gather_attn.argtypes = [P, P, P, i64, P, P, i64, i32, i32, i32, i32, i64, i32, P, P, P, sz, P]
+    for f in (lib.cached_attn_lse, lib.lse_merge_local, lib.sig_score_topk, lib.gather_attn):
+        f.restype = ctypes.c_int
+    lib.lcda_ws_bytes_cached_attn_lse.argtypes = [i32, i32, i32, i32, i64, i64]
+    lib.lcda_ws_bytes_lse_merge_local.argtypes = [i32, i32, i32, i32, i64]
+    lib.lcda_ws_bytes_sig_score_topk.argtypes = [i32, i32, i32, i64]
+    lib.lcda_ws_bytes_gather_attn.argtypes = [i32, i32, i32, i32, i64]
+    for f in (lib.lcda_ws_bytes_cached_attn_lse, lib.lcda_ws_bytes_lse_merge_local,
+              lib.lcda_ws_bytes_sig_score_topk, lib.lcda_ws_bytes_gather_attn):
+        f.restype = ctypes.c_size_t
+    lib.lcda_last_error.restype = ctypes.c_char_p
+    lib.lcda_last_error.argtypes = []
+    lib.lcda_version.restype = ctypes.c_char_p
+    lib.lcda_version.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise LcdaError(fn, status, load().lcda_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LCDA_F32
+    if t.dtype == torch.bfloat16:
+        return LCDA_BF16
+    raise TypeError("q/K/V must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _ws(nbytes: int, device, ws):
+    if ws is not None:
+        _need(ws.numel() * ws.element_size() >= nbytes, "workspace too small: need %d bytes" % nbytes)
+        return ws
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _as_kv(k: torch.Tensor, B: int):
+    """K/V as [Bkv, Hkv, n, d]; returns (tensor4d, kv_batch_stride in elements)."""
+    if k.dim() == 3:
+        k = k.unsqueeze(0)
+    _need(k.dim() == 4, "K/V must be [B, Hkv, n, d] or [Hkv, n, d]")
+    _need(k.is_contiguous(), "K/V must be contiguous")
+    Bk = k.shape[0]
+    _need(Bk in (1, B), "K/V batch %d must be 1 (shared document) or B = %d" % (Bk, B))
+    stride = 0 if (Bk == 1 and B != 1) else k.shape[1] * k.shape[2] * k.shape[3]
+    return k, stride
+
+
+def ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride) -> int:
+    return int(load().lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride))
+
+
+def ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max) -> int:
+    return int(load().lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max))
+
+
+def ws_bytes_sig_score_topk(B, Hq, Hkv, n) -> int:
+    return int(load().lcda_ws_bytes_sig_score_topk(B, Hq, Hkv, n))
+
+
+def ws_bytes_gather_attn(B, Hq, Hkv, d, cap) -> int:
+    return int(load().lcda_ws_bytes_gather_attn(B, Hq, Hkv, d, cap))
+
+
+def cached_attn_lse(q, k, v, out=None, alpha=None, ws=None):
+    """A(q) [B, Hq, d] fp32 and alpha(q) [B, Hq] fp32 of q [B, Hq, d] against K, V.
+
+    K, V: [B, Hkv, n, d] (one cache per batch item) or [1, Hkv, n, d] (one
+    document shared by all B items)."""
+    lib = load()
+    B, Hq, d = q.shape
+    k, stride = _as_kv(k, B)
+    v, _ = _as_kv(v, B)
+    _need(v.shape == k.shape, "K and V shapes differ")
+    _need(q.is_contiguous() and q.is_cuda and k.device == q.device and v.device == q.device,
+          "q, K, V must be contiguous tensors on one GPU")
+    _need(q.dtype == k.dtype == v.dtype, "q, K, V must share a dtype")
+    Hkv, n = k.shape[1], k.shape[2]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    alpha = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if alpha is None else alpha
+    nb = lib.lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, stride)
+    w = _ws(nb, q.device, ws)
+    st = lib.cached_attn_lse(_p(q), _p(k), _p(v), B, Hq, Hkv, d, n, stride, _dtype_code(q),
+                             _p(out), _p(alpha), _p(w), w.numel() * w.element_size(), _stream(q.device))
+    _check("cached_attn_lse", st)
+    return out, alpha
+
+
+def lse_merge_local(q, a_in, alpha_in, k_loc, v_loc, n_loc=None, out=None, alpha_out=None, ws=None,
+                    want_alpha=True):
+    """Exact merge of (A, alpha) with local tokens k_loc, v_loc [B, Hkv, n_loc_max, d].
+
+    n_loc: int32 tensor [B] on the GPU (None: all n_loc_max tokens visible)."""
+    lib = load()
+    B, Hq, d = q.shape
+    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
+    _need(k_loc.is_contiguous() and v_loc.is_contiguous() and q.is_contiguous(), "inputs must be contiguous")
+    _need(a_in.dtype == torch.float32 and alpha_in.dtype == torch.float32, "a_in, alpha_in must be fp32")
+    _need(q.dtype == k_loc.dtype == v_loc.dtype, "q, k_loc, v_loc must share a dtype")
+    if n_loc is not None:
+        _need(n_loc.dtype == torch.int32 and n_loc.is_cuda and n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
+    Hkv, nmax = k_loc.shape[1], k_loc.shape[2]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    if want_alpha and alpha_out is None:
+        alpha_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nb = lib.lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, nmax)
+    w = _ws(nb, q.device, ws)
+    st = lib.lse_merge_local(_p(q), _p(a_in), _p(alpha_in), _p(k_loc), _p(v_loc), _p(n_loc), nmax, B, Hq, Hkv, d,
+                             _dtype_code(q), _p(out), _p(alpha_out), _p(w), w.numel() * w.element_size(),
+                             _stream(q.device))
+    _check("lse_merge_local", st)
+    return out, alpha_out
+
+
+def capacity(n: int, m: int, n_sink: int, n_recent: int) -> int:
+    return int(min(n, m + n_sink + n_recent))
+
+
+def sig_score_topk(key_sigs, q_sigs, m, n_sink, n_recent, cap=None, want_scores=False, idx=None, count=None,
+                   ws=None):
+    """SCORE + TOPK.  key_sigs [B, Hkv, n], q_sigs [B, Hq] (int32 storage of uint32 codes).
+
+    Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, scores [B, Hq, n] int8 or None)."""
+    lib = load()
+    _need(key_sigs.dtype in (torch.int32, torch.uint32) and q_sigs.dtype == key_sigs.dtype, "signatures must be 32-bit")
+    _need(key_sigs.is_contiguous() and q_sigs.is_contiguous(), "signatures must be contiguous")
+    B, Hkv, n = key_sigs.shape
+    Hq = q_sigs.shape[1]
+    cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
+    dev = key_sigs.device
+    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
+    scores = torch.empty((B, Hq, n), dtype=torch.int8, device=dev) if want_scores else None
+    nb = lib.lcda_ws_bytes_sig_score_topk(B, Hq, Hkv, n)
+    w = _ws(nb, dev, ws)
+    st = lib.sig_score_topk(_p(key_sigs), _p(q_sigs), B, Hq, Hkv, n, int(m), int(n_sink), int(n_recent), _p(idx),
+                            cap, _p(count), _p(scores), _p(w), w.numel() * w.element_size(), _stream(dev))
+    _check("sig_score_topk", st)
+    return idx, count, scores
+
+
+def gather_attn(q, k, v, idx, count, out=None, alpha=None, ws=None, want_alpha=True):
+    """Attention of each query head over its selected positions idx[:, :, :count] only."""
+    lib = load()
+    B, Hq, d = q.shape
+    k, stride = _as_kv(k, B)
+    v, _ = _as_kv(v, B)
+    _need(idx.dtype == torch.int32 and count.dtype == torch.int32, "idx and count must be int32")
+    _need(idx.is_contiguous() and count.is_contiguous() and q.is_contiguous(), "inputs must be contiguous")
+    _need(q.dtype == k.dtype == v.dtype, "q, K, V must share a dtype")
+    Hkv, n = k.shape[1], k.shape[2]
+    cap = idx.shape[2]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    if want_alpha and alpha is None:
+        alpha = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nb = lib.lcda_ws_bytes_gather_attn(B, Hq, Hkv, d, cap)
+    w = _ws(nb, q.device, ws)
+    st = lib.gather_attn(_p(q), _p(k), _p(v), stride, _p(idx), _p(count), cap, B, Hq, Hkv, d, n, _dtype_code(q),
+                         _p(out), _p(alpha), _p(w), w.numel() * w.element_size(), _stream(q.device))
+    _check("gather_attn", st)
+    return out, alpha
+
+
+def version() -> str:
+    return load().lcda_version().decode()

@@ -29,7 +29,8 @@ F32, BF16 = 0, 1
 
 def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
     """Compile an oracle C source with gcc into a shared library (in place)."""
-    if force or not os.path.exists(out):
+    stale = not os.path.exists(out) or os.path.getmtime(src) > os.path.getmtime(out)
+    if force or stale:
         tmp = out + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
                "-Wno-unknown-pragmas", src, "-o", tmp, "-lm"]

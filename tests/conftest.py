@@ -16,5 +16,5 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def orc():
     from oracle import oracle as o
-    o.build(force=True)
+    o.build()
     return o.default()

@@ -1,0 +1,98 @@
+"""The C-ABI library: it loads, exports every symbol include/lcda.h declares, and rejects
+invalid arguments before any HIP call (so these run without a GPU: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_decode_attn_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "lcda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("liblcda.so not built")
+    return ops.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = header_symbols()
+    assert set(syms) == set(ops.EXPORTS), syms
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert lib.lcda_version().decode().count(".") == 2
+
+
+P = ctypes.c_void_p
+
+
+def fake(addr=0x10000):
+    return ctypes.c_void_p(addr)   # aligned non-null pointer that is never dereferenced
+
+
+def call_dense(lib, **kw):
+    a = dict(q=fake(), k=fake(), v=fake(), B=1, Hq=4, Hkv=1, d=128, n=64, stride=0, dtype=1,
+             out=fake(), alpha=fake(), ws=fake(), ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.cached_attn_lse(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["d"], a["n"], a["stride"],
+                               a["dtype"], a["out"], a["alpha"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(d=64), 2, "d = 64"),
+    (dict(Hq=6, Hkv=4), 1, "multiple"),
+    (dict(Hkv=0), 1, "positive"),
+    (dict(B=-1), 1, "B = -1"),
+    (dict(n=-1), 1, "n = -1"),
+    (dict(n=1 << 31), 2, "INT32_MAX"),
+    (dict(dtype=7), 2, "dtype"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(out=ctypes.c_void_p(0x10004)), 1, "aligned"),
+    (dict(stride=100), 1, "kv_batch_stride"),
+    (dict(ws_bytes=16), 3, "workspace"),
+    (dict(ws=None), 3, "workspace"),
+])
+def test_cached_attn_lse_rejects(lib, kw, code, text):
+    assert call_dense(lib, **kw) == code
+    assert text in lib.lcda_last_error().decode()
+
+
+def test_merge_and_topk_and_gather_reject(lib):
+    # lse_merge_local: out aliasing a_in
+    st = lib.lse_merge_local(fake(), fake(0x20000), fake(), fake(), fake(), None, 8, 1, 4, 1, 128, 1,
+                             fake(0x20000), None, fake(), 1 << 30, None)
+    assert st == 1 and "alias" in lib.lcda_last_error().decode()
+    # sig_score_topk: cap too small, negative m, too many heads per group
+    st = lib.sig_score_topk(fake(), fake(), 1, 4, 1, 1000, 10, 2, 2, fake(), 13, fake(), None, fake(), 1 << 30, None)
+    assert st == 1 and "cap" in lib.lcda_last_error().decode()
+    st = lib.sig_score_topk(fake(), fake(), 1, 4, 1, 1000, -1, 2, 2, fake(), 13, fake(), None, fake(), 1 << 30, None)
+    assert st == 1
+    st = lib.sig_score_topk(fake(), fake(), 1, 16, 1, 1000, 10, 2, 2, fake(), 14, fake(), None, fake(), 1 << 30, None)
+    assert st == 2
+    st = lib.sig_score_topk(fake(), fake(), 1, 4, 1, 1000, 10, 2, 2, fake(), 14, fake(), None, fake(), 8, None)
+    assert st == 3
+    # gather_attn: null idx
+    st = lib.gather_attn(fake(), fake(), fake(), 0, None, fake(), 16, 1, 4, 1, 128, 100, 1, fake(), None, fake(),
+                         1 << 30, None)
+    assert st == 1 and "idx" in lib.lcda_last_error().decode()
+
+
+def test_workspace_sizes(lib):
+    assert lib.lcda_ws_bytes_cached_attn_lse(1, 32, 8, 128, 61440, 8 * 61440 * 128) > 0
+    assert lib.lcda_ws_bytes_cached_attn_lse(1, 32, 8, 64, 61440, 0) == 0
+    assert lib.lcda_ws_bytes_sig_score_topk(8, 32, 8, 131072) >= 8 * 32 * 32 * 33 * 4
+    assert lib.lcda_ws_bytes_gather_attn(8, 32, 8, 128, 4352) > 0
+    assert lib.lcda_ws_bytes_lse_merge_local(1, 32, 8, 128, 256) > 0
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert call_dense(lib, B=0, q=None, out=None, alpha=None, ws=None, ws_bytes=0) == 0

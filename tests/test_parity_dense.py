@@ -1,0 +1,164 @@
+"""Dense path on the GPU (through the C ABI) against the CPU oracle, element by element.
+
+cached_attn_lse: A and alpha; lse_merge_local: the exact merge with local tokens.
+Bar: row-normwise relative error <= 2e-3 on outputs and <= 1e-3 absolute on alpha
+for bf16 inputs; 1e-5 / 1e-5 for fp32 inputs (tests/util.py)."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_attn_amd import ops, synth
+from tests.util import assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(B, Hq, Hkv, n, dtype, seed, shared=False, scale_q=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn((B, Hq, 128), generator=g) * scale_q).to(dtype)
+    Bk = 1 if shared else B
+    k = torch.randn((Bk, Hkv, n, 128), generator=g).to(dtype)
+    v = torch.randn((Bk, Hkv, n, 128), generator=g).to(dtype)
+    return q, k, v
+
+
+def _dense_case(B, Hq, Hkv, n, dtype, seed, shared=False, scale_q=1.0, orc=None):
+    q, k, v = _inputs(B, Hq, Hkv, n, dtype, seed, shared, scale_q)
+    print("case dense B=%d Hq=%d Hkv=%d n=%d %s shared=%s" % (B, Hq, Hkv, n, dtype, shared), flush=True)
+    out, alpha = ops.cached_attn_lse(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+    return assert_close(out, alpha, ro, ra, dtype, "dense B=%d Hq=%d Hkv=%d n=%d" % (B, Hq, Hkv, n))
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 127, 128, 129, 1000, 4096, 5003])
+def test_dense_bf16_lengths(orc, n):
+    _dense_case(2, 8, 2, n, torch.bfloat16, 100 + n, orc=orc)
+
+
+@pytest.mark.parametrize("n", [1, 17, 64, 1000, 4096])
+def test_dense_fp32_lengths(orc, n):
+    _dense_case(2, 8, 2, n, torch.float32, 200 + n, orc=orc)
+
+
+@pytest.mark.parametrize("B,G", [(1, 1), (1, 2), (3, 3), (1, 8), (2, 16), (1, 32)])
+def test_dense_gqa_shapes(orc, B, G):
+    _dense_case(B, 2 * G, 2, 700, torch.bfloat16, 300 + B * G, orc=orc)
+    _dense_case(B, 2 * G, 2, 300, torch.float32, 400 + B * G, orc=orc)
+
+
+@pytest.mark.parametrize("B", [2, 4, 5, 8, 16, 20])
+def test_dense_shared_document(orc, B):
+    """One cached document read by B batch items: B*G rows share each KV head (MFMA tiles of 16/32/64 rows)."""
+    _dense_case(B, 8, 2, 3000, torch.bfloat16, 500 + B, shared=True, orc=orc)
+
+
+def test_dense_fp32_shared_document(orc):
+    _dense_case(3, 8, 2, 2000, torch.float32, 600, shared=True, orc=orc)
+
+
+def test_dense_large_logits(orc):
+    """Peaked softmax (|s| up to ~100): exercises the running-max rescale."""
+    _dense_case(2, 8, 2, 3000, torch.bfloat16, 700, scale_q=8.0, orc=orc)
+    _dense_case(1, 4, 1, 3000, torch.float32, 701, scale_q=8.0, orc=orc)
+
+
+def test_dense_increasing_logits(orc):
+    """Logits growing along the sequence force a rescale in almost every block."""
+    B, Hq, Hkv, n = 1, 4, 1, 4000
+    q = torch.zeros((B, Hq, 128))
+    q[..., 0] = 1.0
+    k = torch.randn((B, Hkv, n, 128)) * 0.1
+    k[..., 0] = torch.linspace(0, 400, n)
+    v = torch.randn((B, Hkv, n, 128))
+    for dt in (torch.bfloat16, torch.float32):
+        qq, kk, vv = q.to(dt), k.to(dt), v.to(dt)
+        out, alpha = ops.cached_attn_lse(qq.to(DEV), kk.to(DEV), vv.to(DEV))
+        ro, ra = orc.dense_attn(to_np(qq), to_np(kk), to_np(vv))
+        assert_close(out, alpha, ro, ra, dt, "increasing logits %s" % dt)
+
+
+def test_dense_empty_cache(orc):
+    q, k, v = _inputs(2, 8, 2, 0, torch.bfloat16, 800)
+    out, alpha = ops.cached_attn_lse(q.to(DEV), k.to(DEV), v.to(DEV))
+    assert torch.all(out == 0) and torch.all(torch.isneginf(alpha))
+
+
+def test_dense_config1_tiny_fp32(orc):
+    cfg = synth.CONFIGS[1]
+    x = synth.make_inputs(cfg)
+    out, alpha = ops.cached_attn_lse(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV))
+    ro, ra = orc.dense_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]))
+    assert_close(out, alpha, ro, ra, torch.float32, "config 1")
+    mo, ma = ops.lse_merge_local(x["q"].to(DEV), out, alpha, x["k_loc"].to(DEV), x["v_loc"].to(DEV),
+                                 x["n_loc"].to(DEV))
+    rmo, rma = orc.merge_local(to_np(x["q"]), ro, ra, to_np(x["k_loc"]), to_np(x["v_loc"]), to_np(x["n_loc"]))
+    assert_close(mo, ma, rmo, rma, torch.float32, "config 1 merge")
+
+
+# ------------------------------------------------------------------ merge ----
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_merge_ragged_local(orc, dtype):
+    B, Hq, Hkv, n, nl = 4, 8, 2, 900, 300
+    q, k, v = _inputs(B, Hq, Hkv, n, dtype, 900)
+    g = torch.Generator().manual_seed(901)
+    kl = torch.randn((B, Hkv, nl, 128), generator=g).to(dtype)
+    vl = torch.randn((B, Hkv, nl, 128), generator=g).to(dtype)
+    n_loc = torch.tensor([0, 1, 37, 300], dtype=torch.int32)
+    a, al = ops.cached_attn_lse(q.to(DEV), k.to(DEV), v.to(DEV))
+    mo, ma = ops.lse_merge_local(q.to(DEV), a, al, kl.to(DEV), vl.to(DEV), n_loc.to(DEV))
+    # kernel isolation: the oracle merges the GPU's own (A, alpha)
+    ro, ra = orc.merge_local(to_np(q), a.cpu().numpy(), al.cpu().numpy(), to_np(kl), to_np(vl), n_loc.numpy())
+    assert_close(mo, ma, ro, ra, dtype, "merge (GPU A, alpha)")
+    # end to end against dense attention over the concatenation
+    for b in range(B):
+        kk = torch.cat([k[b:b + 1], kl[b:b + 1, :, :int(n_loc[b])]], dim=2)
+        vv = torch.cat([v[b:b + 1], vl[b:b + 1, :, :int(n_loc[b])]], dim=2)
+        fo, fa = orc.dense_attn(to_np(q[b:b + 1]), to_np(kk), to_np(vv))
+        assert_close(mo[b:b + 1], ma[b:b + 1], fo, fa, dtype, "merge end-to-end b=%d" % b)
+
+
+def test_merge_fed_oracle_state(orc):
+    """lse_merge_local fed the oracle's (A, alpha), so a failure points at the merge alone."""
+    B, Hq, Hkv, n, nl = 2, 8, 2, 500, 256
+    q, k, v = _inputs(B, Hq, Hkv, n, torch.bfloat16, 950)
+    g = torch.Generator().manual_seed(951)
+    kl = torch.randn((B, Hkv, nl, 128), generator=g).to(torch.bfloat16)
+    vl = torch.randn((B, Hkv, nl, 128), generator=g).to(torch.bfloat16)
+    ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+    a = torch.from_numpy(ro.astype(np.float32)).to(DEV)
+    al = torch.from_numpy(ra.astype(np.float32)).to(DEV)
+    mo, ma = ops.lse_merge_local(q.to(DEV), a, al, kl.to(DEV), vl.to(DEV))
+    rmo, rma = orc.merge_local(to_np(q), ro.astype(np.float32), ra.astype(np.float32), to_np(kl), to_np(vl))
+    assert_close(mo, ma, rmo, rma, torch.bfloat16, "merge fed oracle state")
+
+
+def test_merge_empty_sides(orc):
+    B, Hq, Hkv, nl = 2, 8, 2, 64
+    q, kl, vl = _inputs(B, Hq, Hkv, nl, torch.bfloat16, 960)
+    a = torch.zeros((B, Hq, 128), device=DEV)
+    al = torch.full((B, Hq), float("-inf"), device=DEV)
+    mo, ma = ops.lse_merge_local(q.to(DEV), a, al, kl.to(DEV), vl.to(DEV))
+    ro, ra = orc.dense_attn(to_np(q), to_np(kl), to_np(vl))
+    assert_close(mo, ma, ro, ra, torch.bfloat16, "merge with empty cached part")
+    mo, ma = ops.lse_merge_local(q.to(DEV), a, al, kl.to(DEV), vl.to(DEV),
+                                 torch.zeros(B, dtype=torch.int32, device=DEV))
+    assert torch.all(mo == 0) and torch.all(torch.isneginf(ma))
+
+
+# ------------------------------------------------------------- full sizes ----
+def test_config2_full_size(orc):
+    """Qwen3-4B-shaped layer at full size: n = 61,440, 8 KV heads, 32 query heads, 256 local tokens;
+    every output row checked."""
+    cfg = synth.CONFIGS[2]
+    x = synth.make_inputs(cfg)
+    print("case config 2 full size", flush=True)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    a, al = ops.cached_attn_lse(q, k, v)
+    mo, ma = ops.lse_merge_local(q, a, al, x["k_loc"].to(DEV), x["v_loc"].to(DEV), x["n_loc"].to(DEV))
+    torch.cuda.synchronize()
+    ro, ra = orc.dense_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]))
+    assert_close(a, al, ro, ra, torch.bfloat16, "config 2 cached part")
+    rmo, rma = orc.merge_local(to_np(x["q"]), ro, ra, to_np(x["k_loc"]), to_np(x["v_loc"]), to_np(x["n_loc"]))
+    assert_close(mo, ma, rmo, rma, torch.bfloat16, "config 2 merged")

@@ -1,0 +1,157 @@
+"""Sparse path on the GPU (through the C ABI) against the CPU oracle.
+
+sig_score_topk: indices, counts and scores bit-exact.
+gather_attn: same tolerances as the dense path; fed the oracle's indices (kernel
+isolation) and end to end."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_attn_amd import ops, synth
+from tests.util import assert_close, sig_np, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sigs(shape, seed, pool=None):
+    g = np.random.default_rng(seed)
+    if pool:
+        vals = g.integers(0, 2 ** 32, pool, dtype=np.uint64).astype(np.uint32)
+        a = vals[g.integers(0, pool, shape)]
+    else:
+        a = g.integers(0, 2 ** 32, shape, dtype=np.uint64).astype(np.uint32)
+    return torch.from_numpy(a.view(np.int32).copy())
+
+
+def _topk_case(orc, B, Hq, Hkv, n, m, s, r, seed, pool=None, scores=True, cap=None):
+    ks = _sigs((B, Hkv, n), seed, pool)
+    qs = _sigs((B, Hq), seed + 1, pool)
+    print("case topk B=%d Hq=%d Hkv=%d n=%d m=%d s=%d r=%d pool=%s" % (B, Hq, Hkv, n, m, s, r, pool), flush=True)
+    idx, cnt, sc = ops.sig_score_topk(ks.to(DEV), qs.to(DEV), m, s, r, cap=cap, want_scores=scores)
+    torch.cuda.synchronize()
+    ri, rc, rs = orc.sig_score_topk(sig_np(ks), sig_np(qs), m, s, r, cap=cap, want_scores=scores)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    if scores:
+        np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+    return ks, qs, idx, cnt
+
+
+def test_four_bit_example(orc):
+    """HashAttention's illustrative example: query 1011 vs keys 1011 / 1001 / 0110 -> distances 0 / 1 / 3."""
+    ks = torch.tensor([[[0b1011, 0b1001, 0b0110]]], dtype=torch.int32)
+    qs = torch.tensor([[0b1011]], dtype=torch.int32)
+    idx, cnt, sc = ops.sig_score_topk(ks.to(DEV), qs.to(DEV), 2, 0, 0, want_scores=True)
+    assert sc.cpu().tolist() == [[[0, -1, -3]]]
+    assert cnt.item() == 2 and idx.cpu().tolist() == [[[0, 1]]]
+
+
+@pytest.mark.parametrize("n,m,s,r", [
+    (1, 1, 0, 0), (5, 2, 1, 1), (100, 10, 3, 7), (100, 0, 4, 4), (100, 100, 0, 0), (100, 150, 2, 2),
+    (100, 10, 60, 50), (4095, 300, 16, 64), (4096, 300, 16, 64), (4097, 300, 16, 64), (10001, 1000, 128, 128),
+    (20000, 625, 0, 0), (20000, 0, 0, 0), (20000, 19000, 5, 5), (9000, 50, 4100, 20),
+])
+def test_topk_shapes(orc, n, m, s, r):
+    _topk_case(orc, 2, 8, 2, n, m, s, r, 10 + n + m)
+
+
+@pytest.mark.parametrize("pool", [1, 2, 5])
+def test_topk_massive_ties(orc, pool):
+    """Few distinct signatures: almost every position ties; the lower position must win."""
+    _topk_case(orc, 1, 4, 1, 9000, 700, 8, 8, 77 + pool, pool=pool)
+
+
+def test_topk_group_sizes(orc):
+    for G in (1, 2, 3, 5, 8):
+        _topk_case(orc, 1, 2 * G, 2, 5000, 200, 16, 16, 90 + G)
+
+
+def test_topk_larger_cap(orc):
+    ks, qs, idx, cnt = _topk_case(orc, 1, 4, 1, 3000, 100, 10, 10, 55, cap=500)
+    assert np.all(idx.cpu().numpy()[..., cnt.max().item():] == -1)
+
+
+def test_config1_sparse(orc):
+    cfg = synth.CONFIGS[1]
+    x = synth.make_inputs(cfg)
+    idx, cnt, sc = ops.sig_score_topk(x["key_sigs"].to(DEV), x["q_sigs"].to(DEV), cfg.m, cfg.n_sink, cfg.n_recent,
+                                      want_scores=True)
+    ri, rc, rs = orc.sig_score_topk(sig_np(x["key_sigs"]), sig_np(x["q_sigs"]), cfg.m, cfg.n_sink, cfg.n_recent,
+                                    want_scores=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+    out, alpha = ops.gather_attn(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), idx, cnt)
+    ro, ra = orc.gather_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), ri, rc)
+    assert_close(out, alpha, ro, ra, torch.float32, "config 1 gather")
+
+
+# ---------------------------------------------------------------- gather ----
+def _kv(B, Hq, Hkv, n, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, Hq, 128), generator=g).to(dtype)
+    k = torch.randn((B, Hkv, n, 128), generator=g).to(dtype)
+    v = torch.randn((B, Hkv, n, 128), generator=g).to(dtype)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gather_fed_oracle_indices(orc, dtype):
+    B, Hq, Hkv, n = 2, 8, 2, 7000
+    q, k, v = _kv(B, Hq, Hkv, n, dtype, 31)
+    ks = _sigs((B, Hkv, n), 32)
+    qs = _sigs((B, Hq), 33)
+    ri, rc, _ = orc.sig_score_topk(sig_np(ks), sig_np(qs), 400, 20, 30)
+    rc[0, 0] = 0          # an empty selected set
+    rc[1, 3] = 1          # a single row
+    out, alpha = ops.gather_attn(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(ri).to(DEV),
+                                 torch.from_numpy(rc).to(DEV))
+    ro, ra = orc.gather_attn(to_np(q), to_np(k), to_np(v), ri, rc)
+    o = out.cpu().numpy()
+    assert np.all(o[0, 0] == 0) and np.isneginf(alpha[0, 0].item())
+    keep = np.ones((B, Hq), bool)
+    keep[0, 0] = False
+    assert_close(o[keep], alpha.cpu().numpy()[keep], ro[keep], ra[keep], dtype, "gather")
+
+
+def test_gather_full_budget_equals_dense(orc):
+    """m >= n selects every position: GATHER-ATT then equals dense attention."""
+    B, Hq, Hkv, n = 2, 8, 2, 3000
+    q, k, v = _kv(B, Hq, Hkv, n, torch.bfloat16, 41)
+    ks = _sigs((B, Hkv, n), 42)
+    qs = _sigs((B, Hq), 43)
+    idx, cnt, _ = ops.sig_score_topk(ks.to(DEV), qs.to(DEV), n, 0, 0)
+    go, ga = ops.gather_attn(q.to(DEV), k.to(DEV), v.to(DEV), idx, cnt)
+    ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+    assert_close(go, ga, ro, ra, torch.bfloat16, "gather with all positions vs dense")
+
+
+def test_gather_shared_document(orc):
+    B, Hq, Hkv, n = 3, 8, 2, 2000
+    g = torch.Generator().manual_seed(51)
+    q = torch.randn((B, Hq, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, Hkv, n, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, Hkv, n, 128), generator=g).to(torch.bfloat16)
+    ks = _sigs((B, Hkv, n), 52)
+    qs = _sigs((B, Hq), 53)
+    ri, rc, _ = orc.sig_score_topk(sig_np(ks), sig_np(qs), 100, 8, 8)
+    out, alpha = ops.gather_attn(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(ri).to(DEV),
+                                 torch.from_numpy(rc).to(DEV))
+    ro, ra = orc.gather_attn(to_np(q), to_np(k), to_np(v), ri, rc)
+    assert_close(out, alpha, ro, ra, torch.bfloat16, "gather shared document")
+
+
+def test_config4_reduced_end_to_end(orc):
+    """Config 4 recipe (random-projection signatures, m = n/32 + 128 + 128) at n = 16,384, B = 2."""
+    cfg = synth.CONFIGS[4]
+    n = 16384
+    x = synth.make_inputs(cfg, n=n, B=2)
+    m = n // 32
+    idx, cnt, _ = ops.sig_score_topk(x["key_sigs"].to(DEV), x["q_sigs"].to(DEV), m, 128, 128)
+    ri, rc, _ = orc.sig_score_topk(sig_np(x["key_sigs"]), sig_np(x["q_sigs"]), m, 128, 128)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    out, alpha = ops.gather_attn(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), idx, cnt)
+    ro, ra = orc.gather_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), ri, rc)
+    assert_close(out, alpha, ro, ra, torch.bfloat16, "config 4 reduced")
