@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one decode step of the named workload through the HIP library:
+  dense61k    (default) Qwen3-4B-shaped layer: 8 KV heads, 32 query heads, d=128,
+              n=61,440 bf16, batch 1: cached_attn_lse + lse_merge_local (256 local tokens)
+  shared36    36 layers of one shared 61,440-token document, 16 queries, 512 private
+              local tokens each: 36 x (cached_attn_lse + lse_merge_local)
+  sparse128k  HashAttention step: 8 KV heads, 32 query heads, n=131,072 bf16, batch 8,
+              m = n/32 + 128 sink + 128 recent: sig_score_topk + gather_attn
+  needles512k n=524,288 bf16, batch 4, 64 planted needles per head: dense vs sparse (m=n/64)
+
+Inputs are synthetic (seeded, drawn on the GPU) and resident in HBM before the timed
+region.  Several independent input sets are cycled so that the bytes a cycle touches
+exceed the 256 MB last-level cache.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from long_context_decode_attn_amd import ops, synth, traffic  # noqa: E402
+
+HBM_PEAK = 8.0e12   # B/s, MI355X published peak
+METRIC = "decode-attention queries/sec + achieved HBM TB/s (KV+sig bytes) vs ~8 TB/s peak"
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self):
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.s.record()
+
+    def stop_ms(self):
+        self.e.record()
+        self.e.synchronize()
+        return self.s.elapsed_time(self.e)
+
+
+def maybe_graph(fn, use_graph: bool):
+    """Capture fn (a sequence of library calls on the current stream) into a HIP graph."""
+    if not use_graph:
+        return fn
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                          # warm the allocator and the code paths outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g.replay
+
+
+def run_steps(step_fns, steps: int, warmup: int, use_graph: bool) -> float:
+    """Time exactly `steps` steps, step i running step_fns[i % len(step_fns)]; returns ms.
+
+    With use_graph the warmup steps and the timed steps are each captured into one
+    HIP graph (one replay each), so the timed region holds exactly `steps` steps
+    and no per-step host launch."""
+    def seq(count):
+        def f():
+            for i in range(count):
+                step_fns[i % len(step_fns)]()
+        return f
+    warm = maybe_graph(seq(max(warmup, 1)), use_graph)
+    main_ = maybe_graph(seq(steps), use_graph)
+    warm()
+    torch.cuda.synchronize()
+    t = Timer()
+    t.start()
+    main_()
+    ms = t.stop_ms()
+    torch.cuda.synchronize()
+    return ms
+
+
+# ------------------------------------------------------------------ dense ----
+class DenseLayer:
+    """Preallocated inputs/outputs/workspace of cached_attn_lse + lse_merge_local for one input set."""
+
+    def __init__(self, cfg, rot, layer=0, device="cuda"):
+        x = synth.make_inputs(cfg, device=device, rot=rot, layer=layer)
+        self.x = x
+        B, Hq = x["q"].shape[:2]
+        Hkv, n = x["k"].shape[1], x["k"].shape[2]
+        stride = 0 if cfg.shared_doc else Hkv * n * 128
+        self.a = torch.empty((B, Hq, 128), device=device)
+        self.al = torch.empty((B, Hq), device=device)
+        self.o = torch.empty((B, Hq, 128), device=device)
+        self.oa = torch.empty((B, Hq), device=device)
+        nb = max(ops.ws_bytes_cached_attn_lse(B, Hq, Hkv, 128, n, stride),
+                 ops.ws_bytes_lse_merge_local(B, Hq, Hkv, 128, x["k_loc"].shape[2]),
+                 ops.ws_bytes_dense_decode_step(B, Hq, Hkv, 128, n, stride, x["k_loc"].shape[2]))
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+
+    def attn(self):
+        ops.cached_attn_lse(self.x["q"], self.x["k"], self.x["v"], out=self.a, alpha=self.al, ws=self.ws)
+
+    def merge(self):
+        ops.lse_merge_local(self.x["q"], self.a, self.al, self.x["k_loc"], self.x["v_loc"], self.x["n_loc"],
+                            out=self.o, alpha_out=self.oa, ws=self.ws)
+
+    def step_two_calls(self):
+        self.attn()
+        self.merge()
+
+    def step(self):
+        ops.dense_decode_step(self.x["q"], self.x["k"], self.x["v"], self.x["k_loc"], self.x["v_loc"],
+                              self.x["n_loc"], out=self.o, alpha_out=self.oa, ws=self.ws)
+
+
+def bench_dense(args, cfg, layers=1):
+    rot = args.rot if args.rot else (8 if layers == 1 else 1)
+    sets = [[DenseLayer(cfg, r, layer=l) for l in range(layers)] for r in range(rot)]
+    torch.cuda.synchronize()
+    B = cfg.B
+
+    def make(r, what):
+        def f():
+            for L in sets[r]:
+                getattr(L, what)()
+        return f
+
+    steps = args.steps
+    ms_step = run_steps([make(r, "step") for r in range(rot)], steps, args.warmup, args.graph) / steps
+    # the same step as the two separate calls, and the dominant call alone
+    ms_two = run_steps([make(r, "step_two_calls") for r in range(rot)], steps, args.warmup, args.graph) / steps
+    ms_a = run_steps([make(r, "attn") for r in range(rot)], steps, args.warmup, args.graph) / (steps * layers)
+
+    n_loc_total = int(sets[0][0].x["n_loc"].sum().item())
+    step_bytes = layers * traffic.dense_step_bytes(B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, cfg.shared_doc, n_loc_total)
+    attn_bytes = traffic.dense_step_bytes(B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, cfg.shared_doc, 0)
+    achieved = attn_bytes / (ms_a * 1e-3)
+    res = {
+        "value": B / (ms_step * 1e-3),
+        "ms_per_step": ms_step,
+        "steps": steps,
+        "step_bytes": step_bytes,
+        "step_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None,
+                     "kernel": "cached_attn_lse (k_split_mfma + k_combine)",
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": ms_a * 1e3},
+        "rotations": rot,
+        "two_call_ms_per_step": ms_two,
+        "two_call_tbps": step_bytes / (ms_two * 1e-3) / 1e12,
+    }
+    return res, sets[0][0]
+
+
+# ----------------------------------------------------------------- sparse ----
+class SparseSet:
+    def __init__(self, cfg, rot, device="cuda", n=None, B=None):
+        x = synth.make_inputs(cfg, device=device, rot=rot, n=n, B=B)
+        self.x = x
+        self.cfg = cfg
+        B, Hq = x["q"].shape[:2]
+        Hkv, n = x["k"].shape[1], x["k"].shape[2]
+        self.cap = ops.capacity(n, cfg.m, cfg.n_sink, cfg.n_recent)
+        self.idx = torch.zeros((B, Hq, self.cap), dtype=torch.int32, device=device)
+        self.cnt = torch.zeros((B, Hq), dtype=torch.int32, device=device)
+        self.o = torch.empty((B, Hq, 128), device=device)
+        self.oa = torch.empty((B, Hq), device=device)
+        nb = max(ops.ws_bytes_sig_score_topk(B, Hq, Hkv, n), ops.ws_bytes_gather_attn(B, Hq, Hkv, 128, self.cap))
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+
+    def topk(self):
+        c = self.cfg
+        ops.sig_score_topk(self.x["key_sigs"], self.x["q_sigs"], c.m, c.n_sink, c.n_recent, cap=self.cap,
+                           idx=self.idx, count=self.cnt, ws=self.ws)
+
+    def gather(self):
+        ops.gather_attn(self.x["q"], self.x["k"], self.x["v"], self.idx, self.cnt, out=self.o, alpha=self.oa,
+                        ws=self.ws)
+
+    def step(self):
+        self.topk()
+        self.gather()
+
+
+def bench_sparse(args, cfg, rot=None):
+    rot = rot or args.rot or 2
+    sets = [SparseSet(cfg, r) for r in range(rot)]
+    torch.cuda.synchronize()
+
+    steps = args.steps
+    ms_step = run_steps([s.step for s in sets], steps, args.warmup, args.graph) / steps
+    ms_g = run_steps([s.gather for s in sets], steps, args.warmup, args.graph) / steps
+    ms_t = run_steps([s.topk for s in sets], steps, args.warmup, args.graph) / steps
+    G = cfg.Hq // cfg.Hkv
+    uniq = [traffic.unique_rows(s.idx.cpu().numpy(), s.cnt.cpu().numpy(), G) for s in sets]
+    per_head_rows = [int(s.cnt.sum().item()) for s in sets]
+    step_bytes = float(np.mean([traffic.sparse_step_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, s.cap, u)
+                                for s, u in zip(sets, uniq)]))
+    gather_bytes = float(np.mean([u * 2 * cfg.d * 2 for u in uniq]))
+    sig_bytes = cfg.B * cfg.Hkv * cfg.n * 4
+    res = {
+        "value": cfg.B / (ms_step * 1e-3),
+        "ms_per_step": ms_step,
+        "steps": steps,
+        "step_bytes": step_bytes,
+        "step_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
+        "unique_rows": float(np.mean(uniq)),
+        "per_head_rows": float(np.mean(per_head_rows)),
+        "sig_score_topk_us": ms_t * 1e3,
+        "gather_attn_us": ms_g * 1e3,
+        "topk_sig_tbps": sig_bytes / (ms_t * 1e-3) / 1e12,
+        "gather_tbps": gather_bytes / (ms_g * 1e-3) / 1e12,
+        "rotations": rot,
+    }
+    return res, sets[0]
+
+
+# -------------------------------------------------------------- CPU oracle ----
+def cpu_baseline_dense(cfg, seconds: float):
+    """The oracle (plain C, fp64) on the host's cores over whole decode steps of the same workload."""
+    from oracle import oracle as orc_mod
+    orc = orc_mod.default()
+    orc.set_threads(os.cpu_count() or 1)
+    x = synth.make_inputs(cfg, device="cpu")
+
+    def np_(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    q, k, v, kl, vl, nl = (np_(x["q"]), np_(x["k"]), np_(x["v"]), np_(x["k_loc"]), np_(x["v_loc"]),
+                           x["n_loc"].numpy())
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        a, al = orc.dense_attn(q, k, v)
+        orc.merge_local(q, a, al, kl, vl, nl)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": cfg.B * steps / el, "unit": "queries/s", "cores": orc.get_threads(), "kind": "oracle",
+            "sample": "%d full decode step(s) of the same workload (cached_attn_lse + lse_merge_local "
+                      "definitions, fp64), %.1f s wall" % (steps, el)}
+
+
+def cpu_baseline_sparse(cfg, seconds: float, B: int = 1):
+    from oracle import oracle as orc_mod
+    orc = orc_mod.default()
+    orc.set_threads(os.cpu_count() or 1)
+    x = synth.make_inputs(cfg, device="cpu", B=B)
+
+    def np_(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    q, k, v = np_(x["q"]), np_(x["k"]), np_(x["v"])
+    ks = x["key_sigs"].numpy().view(np.uint32)
+    qs = x["q_sigs"].numpy().view(np.uint32)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        idx, cnt, _ = orc.sig_score_topk(ks, qs, cfg.m, cfg.n_sink, cfg.n_recent)
+        orc.gather_attn(q, k, v, idx, cnt)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": B * steps / el, "unit": "queries/s", "cores": orc.get_threads(), "kind": "oracle",
+            "sample": "%d step(s) of %d batch item(s) of the same workload (SCORE+TOPK+GATHER-ATT definitions, "
+                      "fp64), %.1f s wall" % (steps, B, el)}
+
+
+# ------------------------------------------------------------------- main ----
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dense61k", choices=["dense61k", "shared36", "sparse128k", "needles512k"])
+    ap.add_argument("--rot", type=int, default=0, help="input sets cycled (0: workload default)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--no-sparse", dest="sparse", action="store_false",
+                    help="skip the sparse-path measurement that rides along with the dense61k line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run the same kernels "
+              "on its share of KV heads or tokens; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ops.load()
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+
+    line = {"metric": METRIC, "unit": "queries/s", "n_gpus": 1, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16 K/V/q drawn on the GPU)"}
+    launch = "hipGraph" if args.graph else "eager"
+    if args.workload in ("dense61k", "shared36"):
+        cfg = synth.CONFIGS[2 if args.workload == "dense61k" else 3]
+        layers = cfg.layers
+        res, _ = bench_dense(args, cfg, layers)
+        line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"],
+                     "roofline": res["roofline"]})
+        line["config"] = {"workload": args.workload + ": " + cfg.name, "batch": cfg.B, "n": cfg.n, "layers": layers,
+                          "kv_heads": cfg.Hkv, "q_heads": cfg.Hq, "d": cfg.d, "n_loc": cfg.n_loc, "launch": launch,
+                          "rotations": res["rotations"]}
+        line["step"] = "dense_decode_step (cached_attn_lse + lse_merge_local fused into one split pass + one combine)"
+        line["two_call_ms_per_step"] = res["two_call_ms_per_step"]
+        line["two_call_tbps"] = res["two_call_tbps"]
+        line["step_bytes"] = res["step_bytes"]
+        line["step_tbps"] = res["step_tbps"]
+        line["step_frac_of_peak"] = res["step_tbps"] * 1e12 / HBM_PEAK
+        if args.workload == "dense61k" and args.sparse:
+            sres, _ = bench_sparse(args, synth.CONFIGS[4])
+            sres["workload"] = "sparse128k: " + synth.CONFIGS[4].name
+            sres["step_frac_of_peak"] = sres["step_tbps"] * 1e12 / HBM_PEAK
+            line["sparse"] = sres
+        if args.cpu_seconds > 0:
+            line["cpu_baseline"] = cpu_baseline_dense(cfg if layers == 1 else synth.CONFIGS[2], args.cpu_seconds)
+    elif args.workload == "sparse128k":
+        cfg = synth.CONFIGS[4]
+        res, _ = bench_sparse(args, cfg)
+        line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"]})
+        ach = res["gather_tbps"] * 1e12
+        line["roofline"] = {"bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": ach / HBM_PEAK, "traffic": None, "kernel": "gather_attn (unique rows)"}
+        line["config"] = {"workload": "sparse128k: " + cfg.name, "launch": launch}
+        line["detail"] = res
+        if args.cpu_seconds > 0:
+            line["cpu_baseline"] = cpu_baseline_sparse(cfg, args.cpu_seconds)
+    else:
+        raise SystemExit("needles512k: use tests/test_needles.py or DESIGN.md for its report")
+    line["device"] = dev_name
+    line["host"] = platform.node()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -130,12 +130,39 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs,
  *   idx    [B, Hq, cap] int32, the first count[b,hq] entries in [0, n)
  *   count  [B, Hq] int32, 0 <= count <= cap
  *   out    [B, Hq, d] fp32;  alpha [B, Hq] fp32 or NULL
- * Entries of idx are trusted: positions outside [0, n) are undefined behaviour.
+ * Entries of idx outside [0, n) and counts outside [0, cap] are clamped into
+ * range (no out-of-bounds access), and the results for such rows are undefined.
  */
 int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_stride,
                 const int32_t* idx, const int32_t* count, int64_t cap,
                 int B, int Hq, int Hkv, int d, int64_t n, int dtype,
                 float* out, float* alpha, void* ws, size_t ws_bytes, void* stream);
+
+/* Fused dense decode step: cached_attn_lse followed by lse_merge_local, in
+ * one pass where possible.
+ *
+ * out and alpha_out are the attention of q over the cached tokens and the
+ * row's local tokens together, i.e. Eq. (3.4) of "Nectar ..." (slide "The
+ * score makes exact local attention composable") applied to the (A, alpha)
+ * of Eq. (3.1): the same quantities lse_merge_local returns after
+ * cached_attn_lse, up to floating-point summation order.  Because the split
+ * of the softmax sum is exact, the cached and local tokens are treated as one
+ * token range: one split pass and one combine pass.
+ *
+ *   q, k, v, kv_batch_stride, n          as in cached_attn_lse
+ *   k_loc, v_loc, n_loc, n_loc_max       as in lse_merge_local
+ *   out [B, Hq, d], alpha_out [B, Hq] (or NULL)   fp32
+ *   a_doc [B, Hq, d], alpha_doc [B, Hq]  fp32, or both NULL: if given, they
+ *        receive cached_attn_lse's (A, alpha), and the call runs as the two
+ *        separate calls (the same happens for fp32 inputs, for a document
+ *        shared by B > 1 items, and for n = 0)
+ *   ws   at least lcda_ws_bytes_dense_decode_step(...) bytes
+ */
+int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,
+                      const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max,
+                      int B, int Hq, int Hkv, int d, int dtype,
+                      float* out, float* alpha_out, float* a_doc, float* alpha_doc,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes each call needs for the given shapes (0 on invalid shapes). */
 size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n,
@@ -143,12 +170,33 @@ size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n,
 size_t lcda_ws_bytes_lse_merge_local(int B, int Hq, int Hkv, int d, int64_t n_loc_max);
 size_t lcda_ws_bytes_sig_score_topk(int B, int Hq, int Hkv, int64_t n);
 size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap);
+size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n,
+                                       int64_t kv_batch_stride, int64_t n_loc_max);
 
 /* Text of the last non-OK status returned on the calling thread. */
 const char* lcda_last_error(void);
 
 /* Library version, e.g. "0.1.0". */
 const char* lcda_version(void);
+
+/* Launch-shape knobs, for measurement and tuning (process-wide; set them
+ * before enqueuing work, never concurrently with other calls).  They change
+ * how work is split over workgroups, never what is computed.  Workspace sizes
+ * (lcda_ws_bytes_*) follow the current values.  Keys:
+ *   "dense_wgs"      target workgroups of the MFMA split with 16/32-row tiles (256)
+ *   "dense_wgs_nt4"  target workgroups of the MFMA split with 64-row tiles (256)
+ *   "valu_wgs"       target workgroups of the fp32 dense split (512)
+ *   "gather_wgs"     target workgroups of the GATHER-ATT split (2048)
+ *   "direct_blocks"  units with at most this many token blocks run as one split
+ *                    that writes its rows directly, without a combine pass (16)
+ *   "dense_variant"  MFMA split K/V loads (16-row tiles): 0 = nontemporal into
+ *                    registers, 1 = cached into registers, 2 = nontemporal into
+ *                    a two-slot LDS ring per wave (0)
+ *   "gather_variant" GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads (0)
+ * Returns LCDA_EINVAL for an unknown key or a negative (or, except
+ * direct_blocks, zero) value.  lcda_get_tuning returns -1 for an unknown key. */
+int lcda_set_tuning(const char* key, int64_t value);
+int64_t lcda_get_tuning(const char* key);
 
 #ifdef __cplusplus
 }

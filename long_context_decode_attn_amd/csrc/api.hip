@@ -94,6 +94,29 @@ int hip_status(const char* fn, hipError_t e) {
     return LCDA_OK;
 }
 
+// Launch the split pass, then the combine pass unless the plan has a single
+// split (the split kernel then writes the final rows itself).
+int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows, float* out, float* alpha,
+           const float* a_in, const float* alpha_in, hipStream_t st) {
+    a.direct = p.splits == 1 ? 1 : 0;
+    a.out = out;
+    a.alpha = alpha;
+    a.a_in = a_in;
+    a.alpha_in = alpha_in;
+    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
+    if (a.direct) return LCDA_OK;
+    CombineArgs c{};
+    c.ml = a.ml;
+    c.acc = a.acc;
+    c.slots = p.splits;
+    c.rows = rows;
+    c.a_in = a_in;
+    c.alpha_in = alpha_in;
+    c.out = out;
+    c.alpha = alpha;
+    return hip_status(fn, launch_combine(c, st));
+}
+
 struct TopkLayout {
     int chunks;
     size_t hist_off, chunk_off, head_off, bytes;
@@ -113,6 +136,11 @@ TopkLayout topk_layout(int B, int Hq, int64_t n) {
 
 }  // namespace
 
+Tuning& tuning() {
+    static Tuning t;
+    return t;
+}
+
 SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared) {
     SplitPlan p{};
     const int G = Hq / Hkv;
@@ -127,7 +155,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = 1;
         p.block = valu_step_tokens();
         units = B * Hq;
-        target = 2048;
+        target = (int)tuning().gather_wgs;
         p.grid_y = Hq;
         p.grid_z = B;
     } else if (dtype == LCDA_BF16) {
@@ -137,7 +165,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = 32;
         units = bkv * Hkv * p.row_groups;
-        target = p.nt == 4 ? 256 : 512;
+        target = (int)(p.nt == 4 ? tuning().dense_wgs_nt4 : tuning().dense_wgs);
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
     } else {
@@ -147,13 +175,14 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = valu_step_tokens();
         units = bkv * Hkv * p.row_groups;
-        target = 512;
+        target = (int)tuning().valu_wgs;
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
     }
     const int64_t nblocks = n_tokens > 0 ? ceil_div(n_tokens, p.block) : 0;
     const int64_t max_splits = nblocks > 0 ? ceil_div(nblocks, p.waves) : 1;
     int64_t splits = ceil_div(target, units > 0 ? units : 1);
+    if (nblocks <= tuning().direct_blocks) splits = 1;   // short: one split, finished in place
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
     const int64_t bps = nblocks > 0 ? ceil_div(nblocks, splits) : 1;
     splits = nblocks > 0 ? ceil_div(nblocks, bps) : 1;
@@ -178,6 +207,34 @@ extern "C" {
 const char* lcda_last_error(void) { return g_err; }
 
 const char* lcda_version(void) { return "0.1.0"; }
+
+int lcda_set_tuning(const char* key, int64_t value) {
+    if (!key) return fail(LCDA_EINVAL, "lcda_set_tuning: key is NULL");
+    if (value < 0) return fail(LCDA_EINVAL, "lcda_set_tuning: %s = %lld < 0", key, (long long)value);
+    Tuning& t = tuning();
+    if (!strcmp(key, "dense_wgs") && value > 0) t.dense_wgs = value;
+    else if (!strcmp(key, "dense_wgs_nt4") && value > 0) t.dense_wgs_nt4 = value;
+    else if (!strcmp(key, "valu_wgs") && value > 0) t.valu_wgs = value;
+    else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
+    else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
+    else if (!strcmp(key, "dense_variant") && value <= 2) t.dense_variant = value;
+    else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
+    else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
+    return LCDA_OK;
+}
+
+int64_t lcda_get_tuning(const char* key) {
+    if (!key) return -1;
+    const Tuning& t = tuning();
+    if (!strcmp(key, "dense_wgs")) return t.dense_wgs;
+    if (!strcmp(key, "dense_wgs_nt4")) return t.dense_wgs_nt4;
+    if (!strcmp(key, "valu_wgs")) return t.valu_wgs;
+    if (!strcmp(key, "gather_wgs")) return t.gather_wgs;
+    if (!strcmp(key, "direct_blocks")) return t.direct_blocks;
+    if (!strcmp(key, "dense_variant")) return t.dense_variant;
+    if (!strcmp(key, "gather_variant")) return t.gather_variant;
+    return -1;
+}
 
 size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride) {
     if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX) return 0;
@@ -243,15 +300,7 @@ int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, 
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
-    CombineArgs c{};
-    c.ml = a.ml;
-    c.acc = a.acc;
-    c.slots = p.splits;
-    c.rows = B * Hq;
-    c.out = out;
-    c.alpha = alpha;
-    return hip_status(fn, launch_combine(c, st));
+    return finish(fn, p, a, dtype, B * Hq, out, alpha, nullptr, nullptr, st);
 }
 
 int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, const void* k_loc,
@@ -298,17 +347,99 @@ int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, con
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
-    CombineArgs c{};
-    c.ml = a.ml;
-    c.acc = a.acc;
-    c.slots = p.splits;
-    c.rows = B * Hq;
-    c.a_in = a_in;
-    c.alpha_in = alpha_in;
-    c.out = out;
-    c.alpha = alpha_out;
-    return hip_status(fn, launch_combine(c, st));
+    return finish(fn, p, a, dtype, B * Hq, out, alpha_out, a_in, alpha_in, st);
+}
+
+// Fused decode step: one split pass over the unified token range (cache, then
+// the row's local tokens), then one combine.  Falls back to the two calls
+// when the fused form does not apply (fp32, shared document, doc-only outputs
+// requested).
+size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride,
+                                       int64_t n_loc_max) {
+    if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX || n_loc_max < 0 ||
+        n + n_loc_max > INT32_MAX)
+        return 0;
+    // the two-call form needs its own workspace and the doc-only (A, alpha) buffers
+    const size_t two = lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride) +
+                       lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max) +
+                       round_up((size_t)B * Hq * (kD + 1) * sizeof(float));
+    const SplitPlan p = plan_split(LCDA_BF16, false, B, Hq, Hkv, n + n_loc_max, false);
+    const size_t fused = partial_layout(B, Hq, p.splits).bytes;
+    return two > fused ? two : fused;
+}
+
+int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,
+                      const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq,
+                      int Hkv, int d, int dtype, float* out, float* alpha_out, float* a_doc, float* alpha_doc,
+                      void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "dense_decode_step";
+    RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
+    RETURN_IF(check_dtype(fn, dtype));
+    RETURN_IF(check_n(fn, "n", n));
+    RETURN_IF(check_n(fn, "n_loc_max", n_loc_max));
+    RETURN_IF(check_n(fn, "n + n_loc_max", n + n_loc_max));
+    RETURN_IF(check_kv_stride(fn, kv_batch_stride, Hkv, n, dtype));
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "q", q, work));
+    RETURN_IF(check_ptr(fn, "k", k, work && n > 0));
+    RETURN_IF(check_ptr(fn, "v", v, work && n > 0));
+    RETURN_IF(check_ptr(fn, "k_loc", k_loc, work && n_loc_max > 0));
+    RETURN_IF(check_ptr(fn, "v_loc", v_loc, work && n_loc_max > 0));
+    RETURN_IF(check_ptr(fn, "n_loc", n_loc, false));
+    RETURN_IF(check_ptr(fn, "out", out, work));
+    RETURN_IF(check_ptr(fn, "alpha_out", alpha_out, false));
+    RETURN_IF(check_ptr(fn, "a_doc", a_doc, false));
+    RETURN_IF(check_ptr(fn, "alpha_doc", alpha_doc, false));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    if ((a_doc == nullptr) != (alpha_doc == nullptr))
+        return fail(LCDA_EINVAL, "%s: a_doc and alpha_doc must both be given or both be NULL", fn);
+    const size_t need = lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, kv_batch_stride, n_loc_max);
+    if (!work) return LCDA_OK;
+    if (!ws || ws_bytes < need)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, need);
+    const bool shared = kv_batch_stride == 0 && B > 1;
+    if (dtype != LCDA_BF16 || shared || a_doc != nullptr || n == 0) {
+        // Two-call form: cached_attn_lse, then lse_merge_local on its result.
+        char* w = static_cast<char*>(ws);
+        const size_t w1 = lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride);
+        const size_t w2 = lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max);
+        float* A = a_doc;
+        float* al = alpha_doc;
+        if (!A) {
+            A = reinterpret_cast<float*>(w + w1 + w2);
+            al = A + (size_t)B * Hq * kD;
+        }
+        RETURN_IF(cached_attn_lse(q, k, v, B, Hq, Hkv, d, n, kv_batch_stride, dtype, A, al, w, w1, stream));
+        return lse_merge_local(q, A, al, k_loc, v_loc, n_loc, n_loc_max, B, Hq, Hkv, d, dtype, out, alpha_out,
+                               w + w1, w2, stream);
+    }
+    const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n + n_loc_max, false);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    SplitArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kv_batch_stride = kv_batch_stride == 0 ? 0 : kv_batch_stride;
+    a.n = n;
+    a.k2 = k_loc;
+    a.v2 = v_loc;
+    a.n_c = n;
+    a.n2 = n_loc_max;
+    a.kv2_batch_stride = (int64_t)Hkv * n_loc_max * kD;
+    a.n2_b = n_loc;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.shared = 0;
+    a.rows = a.G;
+    a.row_groups = p.row_groups;
+    a.splits = p.splits;
+    a.blocks_per_split = p.blocks_per_split;
+    a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
+    a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.scale_log2 = kLog2e / sqrtf((float)kD);
+    return finish(fn, p, a, dtype, B * Hq, out, alpha_out, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
 int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int Hq, int Hkv, int64_t n,
@@ -406,19 +537,7 @@ int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_st
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (cap == 0 || n == 0) {
-        // Nothing can be selected: every slot is written empty by a zero-length split.
-        a.blocks_per_split = 1;
-    }
-    RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
-    CombineArgs c{};
-    c.ml = a.ml;
-    c.acc = a.acc;
-    c.slots = p.splits;
-    c.rows = B * Hq;
-    c.out = out;
-    c.alpha = alpha;
-    return hip_status(fn, launch_combine(c, st));
+    return finish(fn, p, a, dtype, B * Hq, out, alpha, nullptr, nullptr, st);
 }
 
 }  // extern "C"

@@ -41,8 +41,49 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// Final value of one (row, column) from the merged partial state (M, L, acc)
+// of all its tokens, merged with the optional virtual pair (alpha_in, a_in) -
+// given here as values already read (virt = the pair is present and
+// alpha_in > -inf) - exactly as the combine pass does; used when a row has a
+// single split.  bhq = b*Hq + hq.
+template <typename Args>
+__device__ __forceinline__ void finish_row(const Args& a, int64_t bhq, int c, float M, float L, float acc,
+                                           bool virt, float alpha_in, float a_in) {
+    const bool has = L > 0.f;
+    if (!has && !virt) {
+        a.out[bhq * kD + c] = 0.f;
+        if (a.alpha && c == 0) a.alpha[bhq] = -INFINITY;
+        return;
+    }
+    const float mv = virt ? alpha_in * kLog2e : kNoMax;
+    const float Mx = fmaxf(has ? M : kNoMax, mv);
+    const float w = has ? fast_exp2(M - Mx) : 0.f;
+    const float wv = virt ? fast_exp2(mv - Mx) : 0.f;
+    const float Lx = w * L + wv;
+    float x = w * acc;
+    if (virt) x += wv * a_in;
+    a.out[bhq * kD + c] = x * (1.f / Lx);
+    if (a.alpha && c == 0) a.alpha[bhq] = (Mx + log2f(Lx)) * kLn2;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
+}
+
+// s_waitcnt vmcnt(0): wait for every vector-memory load issued so far (gfx9
+// encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima).  Used to drain
+// a kernel prologue so that a software-pipelined loop starts from a state in
+// which only its own block loads are outstanding.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16-byte load marked nontemporal (streamed once; do not keep in cache).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16s(const void* p) {
+    return NT ? ld16_nt(p) : ld16(p);
 }
 
 }  // namespace lcda

@@ -31,7 +31,35 @@ struct SplitArgs {
     float2* ml;                 // partial states (see Partials)
     float* acc;
     float scale_log2;           // log2(e) / sqrt(d)
+    // Fused cache + local step: tokens j >= n_c of row b come from k2 / v2
+    // (local block, element (b, h, j - n_c, c) at b*kv2_batch_stride +
+    // (h*n2 + j - n_c)*d + c); the row's token count is n_c + n2_b[b] (or + n2).
+    const void* k2;             // null: no second segment
+    const void* v2;
+    int64_t n_c;
+    int64_t n2;
+    int64_t kv2_batch_stride;
+    const int32_t* n2_b;
+    // direct = 1 (one split): the split kernel finishes the rows itself,
+    // merging the optional (a_in, alpha_in) pair, and writes out / alpha.
+    int direct;
+    float* out;                 // [B, Hq, d]
+    float* alpha;               // [B, Hq] or null
+    const float* a_in;          // [B, Hq, d] or null
+    const float* alpha_in;      // [B, Hq] or null
 };
+
+// Launch-shape knobs (process-wide; see lcda_set_tuning).
+struct Tuning {
+    int64_t dense_wgs = 256;       // target workgroups, MFMA split with 16/32-row tiles
+    int64_t dense_wgs_nt4 = 256;   // target workgroups, MFMA split with 64-row tiles
+    int64_t valu_wgs = 512;        // target workgroups, VALU dense split
+    int64_t gather_wgs = 2048;     // target workgroups, GATHER-ATT split
+    int64_t direct_blocks = 16;    // at most this many blocks per unit: one split, no combine pass
+    int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads
+    int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads
+};
+Tuning& tuning();
 
 // Kernel variants for the split partial.
 enum SplitKernel { kMfma16 = 0, kValu = 1 };
@@ -79,7 +107,7 @@ struct TopkArgs {
     int8_t* scores;             // [B, Hq, n] or null
     uint32_t* hist;             // ws: [B, Hq, chunks, 33]
     int32_t* chunk_info;        // ws: [B, Hq, chunks, 2] (take, offset)
-    int32_t* head_info;         // ws: [B, Hq, 4] (t, ...)
+    int32_t* head_info;         // ws: [B, Hq, 2] (t, p + 1)
     int chunks;
     int chunk_len;
 };

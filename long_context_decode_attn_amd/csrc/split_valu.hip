@@ -28,9 +28,10 @@ struct Row8;
 template <>
 struct Row8<float> {
     u32x4 a, b;
+    template <bool NT = false>
     __device__ __forceinline__ void load(const float* p) {
-        a = ld16(p);
-        b = ld16(p + 4);
+        a = ld16s<NT>(p);
+        b = ld16s<NT>(p + 4);
     }
     __device__ __forceinline__ void to_float(float (&x)[8]) const {
 #pragma unroll
@@ -44,7 +45,8 @@ struct Row8<float> {
 template <>
 struct Row8<uint16_t> {
     u32x4 a;
-    __device__ __forceinline__ void load(const uint16_t* p) { a = ld16(p); }
+    template <bool NT = false>
+    __device__ __forceinline__ void load(const uint16_t* p) { a = ld16s<NT>(p); }
     __device__ __forceinline__ void to_float(float (&x)[8]) const {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -61,7 +63,8 @@ struct ValuSmem {
 };
 
 // R: query rows per unit (dense) - 1 in gather mode.  U: rows per lane group per step.
-template <typename T, int R, int U, bool GATHER>
+// NTL: K/V rows are loaded nontemporal.
+template <typename T, int R, int U, bool GATHER, bool NTL>
 __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
     __shared__ ValuSmem<T, R> sm;
     const int lane = threadIdx.x & 63;
@@ -81,7 +84,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
         bkv = a.shared ? 0 : b;
         rows_base = 0;
         n_rows = 1;
-        n_tok = a.count[(int64_t)b * a.Hq + hq];
+        // Counts and positions are clamped to the buffers, so entries outside
+        // the documented ranges give undefined values but never a stray access.
+        n_tok = min(max((int64_t)a.count[(int64_t)b * a.Hq + hq], (int64_t)0), a.cap);
         list = a.idx + ((int64_t)b * a.Hq + hq) * a.cap;
     } else {
         h = blockIdx.y;
@@ -122,6 +127,25 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
         }
     }
 
+    // Direct mode with a (alpha_in, a_in) pair: read the values this thread
+    // will finish now, so their latency hides behind the main loop.
+    constexpr int kFin = (R * kD + 64 * kWaves - 1) / (64 * kWaves);
+    float pre_al[kFin], pre_a[kFin];
+#pragma unroll
+    for (int f = 0; f < kFin; ++f) {
+        pre_al[f] = -INFINITY;
+        pre_a[f] = 0.f;
+        const int e = threadIdx.x + f * 64 * kWaves;
+        const int r = e / kD;
+        if (a.direct && a.alpha_in && e < R * kD && r < n_rows) {
+            int b, hq;
+            row_bhq(r, b, hq);
+            const int64_t bhq = (int64_t)b * a.Hq + hq;
+            pre_al[f] = a.alpha_in[bhq];
+            pre_a[f] = a.a_in[bhq * kD + e % kD];
+        }
+    }
+
     float m[R], l[R], acc[R][8];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -133,32 +157,43 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 
     const int64_t t_begin = (int64_t)split * a.blocks_per_split * kStep;
     const int64_t t_end = min(n_tok, t_begin + (int64_t)a.blocks_per_split * kStep);
+    const int64_t stride = (int64_t)kWaves * kStep;
 
-    for (int64_t t0 = t_begin + (int64_t)w * kStep; t0 < t_end; t0 += (int64_t)kWaves * kStep) {
-        Row8<T> kr[U], vr[U];
-        bool valid[U];
+    // Software pipeline over steps of kStep tokens: the positions (gather mode:
+    // entries of the index list) are requested two steps ahead and the K/V rows
+    // one step ahead of the step being computed.  Requests past the end of the
+    // range are clamped to its last entry (cache-resident) and ignored.
+    struct Step {
+        Row8<T> k[U], v[U];
+    };
+    auto positions = [&](int64_t t0, int32_t (&pos)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = t0 + 4 * u + j;
-            valid[u] = t < t_end;
-            int64_t pos;
-            if (GATHER) pos = valid[u] ? (int64_t)list[t] : (int64_t)list[t0];
-            else pos = valid[u] ? t : t0;
-            kr[u].load(kh + pos * kD);
-            vr[u].load(vh + pos * kD);
+            const int64_t t = min(t0 + 4 * u + j, t_end - 1);
+            pos[u] = GATHER ? min(max(list[t], 0), (int32_t)(a.n - 1)) : (int32_t)t;
         }
+    };
+    auto fetch = [&](Step& st, const int32_t (&pos)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            st.k[u].template load<NTL>(kh + (int64_t)pos[u] * kD);
+            st.v[u].template load<NTL>(vh + (int64_t)pos[u] * kD);
+        }
+    };
+    auto compute = [&](const Step& stp, int64_t t0) {
         float s[U][R];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float kf[8];
-            kr[u].to_float(kf);
+            stp.k[u].to_float(kf);
+            const bool valid = t0 + 4 * u + j < t_end;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) d = fmaf(qv[r][e], kf[e], d);
                 d = sum16(d) * a.scale_log2;
-                s[u][r] = valid[u] ? d : -INFINITY;
+                s[u][r] = valid ? d : -INFINITY;
             }
         }
 #pragma unroll
@@ -176,7 +211,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float vf[8];
-            vr[u].to_float(vf);
+            stp.v[u].to_float(vf);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float p = fast_exp2(s[u][r] - m[r]);
@@ -184,6 +219,27 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, vf[e], acc[r][e]);
             }
+        }
+    };
+
+    int64_t t0 = t_begin + (int64_t)w * kStep;
+    if (t0 < t_end) {
+        int32_t pa[U], pb[U];
+        Step sa, sb;
+        positions(t0, pa);
+        positions(t0 + stride, pb);
+        fetch(sa, pa);
+        while (true) {
+            positions(t0 + 2 * stride, pa);
+            fetch(sb, pb);
+            compute(sa, t0);
+            t0 += stride;
+            if (t0 >= t_end) break;
+            positions(t0 + 2 * stride, pb);
+            fetch(sa, pa);
+            compute(sb, t0);
+            t0 += stride;
+            if (t0 >= t_end) break;
         }
     }
 
@@ -211,9 +267,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
     }
     __syncthreads();
 
-    for (int e = threadIdx.x; e < R * kD; e += 64 * kWaves) {
+#pragma unroll
+    for (int f = 0; f < kFin; ++f) {
+        const int e = threadIdx.x + f * 64 * kWaves;
         const int r = e / kD, c = e % kD;
-        if (r >= n_rows) continue;
+        if (e >= R * kD || r >= n_rows) continue;
         float M = sm.ml[0][r].x;
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.ml[ww][r].x);
@@ -226,9 +284,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
         }
         int b, hq;
         row_bhq(r, b, hq);
-        const int64_t slot = ((int64_t)b * a.Hq + hq) * a.splits + split;
-        a.acc[slot * kD + c] = x;
-        if (c == 0) a.ml[slot] = make_float2(M, L);
+        const int64_t bhq = (int64_t)b * a.Hq + hq;
+        if (a.direct) {
+            finish_row(a, bhq, c, M, L, x, pre_al[f] > -INFINITY, pre_al[f], pre_a[f]);
+        } else {
+            const int64_t slot = bhq * a.splits + split;
+            a.acc[slot * kD + c] = x;
+            if (c == 0) a.ml[slot] = make_float2(M, L);
+        }
     }
 }
 
@@ -237,12 +300,13 @@ hipError_t launch_t(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
     dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
     constexpr int U = 4;
     if (GATHER) {
-        hipLaunchKernelGGL((k_split_valu<T, 1, U, true>), grid, block, 0, st, a);
+        if (tuning().gather_variant == 1) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true>), grid, block, 0, st, a);
     } else {
         switch (p.rows_per_group) {
-            case 1: hipLaunchKernelGGL((k_split_valu<T, 1, U, false>), grid, block, 0, st, a); break;
-            case 2: hipLaunchKernelGGL((k_split_valu<T, 2, U, false>), grid, block, 0, st, a); break;
-            case 4: hipLaunchKernelGGL((k_split_valu<T, 4, U, false>), grid, block, 0, st, a); break;
+            case 1: hipLaunchKernelGGL((k_split_valu<T, 1, U, false, false>), grid, block, 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_split_valu<T, 2, U, false, false>), grid, block, 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_split_valu<T, 4, U, false, false>), grid, block, 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     }

@@ -23,7 +23,8 @@ STATUS = {0: "LCDA_OK", 1: "LCDA_EINVAL", 2: "LCDA_EUNSUPPORTED", 3: "LCDA_EWORK
 EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn",
            "lcda_ws_bytes_cached_attn_lse", "lcda_ws_bytes_lse_merge_local",
            "lcda_ws_bytes_sig_score_topk", "lcda_ws_bytes_gather_attn",
-           "lcda_last_error", "lcda_version")
+           "lcda_last_error", "lcda_version", "lcda_set_tuning", "lcda_get_tuning",
+           "dense_decode_step", "lcda_ws_bytes_dense_decode_step")
 
 _lib = None
 
@@ -61,6 +62,14 @@ def load(path: str = LIB_PATH):
     lib.lcda_last_error.argtypes = []
     lib.lcda_version.restype = ctypes.c_char_p
     lib.lcda_version.argtypes = []
+    lib.dense_decode_step.argtypes = [P, P, P, i64, i64, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.dense_decode_step.restype = ctypes.c_int
+    lib.lcda_ws_bytes_dense_decode_step.argtypes = [i32, i32, i32, i32, i64, i64, i64]
+    lib.lcda_ws_bytes_dense_decode_step.restype = ctypes.c_size_t
+    lib.lcda_set_tuning.argtypes = [ctypes.c_char_p, i64]
+    lib.lcda_set_tuning.restype = ctypes.c_int
+    lib.lcda_get_tuning.argtypes = [ctypes.c_char_p]
+    lib.lcda_get_tuning.restype = i64
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -177,6 +186,38 @@ def lse_merge_local(q, a_in, alpha_in, k_loc, v_loc, n_loc=None, out=None, alpha
     return out, alpha_out
 
 
+def ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, kv_batch_stride, n_loc_max) -> int:
+    return int(load().lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, kv_batch_stride, n_loc_max))
+
+
+def dense_decode_step(q, k, v, k_loc, v_loc, n_loc=None, out=None, alpha_out=None, a_doc=None, alpha_doc=None,
+                      ws=None, want_alpha=True):
+    """cached_attn_lse followed by lse_merge_local, fused into one pass where possible.
+
+    Returns (out, alpha_out); a_doc / alpha_doc (both or neither) receive the cached-only (A, alpha)."""
+    lib = load()
+    B, Hq, d = q.shape
+    k, stride = _as_kv(k, B)
+    v, _ = _as_kv(v, B)
+    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
+    _need(q.is_contiguous() and k_loc.is_contiguous() and v_loc.is_contiguous(), "inputs must be contiguous")
+    _need(q.dtype == k.dtype == v.dtype == k_loc.dtype == v_loc.dtype, "q, K, V, k_loc, v_loc must share a dtype")
+    if n_loc is not None:
+        _need(n_loc.dtype == torch.int32 and n_loc.is_cuda and n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
+    Hkv, n = k.shape[1], k.shape[2]
+    nmax = k_loc.shape[2]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    if want_alpha and alpha_out is None:
+        alpha_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nb = lib.lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, stride, nmax)
+    w = _ws(nb, q.device, ws)
+    st = lib.dense_decode_step(_p(q), _p(k), _p(v), stride, n, _p(k_loc), _p(v_loc), _p(n_loc), nmax, B, Hq, Hkv, d,
+                               _dtype_code(q), _p(out), _p(alpha_out), _p(a_doc), _p(alpha_doc), _p(w),
+                               w.numel() * w.element_size(), _stream(q.device))
+    _check("dense_decode_step", st)
+    return out, alpha_out
+
+
 def capacity(n: int, m: int, n_sink: int, n_recent: int) -> int:
     return int(min(n, m + n_sink + n_recent))
 
@@ -224,6 +265,15 @@ def gather_attn(q, k, v, idx, count, out=None, alpha=None, ws=None, want_alpha=T
                          _p(out), _p(alpha), _p(w), w.numel() * w.element_size(), _stream(q.device))
     _check("gather_attn", st)
     return out, alpha
+
+
+def set_tuning(key: str, value: int) -> None:
+    """Launch-shape knob (see lcda_set_tuning in include/lcda.h)."""
+    _check("lcda_set_tuning", load().lcda_set_tuning(key.encode(), int(value)))
+
+
+def get_tuning(key: str) -> int:
+    return int(load().lcda_get_tuning(key.encode()))
 
 
 def version() -> str:

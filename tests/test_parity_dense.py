@@ -162,3 +162,66 @@ def test_config2_full_size(orc):
     assert_close(a, al, ro, ra, torch.bfloat16, "config 2 cached part")
     rmo, rma = orc.merge_local(to_np(x["q"]), ro, ra, to_np(x["k_loc"]), to_np(x["v_loc"]), to_np(x["n_loc"]))
     assert_close(mo, ma, rmo, rma, torch.bfloat16, "config 2 merged")
+
+
+# ------------------------------------------------------ fused decode step ----
+def _step_case(orc, B, Hq, Hkv, n, nl_max, n_loc, dtype, seed, shared=False, doc=False):
+    q, k, v = _inputs(B, Hq, Hkv, n, dtype, seed, shared)
+    g = torch.Generator().manual_seed(seed + 1)
+    kl = torch.randn((B, Hkv, nl_max, 128), generator=g).to(dtype)
+    vl = torch.randn((B, Hkv, nl_max, 128), generator=g).to(dtype)
+    nlt = torch.tensor(n_loc, dtype=torch.int32)
+    print("case step B=%d Hq=%d Hkv=%d n=%d n_loc=%s %s shared=%s doc=%s" % (B, Hq, Hkv, n, n_loc, dtype, shared, doc),
+          flush=True)
+    a_doc = torch.empty((B, Hq, 128), device=DEV) if doc else None
+    al_doc = torch.empty((B, Hq), device=DEV) if doc else None
+    out, alpha = ops.dense_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), kl.to(DEV), vl.to(DEV), nlt.to(DEV),
+                                       a_doc=a_doc, alpha_doc=al_doc)
+    torch.cuda.synchronize()
+    ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+    mo, ma = orc.merge_local(to_np(q), ro, ra, to_np(kl), to_np(vl), nlt.numpy())
+    assert_close(out, alpha, mo, ma, dtype, "decode step")
+    if doc:
+        assert_close(a_doc, al_doc, ro, ra, dtype, "decode step doc-only part")
+
+
+@pytest.mark.parametrize("n,n_loc", [(61440 // 16, [256]), (1000, [0, 17, 256]), (31, [5, 40]), (4096, [300, 0]),
+                                     (1, [1, 64]), (5003, [64, 64])])
+def test_decode_step_fused(orc, n, n_loc):
+    """Cache and local tokens as one token range (cache length not a multiple of 32: a block straddles)."""
+    _step_case(orc, len(n_loc), 32, 8, n, max(n_loc), n_loc, torch.bfloat16, 1000 + n)
+
+
+def test_decode_step_fallbacks(orc):
+    """fp32, a shared document, and doc-only outputs run as the two separate calls."""
+    _step_case(orc, 2, 8, 2, 700, 64, [64, 3], torch.float32, 1100)
+    _step_case(orc, 3, 8, 2, 900, 32, [32, 1, 0], torch.bfloat16, 1101, shared=True)
+    _step_case(orc, 2, 8, 2, 800, 48, [48, 10], torch.bfloat16, 1102, doc=True)
+    _step_case(orc, 2, 8, 2, 0, 48, [48, 10], torch.bfloat16, 1103)
+
+
+def test_decode_step_config2_full_size(orc):
+    cfg = synth.CONFIGS[2]
+    x = synth.make_inputs(cfg)
+    out, alpha = ops.dense_decode_step(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["k_loc"].to(DEV),
+                                       x["v_loc"].to(DEV), x["n_loc"].to(DEV))
+    torch.cuda.synchronize()
+    ro, ra = orc.dense_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]))
+    mo, ma = orc.merge_local(to_np(x["q"]), ro, ra, to_np(x["k_loc"]), to_np(x["v_loc"]), to_np(x["n_loc"]))
+    assert_close(out, alpha, mo, ma, torch.bfloat16, "config 2 fused step")
+
+
+# ------------------------------------------------------- kernel variants ----
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_dense_split_variants(orc, variant):
+    """Every MFMA split variant (nontemporal / cached register loads, LDS ring) gives the oracle's result,
+    for the plain call and the fused step, including ragged and short ranges."""
+    old = ops.get_tuning("dense_variant")
+    ops.set_tuning("dense_variant", variant)
+    try:
+        for n in (33, 1000, 5003, 61440 // 8):
+            _dense_case(2, 8, 2, n, torch.bfloat16, 1200 + n + variant, orc=orc)
+        _step_case(orc, 2, 32, 8, 3001, 200, [200, 7], torch.bfloat16, 1300 + variant)
+        _step_case(orc, 1, 32, 8, 4096, 256, [256], torch.bfloat16, 1310 + variant)
+    finally:
+        ops.set_tuning("dense_variant", old)

@@ -155,3 +155,28 @@ def test_config4_reduced_end_to_end(orc):
     out, alpha = ops.gather_attn(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), idx, cnt)
     ro, ra = orc.gather_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), ri, rc)
     assert_close(out, alpha, ro, ra, torch.bfloat16, "config 4 reduced")
+
+
+def test_gather_clamps_out_of_range_entries(orc):
+    """Regression: counts beyond cap (or negative) and positions outside [0, n) are clamped by the
+    kernel (results for such rows are undefined, but nothing is read out of bounds); valid rows in
+    the same call are unaffected."""
+    B, Hq, Hkv, n, cap = 2, 8, 2, 3000, 64
+    q, k, v = _kv(B, Hq, Hkv, n, torch.bfloat16, 61)
+    g = np.random.default_rng(62)
+    idx = g.integers(0, n, (B, Hq, cap)).astype(np.int32)
+    cnt = g.integers(0, cap + 1, (B, Hq)).astype(np.int32)
+    bad_idx = idx.copy()
+    bad_cnt = cnt.copy()
+    bad_idx[0, 1, :] = g.integers(-(1 << 30), 1 << 30, cap).astype(np.int32)
+    bad_cnt[0, 2] = cap + 1000
+    bad_cnt[1, 5] = -7
+    out, alpha = ops.gather_attn(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(bad_idx).to(DEV),
+                                 torch.from_numpy(bad_cnt).to(DEV))
+    torch.cuda.synchronize()
+    ro, ra = orc.gather_attn(to_np(q), to_np(k), to_np(v), idx, cnt)
+    keep = np.ones((B, Hq), bool)
+    keep[0, 1] = keep[0, 2] = keep[1, 5] = False
+    assert_close(out.cpu().numpy()[keep], alpha.cpu().numpy()[keep], ro[keep], ra[keep], torch.bfloat16,
+                 "gather rows next to clamped rows")
+    assert torch.all(out[1, 5] == 0) and torch.isneginf(alpha[1, 5])     # a negative count is an empty set
