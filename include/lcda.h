@@ -189,9 +189,10 @@ const char* lcda_version(void);
  *   "gather_wgs"     target workgroups of the GATHER-ATT split (2048)
  *   "direct_blocks"  units with at most this many token blocks run as one split
  *                    that writes its rows directly, without a combine pass (16)
- *   "dense_variant"  MFMA split K/V loads (16-row tiles): 0 = nontemporal into
- *                    registers, 1 = cached into registers, 2 = nontemporal into
- *                    a two-slot LDS ring per wave (0)
+ *   "dense_variant"  MFMA split K/V pipeline (16-row tiles): 0 = nontemporal
+ *                    loads one block ahead, 1 = cached loads one block ahead,
+ *                    2 = nontemporal two blocks ahead, 3 = as 0 with registers
+ *                    capped so two workgroups share a CU (0)
  *   "gather_variant" GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads (0)
  * Returns LCDA_EINVAL for an unknown key or a negative (or, except
  * direct_blocks, zero) value.  lcda_get_tuning returns -1 for an unknown key. */

@@ -70,15 +70,18 @@ int check_kv_stride(const char* fn, int64_t stride, int Hkv, int64_t n, int dtyp
     return LCDA_OK;
 }
 
+// Workspace of a split pass: one arrival counter per work unit (at most one
+// unit per query row), then the partial states of every (row, split) slot.
 struct PartialLayout {
-    size_t ml_off, acc_off, bytes;
+    size_t ctr_off, ml_off, acc_off, bytes;
 };
 
 PartialLayout partial_layout(int B, int Hq, int splits) {
     PartialLayout l;
     const size_t slots = (size_t)B * Hq * splits;
-    l.ml_off = 0;
-    l.acc_off = round_up(slots * sizeof(float2));
+    l.ctr_off = 0;
+    l.ml_off = round_up((size_t)B * Hq * sizeof(unsigned long long));
+    l.acc_off = l.ml_off + round_up(slots * sizeof(float2));
     l.bytes = l.acc_off + round_up(slots * kD * sizeof(float));
     return l;
 }
@@ -95,7 +98,9 @@ int hip_status(const char* fn, hipError_t e) {
 }
 
 // Launch the split pass, then the combine pass unless the plan has a single
-// split (the split kernel then writes the final rows itself).
+// split (the split kernel then writes the final rows itself) or the split
+// kernel combines each unit itself (MFMA: the last workgroup of a unit to
+// finish merges its rows).
 int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows, float* out, float* alpha,
            const float* a_in, const float* alpha_in, hipStream_t st) {
     a.direct = p.splits == 1 ? 1 : 0;
@@ -104,7 +109,7 @@ int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows
     a.a_in = a_in;
     a.alpha_in = alpha_in;
     RETURN_IF(hip_status(fn, launch_split(p, a, dtype, st)));
-    if (a.direct) return LCDA_OK;
+    if (a.direct || p.kernel == kMfma16) return LCDA_OK;
     CombineArgs c{};
     c.ml = a.ml;
     c.acc = a.acc;
@@ -140,6 +145,10 @@ Tuning& tuning() {
     static Tuning t;
     return t;
 }
+
+// Token range of a fused step: the cache tokens, padded to whole 32-token
+// blocks, then the local tokens (so no block spans both).
+int64_t fused_tokens(int64_t n, int64_t n_loc_max) { return (n + 31) / 32 * 32 + n_loc_max; }
 
 SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared) {
     SplitPlan p{};
@@ -217,7 +226,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "valu_wgs") && value > 0) t.valu_wgs = value;
     else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
-    else if (!strcmp(key, "dense_variant") && value <= 2) t.dense_variant = value;
+    else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
     else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
     return LCDA_OK;
@@ -298,6 +307,7 @@ int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, 
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(fn, p, a, dtype, B * Hq, out, alpha, nullptr, nullptr, st);
@@ -345,6 +355,7 @@ int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, con
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(fn, p, a, dtype, B * Hq, out, alpha_out, a_in, alpha_in, st);
@@ -357,13 +368,13 @@ int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, con
 size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride,
                                        int64_t n_loc_max) {
     if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX || n_loc_max < 0 ||
-        n + n_loc_max > INT32_MAX)
+        fused_tokens(n, n_loc_max) > INT32_MAX)
         return 0;
     // the two-call form needs its own workspace and the doc-only (A, alpha) buffers
     const size_t two = lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride) +
                        lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max) +
                        round_up((size_t)B * Hq * (kD + 1) * sizeof(float));
-    const SplitPlan p = plan_split(LCDA_BF16, false, B, Hq, Hkv, n + n_loc_max, false);
+    const SplitPlan p = plan_split(LCDA_BF16, false, B, Hq, Hkv, fused_tokens(n, n_loc_max), false);
     const size_t fused = partial_layout(B, Hq, p.splits).bytes;
     return two > fused ? two : fused;
 }
@@ -377,7 +388,7 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
     RETURN_IF(check_dtype(fn, dtype));
     RETURN_IF(check_n(fn, "n", n));
     RETURN_IF(check_n(fn, "n_loc_max", n_loc_max));
-    RETURN_IF(check_n(fn, "n + n_loc_max", n + n_loc_max));
+    RETURN_IF(check_n(fn, "n + n_loc_max (cache padded to 32)", fused_tokens(n, n_loc_max)));
     RETURN_IF(check_kv_stride(fn, kv_batch_stride, Hkv, n, dtype));
     const bool work = B > 0;
     RETURN_IF(check_ptr(fn, "q", q, work));
@@ -413,7 +424,7 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
         return lse_merge_local(q, A, al, k_loc, v_loc, n_loc, n_loc_max, B, Hq, Hkv, d, dtype, out, alpha_out,
                                w + w1, w2, stream);
     }
-    const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n + n_loc_max, false);
+    const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, fused_tokens(n, n_loc_max), false);
     const PartialLayout lay = partial_layout(B, Hq, p.splits);
     SplitArgs a{};
     a.q = q;
@@ -438,6 +449,7 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     return finish(fn, p, a, dtype, B * Hq, out, alpha_out, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
@@ -535,6 +547,7 @@ int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_st
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(fn, p, a, dtype, B * Hq, out, alpha, nullptr, nullptr, st);

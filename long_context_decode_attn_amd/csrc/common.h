@@ -66,15 +66,160 @@ __device__ __forceinline__ void finish_row(const Args& a, int64_t bhq, int c, fl
     if (a.alpha && c == 0) a.alpha[bhq] = (Mx + log2f(Lx)) * kLn2;
 }
 
+// s_waitcnt vmcnt(0): wait for every vector-memory access issued so far to
+// complete (gfx9 encoding: vmcnt = 0, expcnt and lgkmcnt left at their
+// maxima; on gfx9 vmcnt counts stores as well as loads).  Drains a kernel
+// prologue so that a software-pipelined loop starts with only its own block
+// loads outstanding, and waits for stores to be acknowledged.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Partial states cross workgroups (and XCDs, whose L2 caches are not kept
+// coherent with each other) through device-scope stores and loads: a store
+// with device scope is written through to the device's coherence point before
+// it is acknowledged, and a load with device scope reads from there.  Only
+// these values are published, so no whole-cache write-back or invalidate is
+// needed.
+__device__ __forceinline__ void store_dev(float* p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(float2* p, float2 x) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       __builtin_bit_cast(unsigned long long, x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_dev2(const float* p) {   // two adjacent floats, 8-byte aligned
+    return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Tag of the arrival counter at address c: a hash of the address, so that a
+// counter word is recognised as one this library left (tag, 0) and anything
+// else (a fresh workspace, other data) is not.
+__device__ __forceinline__ uint32_t ctr_tag(const unsigned long long* c) {
+    uint32_t x = (uint32_t)((uintptr_t)c >> 3) ^ 0x6C8E9CF5u;   // MurmurHash3's 32-bit finalizer
+    x ^= x >> 16;
+    x *= 0x85EBCA6Bu;
+    x ^= x >> 13;
+    x *= 0xC2B2AE35u;
+    x ^= x >> 16;
+    return x;
+}
+
+// Arrival of one workgroup at the end of a split pass over unit `unit`, after
+// every thread wrote its partial states with store_dev: returns true, in every
+// thread, in the last of the unit's a.splits workgroups to arrive.  The
+// counter holds (tag << 32 | arrivals); between calls it is (tag, 0), which the
+// last arrival restores.  Normally an arrival is one fetch-add.  A counter word
+// without its tag (never used, or overwritten) is replaced by (tag, 1) with a
+// compare-exchange by the first workgroup to find it so; the others then count
+// on the valid word.  The exchange loop only runs in that case and ends once
+// any workgroup has installed the word.
+template <class Args>
+__device__ __forceinline__ bool arrive_last(const Args& a, int64_t unit, int* s_flag) {
+    wait_vm_all();    // this thread's device-scope stores are acknowledged
+    __syncthreads();  // ... in every thread of the workgroup
+    if (threadIdx.x == 0) {
+        unsigned long long* c = a.ctr + unit;
+        const uint32_t tag = ctr_tag(c);
+        const unsigned long long valid0 = (unsigned long long)tag << 32;
+        unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t count;
+        if ((uint32_t)(old >> 32) == tag) {
+            count = (uint32_t)old + 1u;
+        } else {
+            unsigned long long cur = old + 1ull;
+            while (true) {
+                if ((uint32_t)(cur >> 32) == tag) {
+                    old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    count = (uint32_t)old + 1u;
+                    break;
+                }
+                if (__hip_atomic_compare_exchange_strong(c, &cur, valid0 | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)) {
+                    count = 1u;
+                    break;
+                }
+            }
+        }
+        const bool last = count == (uint32_t)a.splits;
+        if (last) __hip_atomic_store(c, valid0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// One wave merges the a.splits partial states of query row bhq (and the
+// optional virtual pair (a_in, alpha_in)) into out / alpha, as the combine
+// pass does: M = max m_s, L = sum l_s 2^(m_s - M), A = sum acc_s 2^(m_s - M) / L.
+// Partial states are read with device-scope loads.  Lane l owns output
+// columns 2l, 2l + 1.
+template <class Args>
+__device__ __forceinline__ void combine_row(const Args& a, int64_t bhq, int lane) {
+    const int S = a.splits;
+    const float* ml = reinterpret_cast<const float*>(a.ml + bhq * S);
+    const float* acc = a.acc + bhq * S * kD + 2 * lane;
+    float mloc = kNoMax;
+    int anyl = 0;
+    for (int s = lane; s < S; s += 64) {
+        const f32x2 x = load_dev2(ml + 2 * s);
+        if (x.y > 0.f) {
+            mloc = fmaxf(mloc, x.x);
+            anyl = 1;
+        }
+    }
+    const bool virt = a.alpha_in != nullptr && a.alpha_in[bhq] > -INFINITY;
+    if (!__any(anyl) && !virt) {
+        *reinterpret_cast<f32x2*>(a.out + bhq * kD + 2 * lane) = f32x2{0.f, 0.f};
+        if (a.alpha && lane == 0) a.alpha[bhq] = -INFINITY;
+        return;
+    }
+    const float mv = virt ? a.alpha_in[bhq] * kLog2e : kNoMax;
+    const float M = fmaxf(wave_max(mloc), mv);
+    f32x2 o = {0.f, 0.f};
+    float lsum = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int s = s0 + lane;
+        const f32x2 x = s < S ? load_dev2(ml + 2 * s) : f32x2{kNoMax, 0.f};
+        const float w = x.y > 0.f ? fast_exp2(x.x - M) : 0.f;
+        lsum += w * x.y;
+        const int wi_bits = __builtin_bit_cast(int, w);
+        const int cnt = min(64, S - s0);
+        const float* base = acc + (int64_t)s0 * kD;
+        int i = 0;
+        for (; i + 8 <= cnt; i += 8) {
+            f32x2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = load_dev2(base + (int64_t)(i + u) * kD);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                o += __builtin_bit_cast(float, __builtin_amdgcn_readlane(wi_bits, i + u)) * v[u];
+        }
+        for (; i < cnt; ++i)
+            o += __builtin_bit_cast(float, __builtin_amdgcn_readlane(wi_bits, i)) * load_dev2(base + (int64_t)i * kD);
+    }
+    const float wv = virt ? fast_exp2(mv - M) : 0.f;
+    const float L = wave_sum(lsum) + wv;
+    if (virt) o += wv * *reinterpret_cast<const f32x2*>(a.a_in + bhq * kD + 2 * lane);
+    *reinterpret_cast<f32x2*>(a.out + bhq * kD + 2 * lane) = o * (1.f / L);
+    if (a.alpha && lane == 0) a.alpha[bhq] = (M + log2f(L)) * kLn2;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// s_waitcnt vmcnt(0): wait for every vector-memory load issued so far (gfx9
-// encoding: vmcnt = 0, expcnt and lgkmcnt left at their maxima).  Used to drain
-// a kernel prologue so that a software-pipelined loop starts from a state in
-// which only its own block loads are outstanding.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 16-byte load marked nontemporal (streamed once; do not keep in cache).
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {

@@ -30,6 +30,10 @@ struct SplitArgs {
     int blocks_per_split;       // split length in blocks of `block` tokens
     float2* ml;                 // partial states (see Partials)
     float* acc;
+    // Arrival counters, one per unit (MFMA split, more than one split): the
+    // last of a unit's `splits` workgroups to arrive combines the unit's rows
+    // (see arrive_last).
+    unsigned long long* ctr;
     float scale_log2;           // log2(e) / sqrt(d)
     // Fused cache + local step: tokens j >= n_c of row b come from k2 / v2
     // (local block, element (b, h, j - n_c, c) at b*kv2_batch_stride +
@@ -56,7 +60,8 @@ struct Tuning {
     int64_t valu_wgs = 512;        // target workgroups, VALU dense split
     int64_t gather_wgs = 2048;     // target workgroups, GATHER-ATT split
     int64_t direct_blocks = 16;    // at most this many blocks per unit: one split, no combine pass
-    int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads
+    int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads,
+                                   // 2 = two blocks ahead, 3 = nontemporal with two waves per SIMD
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads
 };
 Tuning& tuning();

@@ -24,6 +24,10 @@
 //   (column n of block nb is d = 8n + nb).
 // - Online softmax with a lazy rescale: the running max only moves when a row's
 //   block max exceeds it by more than 2^8, which keeps every weight <= 256.
+// - K/V blocks are read with buffer loads against a per-block resource (the
+//   block's first row in scalar registers, its size the rows left in the
+//   segment), so a lane holds two 32-bit offsets instead of 16 addresses, and
+//   rows past the end read as zero; their scores are masked.
 // - The next block's loads are issued before the current block is computed.
 // - The 4 waves of a workgroup interleave blocks of the split and merge their
 //   states through LDS, so each (row, split) slot is written once.
@@ -69,109 +73,48 @@ struct BlockRegs {
     u32x4 v[8];     // [k element e]: 8 d values of token tok_of(j, e)
 };
 
-// Token t of the row's token range lives in segment 1 (kh, vh) when t < n_c,
-// else at t - n_c in segment 2 (kh2, vh2).  A block entirely on one side uses
-// that side's base; only a block that straddles n_c selects per lane.
+// A row's token range: segment 1 (kh, vh) holds rows [0, n_c); in a fused step
+// segment 2 (kh2, vh2) holds its rows at unified tokens [n_c_al, n_eff), where
+// n_c_al is n_c rounded up to a whole block, so no block spans both segments
+// (the at most 31 positions in between are masked like a tail).
 struct Segs {
     const uint16_t* kh;
     const uint16_t* vh;
     const uint16_t* kh2;
     const uint16_t* vh2;
-    int64_t n_c;
+    int64_t n_c, n_c_al, n_eff;
 };
 
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format, no swizzle
+
+// Block of 32 tokens starting at unified token t: returns the rows of it that
+// hold tokens (1..32) and requests all 32 rows; rows past the segment's end
+// read as zero.  koff = 256*c16 + 16*j (K row c16 of each 16-token half);
+// voff = 1024*j + 16*c16 (V row 4j): the V rows tok_of(j, e) are 4j + e and
+// 16 + 4j + (e - 4).
 template <bool NTL, bool FUSED>
-__device__ __forceinline__ const uint16_t* row_ptr(const Segs& sg, bool second, int64_t tok, bool k) {
-    if (!FUSED) return (k ? sg.kh : sg.vh) + tok * kD;
-    return second ? (k ? sg.kh2 : sg.vh2) + (tok - sg.n_c) * kD : (k ? sg.kh : sg.vh) + tok * kD;
-}
-
-template <bool NTL, bool FUSED>
-__device__ __forceinline__ void load_block(BlockRegs& r, const Segs& sg, int64_t t, int64_t last, int j, int c16) {
-    // uniform per block: 0 = all in segment 1, 1 = all in segment 2, 2 = straddles
-    const int side = !FUSED ? 0 : (t + kBlock <= sg.n_c ? 0 : (t >= sg.n_c ? 1 : 2));
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int64_t tok = min(t + 16 * tb + c16, last);
-        const bool second = side == 1 || (side == 2 && tok >= sg.n_c);
-        const uint16_t* p = row_ptr<NTL, FUSED>(sg, second, tok, true) + 8 * j;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) r.k[tb][c] = ld16s<NTL>(p + 32 * c);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int64_t tok = min(t + tok_of(j, e), last);
-        const bool second = side == 1 || (side == 2 && tok >= sg.n_c);
-        r.v[e] = ld16s<NTL>(row_ptr<NTL, FUSED>(sg, second, tok, false) + 8 * c16);
-    }
-}
-
-// ---- LDS-ring variant -------------------------------------------------------
-// Each wave owns two 16 KB LDS slots.  A block is requested straight into a
-// slot with global->LDS loads (no VGPRs are held while it is in flight): lane l
-// of load instruction i writes its 16 bytes at slot + 1024*i + 16*l, and later
-// reads them back from the same place, so the register layout after the read
-// is exactly the one load_block produces.  The wait for a slot's data is an
-// explicit vmcnt, and the read of the slot is a single asm block that waits for
-// its own LDS reads, so the compiler never has to guess which slot a wait is
-// for.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-constexpr int kSlotBytes = 16384;
-constexpr int kVmcnt16 = 0x4F70;   // s_waitcnt vmcnt(16) (gfx9 encoding; other counters at maxima)
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-template <bool NTL, bool FUSED>
-__device__ __forceinline__ void dma_block(char* slot, const Segs& sg, int64_t t, int64_t last, int j, int c16) {
-    const int side = !FUSED ? 0 : (t + kBlock <= sg.n_c ? 0 : (t >= sg.n_c ? 1 : 2));
+__device__ __forceinline__ int load_block(BlockRegs& r, const Segs& sg, int64_t t, uint32_t koff, uint32_t voff) {
+    const bool second = FUSED && t >= sg.n_c_al;
+    const uint16_t* kseg = second ? sg.kh2 : sg.kh;
+    const uint16_t* vseg = second ? sg.vh2 : sg.vh;
+    const int64_t row = second ? t - sg.n_c_al : t;
+    const int64_t left = (second ? sg.n_eff - sg.n_c_al : (FUSED ? sg.n_c : sg.n_eff)) - row;
+    const int valid = (int)(left < kBlock ? left : kBlock);
+    const int nrec = valid * kD * 2;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kseg + row * kD), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vseg + row * kD), 0, nrec, kRsrcWord3);
     constexpr int aux = NTL ? 2 : 0;   // nontemporal
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int64_t tok = min(t + 16 * tb + c16, last);
-        const bool second = side == 1 || (side == 2 && tok >= sg.n_c);
-        const uint16_t* p = row_ptr<NTL, FUSED>(sg, second, tok, true) + 8 * j;
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            __builtin_amdgcn_global_load_lds((const void*)(p + 32 * c), (lds_ptr_t)(slot + 1024 * (4 * tb + c)), 16, 0,
-                                             aux);
-    }
+            r.k[tb][c] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 4096 * tb + 64 * c, 0, aux);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int64_t tok = min(t + tok_of(j, e), last);
-        const bool second = side == 1 || (side == 2 && tok >= sg.n_c);
-        __builtin_amdgcn_global_load_lds((const void*)(row_ptr<NTL, FUSED>(sg, second, tok, false) + 8 * c16),
-                                         (lds_ptr_t)(slot + 1024 * (8 + e)), 16, 0, aux);
-    }
-}
-
-// This lane's 16 pieces of a slot (addr = slot + 16*lane) into registers.
-__device__ __forceinline__ void lds_read_block(BlockRegs& r, uint32_t addr) {
-    asm volatile(
-        "ds_read_b128 %0, %16 offset:0\n\t"
-        "ds_read_b128 %1, %16 offset:1024\n\t"
-        "ds_read_b128 %2, %16 offset:2048\n\t"
-        "ds_read_b128 %3, %16 offset:3072\n\t"
-        "ds_read_b128 %4, %16 offset:4096\n\t"
-        "ds_read_b128 %5, %16 offset:5120\n\t"
-        "ds_read_b128 %6, %16 offset:6144\n\t"
-        "ds_read_b128 %7, %16 offset:7168\n\t"
-        "ds_read_b128 %8, %16 offset:8192\n\t"
-        "ds_read_b128 %9, %16 offset:9216\n\t"
-        "ds_read_b128 %10, %16 offset:10240\n\t"
-        "ds_read_b128 %11, %16 offset:11264\n\t"
-        "ds_read_b128 %12, %16 offset:12288\n\t"
-        "ds_read_b128 %13, %16 offset:13312\n\t"
-        "ds_read_b128 %14, %16 offset:14336\n\t"
-        "ds_read_b128 %15, %16 offset:15360\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=v"(r.k[0][0]), "=v"(r.k[0][1]), "=v"(r.k[0][2]), "=v"(r.k[0][3]), "=v"(r.k[1][0]), "=v"(r.k[1][1]),
-          "=v"(r.k[1][2]), "=v"(r.k[1][3]), "=v"(r.v[0]), "=v"(r.v[1]), "=v"(r.v[2]), "=v"(r.v[3]), "=v"(r.v[4]),
-          "=v"(r.v[5]), "=v"(r.v[6]), "=v"(r.v[7])
-        : "v"(addr)
-        : "memory");
+    for (int e = 0; e < 8; ++e)
+        r.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + (e < 4 ? 0 : 4096) + 256 * (e & 3), 0, aux);
+    return valid;
 }
 
 template <int NT>
@@ -183,8 +126,8 @@ struct WaveState {
 };
 
 template <int NT>
-__device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs& r, int64_t t,
-                                              int64_t n_eff, float scale, int j, int c16) {
+__device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs& r, int valid, float scale, int j,
+                                              int c16) {
     // V operand: column n = c16 of d-block nb is d = 8*c16 + nb; k element e is token tok_of(j, e).
     bf16x8 vb[8];
 #pragma unroll
@@ -196,7 +139,7 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
             x[qd] = __builtin_amdgcn_perm(r.v[2 * qd + 1][nb >> 1], r.v[2 * qd][nb >> 1], sel);
         vb[nb] = as_bf16x8(x);
     }
-    // Scores: s[rt][tb][i] is token t + 16*tb + 4*j + i of row 16*rt + c16.
+    // Scores: s[rt][tb][i] is token 16*tb + 4*j + i of the block, row 16*rt + c16.
     f32x4 s[NT][2];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
@@ -208,7 +151,7 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[tb][c]), st.q[rt][c], acc, 0, 0, 0);
             s[rt][tb] = acc;
         }
-    const bool full = (t + kBlock <= n_eff);
+    const bool full = valid >= kBlock;
     float bm[NT];
     bool need = false;
 #pragma unroll
@@ -219,7 +162,7 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float x = s[rt][tb][i] * scale;
-                if (!full && t + 16 * tb + 4 * j + i >= n_eff) x = -INFINITY;
+                if (!full && 16 * tb + 4 * j + i >= valid) x = -INFINITY;
                 s[rt][tb][i] = x;
                 mx = fmaxf(mx, x);
             }
@@ -266,50 +209,48 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
 
 // DEPTH: blocks requested ahead of the one being computed (DEPTH + 1 register
 // sets rotate).  NTL: nontemporal K/V loads.  FUSED: the row's tokens continue
-// past n_c in a second segment (the local block of a fused decode step).
-template <int NT>
-union SplitSmem {
-    MfmaSmem<NT> m;
-    char ring[kWaves][2][kSlotBytes];
-};
-
-template <int NT, int DEPTH, bool NTL, bool FUSED, bool RING>
-__global__ __launch_bounds__(64 * kWaves) void k_split_mfma(SplitArgs a) {
-    __shared__ __attribute__((aligned(16))) SplitSmem<NT> smu;
-    MfmaSmem<NT>& sm = smu.m;
+// in a second segment (the local block of a fused decode step).  WPE: waves
+// per SIMD the register allocation leaves room for (2 caps a wave at 256
+// VGPRs so two workgroups share a CU).  DIRECT: one split per unit, rows
+// finished in place (a.direct).
+template <int NT, int DEPTH, bool NTL, bool FUSED, int WPE, bool DIRECT>
+__global__ __launch_bounds__(64 * kWaves, WPE) void k_split_mfma(SplitArgs a) {
+    __shared__ __attribute__((aligned(16))) MfmaSmem<NT> sm;
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps t in scalars
     const int j = lane >> 4, c16 = lane & 15;
+    const uint32_t koff = 256u * c16 + 16u * j;
+    const uint32_t voff = 1024u * j + 16u * c16;
     const int split = blockIdx.x, h = blockIdx.y;
     const int bkv = blockIdx.z / a.row_groups, rg = blockIdx.z % a.row_groups;
     const int rows_base = rg * 16 * NT;
 
-    int64_t n_eff = a.n;
-    if (a.n_b) n_eff = min((int64_t)a.n_b[bkv], a.n);
     const int64_t head_off = (int64_t)bkv * a.kv_batch_stride + (int64_t)h * a.n * kD;
     Segs sg;
     sg.kh = static_cast<const uint16_t*>(a.k) + head_off;
     sg.vh = static_cast<const uint16_t*>(a.v) + head_off;
     sg.n_c = a.n;
+    sg.n_c_al = a.n;
     sg.kh2 = sg.vh2 = nullptr;
+    sg.n_eff = a.n_b ? min((int64_t)a.n_b[bkv], a.n) : a.n;
     if (FUSED) {
         const int64_t off2 = (int64_t)bkv * a.kv2_batch_stride + (int64_t)h * a.n2 * kD;
         sg.kh2 = static_cast<const uint16_t*>(a.k2) + off2;
         sg.vh2 = static_cast<const uint16_t*>(a.v2) + off2;
-        n_eff = a.n + (a.n2_b ? min(max((int64_t)a.n2_b[bkv], (int64_t)0), a.n2) : a.n2);
+        sg.n_c_al = (a.n + kBlock - 1) / kBlock * kBlock;
+        sg.n_eff = sg.n_c_al + (a.n2_b ? min(max((int64_t)a.n2_b[bkv], (int64_t)0), a.n2) : a.n2);
     }
 
     const int64_t t_begin = (int64_t)split * a.blocks_per_split * kBlock;
-    const int64_t t_end = min(n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
+    const int64_t t_end = min(sg.n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
     const int64_t step = (int64_t)kWaves * kBlock;
-    const int64_t last = n_eff - 1;
     int64_t t = t_begin + w * kBlock;
 
     // Direct mode with a (alpha_in, a_in) pair: read the values this thread
     // will finish now, so their latency hides behind the main loop.
     constexpr int kFin = 16 * NT * kD / (64 * kWaves);
     float pre_al[kFin], pre_a[kFin];
-    if (a.direct && a.alpha_in) {   // uniform; clamped rows keep the loads branch-free
+    if (DIRECT && a.alpha_in) {   // uniform; clamped rows keep the loads branch-free
 #pragma unroll
         for (int f = 0; f < kFin; ++f) {
             const int e = threadIdx.x + f * 64 * kWaves;
@@ -348,45 +289,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_mfma(SplitArgs a) {
         st.l[rt] = 0.f;
     }
 
-    if (RING) {
-        // Drain the prologue's own loads, then request the first two blocks
-        // into this wave's two slots.  Past the end of the range the current
-        // block is requested again (cache-resident), which keeps exactly one
-        // block's loads (16) younger than the block being waited for.
-        wait_vm_all();
-        char* slots = smu.ring[w][0];
-        const uint32_t lane_off = lds_addr(slots) + 16 * lane;
-        int slot = 0;
-        if (t < t_end) {
-            dma_block<NTL, FUSED>(slots, sg, t, last, j, c16);
-            const int64_t t1 = t + step;
-            dma_block<NTL, FUSED>(slots + kSlotBytes, sg, t1 < t_end ? t1 : t, last, j, c16);
-            while (true) {
-                __builtin_amdgcn_s_waitcnt(kVmcnt16);   // this slot has landed
-                BlockRegs r;
-                lds_read_block(r, lane_off + slot * kSlotBytes);
-                const int64_t tn = t + 2 * step;
-                dma_block<NTL, FUSED>(slots + slot * kSlotBytes, sg, tn < t_end ? tn : t, last, j, c16);
-                compute_block<NT>(st, r, t, n_eff, a.scale_log2, j, c16);
-                t += step;
-                if (t >= t_end) break;
-                slot ^= 1;
-            }
-        }
-        wait_vm_all();     // the refills past the end
-        __syncthreads();   // every wave is done with its slots before they become the merge buffer
-    } else {
     // Request the first DEPTH blocks, then drain everything issued so far (the
     // query fragments, the merge inputs and these blocks), so that inside the
     // loop only the loop's own block loads are ever outstanding.  Past the end
     // of the range the current block is requested again (cache-resident),
     // which keeps the number of loads per step uniform.
     BlockRegs buf[DEPTH + 1];
+    int valid[DEPTH + 1];
     if (t < t_end) {
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) {
             const int64_t tu = t + u * step;
-            load_block<NTL, FUSED>(buf[u], sg, tu < t_end ? tu : t, last, j, c16);
+            valid[u] = load_block<NTL, FUSED>(buf[u], sg, tu < t_end ? tu : t, koff, voff);
         }
     }
     wait_vm_all();
@@ -398,16 +312,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_mfma(SplitArgs a) {
             for (int u = 0; u <= DEPTH; ++u) {
                 if (!done) {
                     const int64_t tn = t + DEPTH * step;
-                    load_block<NTL, FUSED>(buf[(u + DEPTH) % (DEPTH + 1)], sg, tn < t_end ? tn : t, last, j, c16);
+                    const int nx = (u + DEPTH) % (DEPTH + 1);
+                    valid[nx] = load_block<NTL, FUSED>(buf[nx], sg, tn < t_end ? tn : t, koff, voff);
                     // Keep every load of the block ahead above the first use of the current one.
                     __builtin_amdgcn_sched_barrier(0);
-                    compute_block<NT>(st, buf[u], t, n_eff, a.scale_log2, j, c16);
+                    compute_block<NT>(st, buf[u], valid[u], a.scale_log2, j, c16);
                     t += step;
                     done = t >= t_end;
                 }
             }
         }
-    }
     }
 
     // Per-wave state -> LDS.
@@ -446,12 +360,27 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_mfma(SplitArgs a) {
         const int b = a.shared ? r / a.G : bkv;
         const int g = a.shared ? r % a.G : r;
         const int64_t bhq = (int64_t)b * a.Hq + h * a.G + g;
-        if (a.direct) {
+        if (DIRECT) {
             finish_row(a, bhq, c, M, L, acc, pre_al[f] > -INFINITY, pre_al[f], pre_a[f]);
         } else {
             const int64_t slot = bhq * a.splits + split;
-            a.acc[slot * kD + c] = acc;
-            if (c == 0) a.ml[slot] = make_float2(M, L);
+            store_dev(a.acc + slot * kD + c, acc);
+            if (c == 0) store_dev(a.ml + slot, make_float2(M, L));
+        }
+    }
+
+    // The unit's last workgroup to finish merges every split of its rows.
+    if constexpr (!DIRECT) {
+        __shared__ int s_last;
+        const int64_t unit = ((int64_t)bkv * a.Hkv + h) * a.row_groups + rg;
+        if (arrive_last(a, unit, &s_last)) {
+            const int nrows = min(16 * NT, a.rows - rows_base);
+            for (int rr = w; rr < nrows; rr += kWaves) {
+                const int r = rows_base + rr;
+                const int b = a.shared ? r / a.G : bkv;
+                const int g = a.shared ? r % a.G : r;
+                combine_row(a, (int64_t)b * a.Hq + h * a.G + g, lane);
+            }
         }
     }
 }
@@ -462,19 +391,27 @@ hipError_t launch_split_mfma(const SplitPlan& p, const SplitArgs& a, hipStream_t
     dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
     const int variant = (int)tuning().dense_variant;
     const bool fused = a.k2 != nullptr;
-#define LCDA_SPLIT(NT_, NTL_, RING_)                                                                   \
-    do {                                                                                               \
-        if (fused) hipLaunchKernelGGL((k_split_mfma<NT_, 1, NTL_, true, RING_>), grid, block, 0, st, a); \
-        else hipLaunchKernelGGL((k_split_mfma<NT_, 1, NTL_, false, RING_>), grid, block, 0, st, a);    \
+    const bool direct = a.direct != 0;
+#define LCDA_SPLIT(NT_, DEPTH_, NTL_, WPE_)                                                                   \
+    do {                                                                                                      \
+        if (fused && direct)                                                                                  \
+            hipLaunchKernelGGL((k_split_mfma<NT_, DEPTH_, NTL_, true, WPE_, true>), grid, block, 0, st, a);   \
+        else if (fused)                                                                                       \
+            hipLaunchKernelGGL((k_split_mfma<NT_, DEPTH_, NTL_, true, WPE_, false>), grid, block, 0, st, a);  \
+        else if (direct)                                                                                      \
+            hipLaunchKernelGGL((k_split_mfma<NT_, DEPTH_, NTL_, false, WPE_, true>), grid, block, 0, st, a);  \
+        else                                                                                                  \
+            hipLaunchKernelGGL((k_split_mfma<NT_, DEPTH_, NTL_, false, WPE_, false>), grid, block, 0, st, a); \
     } while (0)
     switch (p.nt) {
         case 1:
-            if (variant == 1) LCDA_SPLIT(1, false, false);
-            else if (variant == 2) LCDA_SPLIT(1, true, true);
-            else LCDA_SPLIT(1, true, false);
+            if (variant == 1) LCDA_SPLIT(1, 1, false, 1);
+            else if (variant == 2) LCDA_SPLIT(1, 2, true, 1);
+            else if (variant == 3 && !direct) LCDA_SPLIT(1, 1, true, 2);
+            else LCDA_SPLIT(1, 1, true, 1);
             break;
-        case 2: LCDA_SPLIT(2, true, false); break;
-        case 4: LCDA_SPLIT(4, true, false); break;
+        case 2: LCDA_SPLIT(2, 1, true, 1); break;
+        case 4: LCDA_SPLIT(4, 1, true, 1); break;
         default: return hipErrorInvalidValue;
     }
 #undef LCDA_SPLIT

@@ -1,0 +1,106 @@
+"""The split pass's in-kernel combine: the last workgroup of each unit merges the unit's rows, found
+through per-unit arrival counters in the caller's workspace (each tagged with a hash of its address
+and left at a zero count by every call).
+
+Checks that results do not depend on what the workspace held before (zeros, all ones or random bytes
+that must be recognised as untagged, an earlier call of another shape, the same call replayed from a
+HIP graph), against the CPU oracle and, for replays, bit for bit against the eager call."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_attn_amd import ops
+from tests.util import assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _kv(B, Hq, Hkv, n, seed, n_loc=0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, Hq, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, n, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, n, 128), generator=g).to(torch.bfloat16)
+    kl = torch.randn((B, Hkv, n_loc, 128), generator=g).to(torch.bfloat16)
+    vl = torch.randn((B, Hkv, n_loc, 128), generator=g).to(torch.bfloat16)
+    return q, k, v, kl, vl
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_garbage_workspace(orc, fill):
+    """Whatever bytes the workspace starts with, the counters start from zero for a new call."""
+    B, Hq, Hkv, n, nl = 2, 32, 8, 8192, 100
+    q, k, v, kl, vl = _kv(B, Hq, Hkv, n, 71, nl)
+    nb = ops.ws_bytes_dense_decode_step(B, Hq, Hkv, 128, n, Hkv * n * 128, nl)
+    if fill == "zeros":
+        ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    elif fill == "ones":
+        ws = torch.full((nb,), 255, dtype=torch.uint8, device=DEV)
+    else:
+        ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, generator=torch.Generator().manual_seed(72)).to(DEV)
+    print("case garbage workspace fill=%s" % fill, flush=True)
+    a, al = ops.cached_attn_lse(q.to(DEV), k.to(DEV), v.to(DEV), ws=ws)
+    out, alpha = ops.dense_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), kl.to(DEV), vl.to(DEV), ws=ws)
+    torch.cuda.synchronize()
+    ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+    assert_close(a, al, ro, ra, torch.bfloat16, "cached part, %s workspace" % fill)
+    mo, ma = orc.merge_local(to_np(q), ro, ra, to_np(kl), to_np(vl), np.full(B, nl, np.int32))
+    assert_close(out, alpha, mo, ma, torch.bfloat16, "fused step, %s workspace" % fill)
+
+
+def test_one_workspace_many_calls(orc):
+    """Calls of different shapes back to back on one workspace (counters of one call left for the next)."""
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device=DEV)
+    cases = [(1, 32, 8, 20000), (2, 8, 2, 3001), (1, 32, 8, 61440 // 4), (3, 16, 4, 777)]
+    outs = []
+    for i in range(3):
+        for B, Hq, Hkv, n in cases:
+            q, k, v, _, _ = _kv(B, Hq, Hkv, n, 80 + n)
+            assert ops.ws_bytes_cached_attn_lse(B, Hq, Hkv, 128, n, Hkv * n * 128) <= ws.numel()
+            outs.append((q, k, v) + ops.cached_attn_lse(q.to(DEV), k.to(DEV), v.to(DEV), ws=ws))
+    torch.cuda.synchronize()
+    print("case one workspace, %d calls" % len(outs), flush=True)
+    for q, k, v, a, al in outs[-len(cases):]:
+        ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+        assert_close(a, al, ro, ra, torch.bfloat16, "call on a shared workspace")
+    for (q, k, v, a, al), (_, _, _, a2, al2) in zip(outs[:len(cases)], outs[-len(cases):]):
+        assert torch.equal(a, a2) and torch.equal(al, al2)
+
+
+def test_graph_replays_match_eager():
+    """A captured decode step replays with the same counter tag; eager calls on the same workspace run in
+    between.  Every replay equals an eager call on the same inputs, bit for bit."""
+    B, Hq, Hkv, n, nl = 1, 32, 8, 16384, 256
+    q, k, v, kl, vl = (t.to(DEV) for t in _kv(B, Hq, Hkv, n, 90, nl))
+    nb = ops.ws_bytes_dense_decode_step(B, Hq, Hkv, 128, n, Hkv * n * 128, nl)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ws_ref = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, 128), device=DEV)
+    alpha = torch.empty((B, Hq), device=DEV)
+    ref_o = torch.empty_like(out)
+    ref_a = torch.empty_like(alpha)
+
+    def step():
+        ops.dense_decode_step(q, k, v, kl, vl, out=out, alpha_out=alpha, ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=DEV).manual_seed(91)
+    for r in range(4):
+        print("case graph replay %d" % r, flush=True)
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+        k[:, :, : 64 * (r + 1)] = torch.randn((B, Hkv, 64 * (r + 1), 128), generator=gen, device=DEV).to(k.dtype)
+        # an eager call of another shape on the same workspace, then the replay
+        ops.cached_attn_lse(q[:, :8], k[:, :2, :3000].contiguous(), v[:, :2, :3000].contiguous(), ws=ws)
+        g.replay()
+        ops.dense_decode_step(q, k, v, kl, vl, out=ref_o, alpha_out=ref_a, ws=ws_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(alpha, ref_a), "replay %d differs from the eager call" % r

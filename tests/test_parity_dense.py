@@ -188,7 +188,8 @@ def _step_case(orc, B, Hq, Hkv, n, nl_max, n_loc, dtype, seed, shared=False, doc
 @pytest.mark.parametrize("n,n_loc", [(61440 // 16, [256]), (1000, [0, 17, 256]), (31, [5, 40]), (4096, [300, 0]),
                                      (1, [1, 64]), (5003, [64, 64])])
 def test_decode_step_fused(orc, n, n_loc):
-    """Cache and local tokens as one token range (cache length not a multiple of 32: a block straddles)."""
+    """Cache and local tokens as one token range (cache length not a multiple of 32: the local tokens start at
+    the next block boundary and the gap is masked)."""
     _step_case(orc, len(n_loc), 32, 8, n, max(n_loc), n_loc, torch.bfloat16, 1000 + n)
 
 
@@ -212,12 +213,14 @@ def test_decode_step_config2_full_size(orc):
 
 
 # ------------------------------------------------------- kernel variants ----
-@pytest.mark.parametrize("variant", [0, 1, 2])
-def test_dense_split_variants(orc, variant):
-    """Every MFMA split variant (nontemporal / cached register loads, LDS ring) gives the oracle's result,
-    for the plain call and the fused step, including ragged and short ranges."""
+@pytest.mark.parametrize("variant,wgs", [(0, 256), (1, 256), (2, 256), (3, 256), (3, 512), (3, 1024)])
+def test_dense_split_variants(orc, variant, wgs):
+    """Every MFMA split variant (nontemporal / cached loads, one or two blocks ahead, two waves per SIMD) and
+    launch width gives the oracle's result, for the plain call and the fused step, ragged and short ranges."""
     old = ops.get_tuning("dense_variant")
+    old_w = ops.get_tuning("dense_wgs")
     ops.set_tuning("dense_variant", variant)
+    ops.set_tuning("dense_wgs", wgs)
     try:
         for n in (33, 1000, 5003, 61440 // 8):
             _dense_case(2, 8, 2, n, torch.bfloat16, 1200 + n + variant, orc=orc)
@@ -225,3 +228,4 @@ def test_dense_split_variants(orc, variant):
         _step_case(orc, 1, 32, 8, 4096, 256, [256], torch.bfloat16, 1310 + variant)
     finally:
         ops.set_tuning("dense_variant", old)
+        ops.set_tuning("dense_wgs", old_w)
