@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from long_context_decode_attn_amd import ops, synth, traffic  # noqa: E402
+from long_context_decode_attn_amd.profsum import kernel_source_digest  # noqa: E402
 
 HBM_PEAK = 8.0e12   # B/s, MI355X published peak
 METRIC = "decode-attention queries/sec + achieved HBM TB/s (KV+sig bytes) vs ~8 TB/s peak"
@@ -145,9 +146,15 @@ def bench_dense(args, cfg, layers=1):
     ms_a = run_steps([make(r, "attn") for r in range(rot)], steps, args.warmup, args.graph) / (steps * layers)
 
     n_loc_total = int(sets[0][0].x["n_loc"].sum().item())
-    step_bytes = layers * traffic.dense_step_bytes(B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, cfg.shared_doc, n_loc_total)
+    layer_bytes = traffic.dense_step_bytes(B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, cfg.shared_doc, n_loc_total)
+    step_bytes = layers * layer_bytes
     attn_bytes = traffic.dense_step_bytes(B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, cfg.shared_doc, 0)
-    achieved = attn_bytes / (ms_a * 1e-3)
+    # The dominant kernel: one split-KV launch per layer and step (bf16, one cache per batch item:
+    # k_split_mfma over cache + local tokens with the LSE combine inside).  Its launches run back to back
+    # in the timed graph, so its average launch duration is the per-layer step time.
+    fused = not cfg.shared_doc
+    launch_us = ms_step * 1e3 / layers
+    achieved = layer_bytes / (launch_us * 1e-6)
     res = {
         "value": B / (ms_step * 1e-3),
         "ms_per_step": ms_step,
@@ -155,14 +162,57 @@ def bench_dense(args, cfg, layers=1):
         "step_bytes": step_bytes,
         "step_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": None,
-                     "kernel": "cached_attn_lse (k_split_mfma + k_combine)",
-                     "bytes_per_launch": attn_bytes, "avg_launch_us": ms_a * 1e3},
+                     "frac": achieved / HBM_PEAK,
+                     "traffic": traffic_from_profile("split_mfma_" + ("dense61k" if layers == 1 else "shared36"),
+                                                     layer_bytes) if fused else None,
+                     "kernel": ("k_split_mfma (dense_decode_step: cache + local tokens, LSE combine in-kernel; "
+                                "one launch per layer)") if fused else
+                               "k_split_mfma + k_split_mfma (cached_attn_lse, lse_merge_local) per layer",
+                     "bytes_per_launch": layer_bytes, "avg_launch_us": launch_us},
         "rotations": rot,
         "two_call_ms_per_step": ms_two,
         "two_call_tbps": step_bytes / (ms_two * 1e-3) / 1e12,
+        "cached_attn_lse_us": ms_a * 1e3,
+        "cached_attn_lse_tbps": attn_bytes / (ms_a * 1e-3) / 1e12,
     }
     return res, sets[0][0]
+
+
+# ---------------------------------------------------------------- traffic ----
+def traffic_from_profile(name: str, algorithmic_bytes: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    profiles/traffic_<name>.txt (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the
+    same counter's reading for a copy of known size).  None when there is no summary or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes: int, reps: int) -> dict:
+    """A plain device-to-device copy of known size (the counter calibration kernel)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = Timer()
+    t.start()
+    for _ in range(reps):
+        dst.copy_(src)
+    ms = t.stop_ms() / reps
+    return {"copy_bytes": nbytes, "reps": reps, "read_bytes": nbytes, "write_bytes": nbytes,
+            "ms_per_copy": ms, "tbps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e12}
 
 
 # ----------------------------------------------------------------- sparse ----
@@ -293,6 +343,8 @@ def main():
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
                     help="skip the sparse-path measurement that rides along with the dense61k line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0: skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (--steps times), for counter calibration")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -302,8 +354,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    ops.load()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        print(json.dumps(calibrate_copy(args.calibrate_copy << 20, args.steps)))
+        return
+    ops.load()
     dev_name = torch.cuda.get_device_name(0)
 
     line = {"metric": METRIC, "unit": "queries/s", "n_gpus": 1, "warmup": args.warmup,
@@ -319,7 +374,10 @@ def main():
         line["config"] = {"workload": args.workload + ": " + cfg.name, "batch": cfg.B, "n": cfg.n, "layers": layers,
                           "kv_heads": cfg.Hkv, "q_heads": cfg.Hq, "d": cfg.d, "n_loc": cfg.n_loc, "launch": launch,
                           "rotations": res["rotations"]}
-        line["step"] = "dense_decode_step (cached_attn_lse + lse_merge_local fused into one split pass + one combine)"
+        line["step"] = ("dense_decode_step: cached_attn_lse + lse_merge_local as one split-KV launch whose last "
+                        "workgroup per (batch, KV head) does the LSE combine" if not cfg.shared_doc else
+                        "36 x (cached_attn_lse + lse_merge_local) over one shared document")
+        line["cached_attn_lse_us"] = res["cached_attn_lse_us"]
         line["two_call_ms_per_step"] = res["two_call_ms_per_step"]
         line["two_call_tbps"] = res["two_call_tbps"]
         line["step_bytes"] = res["step_bytes"]

@@ -122,6 +122,7 @@ int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows
     return hip_status(fn, launch_combine(c, st));
 }
 
+// Workspace of sig_score_topk: histograms, per-chunk and per-head selection results.
 struct TopkLayout {
     int chunks;
     size_t hist_off, chunk_off, head_off, bytes;
@@ -129,13 +130,13 @@ struct TopkLayout {
 
 TopkLayout topk_layout(int B, int Hq, int64_t n) {
     TopkLayout l;
-    const int cl = topk_chunk_len(n);
+    const int64_t cl = topk_chunk_len(n);
     l.chunks = (int)ceil_div(n, cl);
     const size_t rows = (size_t)B * Hq;
     l.hist_off = 0;
-    l.chunk_off = round_up(rows * l.chunks * 33 * sizeof(uint32_t));
-    l.head_off = l.chunk_off + round_up(rows * l.chunks * sizeof(int32_t));
-    l.bytes = l.head_off + round_up(rows * sizeof(uint64_t));
+    l.chunk_off = l.hist_off + round_up(rows * l.chunks * topk_hist_row() * sizeof(uint32_t));
+    l.head_off = l.chunk_off + round_up(rows * l.chunks * 4 * sizeof(int32_t));
+    l.bytes = l.head_off + round_up(rows * 2 * sizeof(int32_t));
     return l;
 }
 

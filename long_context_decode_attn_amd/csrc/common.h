@@ -98,6 +98,13 @@ __device__ __forceinline__ void store_dev(float2* p, float2 x) {
     __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
                        __builtin_bit_cast(unsigned long long, x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_dev(uint32_t* p, uint32_t x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_dev_u64(const void* p) {   // 8-byte aligned
+    return __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ f32x2 load_dev2(const float* p) {   // two adjacent floats, 8-byte aligned
     return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -116,21 +123,19 @@ __device__ __forceinline__ uint32_t ctr_tag(const unsigned long long* c) {
     return x;
 }
 
-// Arrival of one workgroup at the end of a split pass over unit `unit`, after
-// every thread wrote its partial states with store_dev: returns true, in every
-// thread, in the last of the unit's a.splits workgroups to arrive.  The
-// counter holds (tag << 32 | arrivals); between calls it is (tag, 0), which the
-// last arrival restores.  Normally an arrival is one fetch-add.  A counter word
-// without its tag (never used, or overwritten) is replaced by (tag, 1) with a
+// Arrival of one workgroup at counter c, after every thread wrote what it
+// publishes with device-scope stores: returns true, in every thread, in the
+// last of `target` workgroups to arrive.  The counter holds
+// (tag << 32 | arrivals); between calls it is (tag, 0), which the last arrival
+// restores.  Normally an arrival is one fetch-add.  A counter word without its
+// tag (never used, or overwritten) is replaced by (tag, 1) with a
 // compare-exchange by the first workgroup to find it so; the others then count
 // on the valid word.  The exchange loop only runs in that case and ends once
 // any workgroup has installed the word.
-template <class Args>
-__device__ __forceinline__ bool arrive_last(const Args& a, int64_t unit, int* s_flag) {
+__device__ __forceinline__ bool arrive_count(unsigned long long* c, uint32_t target, int* s_flag) {
     wait_vm_all();    // this thread's device-scope stores are acknowledged
     __syncthreads();  // ... in every thread of the workgroup
     if (threadIdx.x == 0) {
-        unsigned long long* c = a.ctr + unit;
         const uint32_t tag = ctr_tag(c);
         const unsigned long long valid0 = (unsigned long long)tag << 32;
         unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -152,12 +157,18 @@ __device__ __forceinline__ bool arrive_last(const Args& a, int64_t unit, int* s_
                 }
             }
         }
-        const bool last = count == (uint32_t)a.splits;
+        const bool last = count == target;
         if (last) __hip_atomic_store(c, valid0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = last ? 1 : 0;
     }
     __syncthreads();
     return *s_flag != 0;
+}
+
+// The split pass's arrival: unit `unit` has a.splits workgroups.
+template <class Args>
+__device__ __forceinline__ bool arrive_last(const Args& a, int64_t unit, int* s_flag) {
+    return arrive_count(a.ctr + unit, (uint32_t)a.splits, s_flag);
 }
 
 // One wave merges the a.splits partial states of query row bhq (and the

@@ -110,13 +110,14 @@ struct TopkArgs {
     int32_t* idx;               // [B, Hq, cap]
     int32_t* count;             // [B, Hq]
     int8_t* scores;             // [B, Hq, n] or null
-    uint32_t* hist;             // ws: [B, Hq, chunks, 33]
-    int32_t* chunk_info;        // ws: [B, Hq, chunks, 2] (take, offset)
-    int32_t* head_info;         // ws: [B, Hq, 2] (t, p + 1)
-    int chunks;
-    int chunk_len;
+    uint32_t* hist;             // ws: [B, Hq, chunks, topk_hist_row()] distance histograms
+    int32_t* chunk_info;        // ws: [B, Hq, chunks, 4] (output offset, ties taken, ties, -)
+    int32_t* head_info;         // ws: [B, Hq, 2] (t, quota)
+    int chunks;                 // ceil(n / chunk_len) <= 64
+    int64_t chunk_len;
 };
 int topk_chunk_len(int64_t n);
+int topk_hist_row();
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
 }  // namespace lcda

@@ -6,24 +6,35 @@
 // position, united with the first n_sink and last n_recent positions, in
 // ascending order.
 //
-// Distances take only 33 values, so the top m is fixed by a threshold pair
-// (t, p): position i is in the top m iff d_i < t, or d_i == t and i <= p.
-// Three kernels; the two that scan signatures read each KV head's codes once
-// for all G query heads of its group:
-//   1. k_sig_hist    - per chunk of kChunk positions (one wavefront) and query
-//                      head, the 33-bin histogram of distances.  Counts go to 16
-//                      LDS copies (lane % 16), padded so lanes rarely collide.
-//   2. k_topk_select - per query head: global histogram -> t and the tie quota;
-//                      the chunk holding the last tie taken is scanned for p;
-//                      chunks covered by a window are counted whole and the (at
-//                      most two) chunks a window edge cuts are scanned; per-chunk
-//                      output offsets by an exclusive scan; count and the -1
-//                      padding are written.
-//   3. k_sig_compact - per chunk: recompute the distances (the codes are still
-//                      cache-resident), flag top-m or window positions and write
-//                      them in order with ballot / mbcnt ranks.
-// Each wavefront requests its whole chunk (4096 codes, 64 per lane) before
-// using any of it.
+// Distances take only 33 values, so the top m is fixed by a threshold t and a
+// tie quota: every position with d < t is in, and of the positions with
+// d == t the lowest `quota` are.  Split over chunks of a head's positions, the
+// ties a chunk takes are its first `taken_c` ties, where taken_c follows from
+// the tie counts of the chunks before it.
+//
+// Three kernels; the two that scan codes read each KV head's codes once for
+// all G query heads of its group.  The scans are bound by instruction issue
+// (one xor + popcount per position and query head, plus bookkeeping), so the
+// per-position work is kept to a few vector instructions.
+//   1. k_topk_hist    - per chunk: the 33-bin distance histogram of each query
+//                       head, in 64 lane-private LDS copies (the increments of
+//                       one instruction never collide).
+//   2. k_topk_select  - per query head (one wavefront, lane = chunk): t and the
+//                       quota from the summed histograms, each chunk's ties
+//                       taken, the window positions outside the top m in the
+//                       chunks a window edge cuts (only the window part of those
+//                       chunks is scanned), per-chunk output offsets, the count
+//                       and the -1 padding.
+//   3. k_topk_compact - per chunk: the codes are staged in LDS; one wavefront
+//                       per query head writes the selected positions in order at
+//                       the chunk's offset (ballot / mbcnt ranks).  A chunk that
+//                       takes all or none of its ties and meets no window keeps
+//                       exactly the positions with d below one threshold; only
+//                       the chunk taking part of its ties and the chunks a
+//                       window meets walk the full rule.
+// A chunk is a whole number of 4096-position sub-chunks, chosen so that a head
+// has at most 64 chunks.  Positions are below n <= INT32_MAX; loop bounds that
+// can step past n are 64-bit.
 
 #include "common.h"
 #include "internal.h"
@@ -31,393 +42,497 @@
 namespace lcda {
 namespace {
 
-constexpr int kChunk = 4096;            // positions per chunk (one wavefront)
-constexpr int kPerLane = kChunk / 64;   // codes per lane
-constexpr int kMaxG = 8;                // query heads per KV head handled by one pass
+constexpr int kSub = 4096;            // positions per sub-chunk (256 threads x 16)
+constexpr int kMaxChunks = 64;        // chunks per head: one lane each in the select wavefront
 constexpr int kBins = 33;
-constexpr int kCopies = 16;             // LDS histogram copies (lane % 16)
-constexpr int kBinStride = kCopies + 1; // words per bin (one pad word spreads banks)
+constexpr int kRow = 36;              // words per histogram row: 33 bins, padded to 9 x 16 bytes
+constexpr int kPre = 8;               // window-part steps of 64 positions prefetched in the select
 
-// ---- 1. histogram -----------------------------------------------------------
-// Lane l holds positions beg + 4*(l + 64*u) + e, u < kPerLane/4, e < 4.
-// Positions fit in 32 bits (n <= INT32_MAX).  A full chunk runs without any
-// per-position test; in the last, short chunk positions at or past the end
-// count into a spare bin (kBins) that is never read.
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// ---- loads ------------------------------------------------------------------
+// Thread tid's 16 codes of the sub-chunk at sb: positions sb + 4*(tid + 256*u) + e.
+// Addresses are clamped into [.., end); entries at or past end are ignored by the caller.
+template <bool VEC>
+__device__ __forceinline__ void load_sub(uint32_t (&x)[16], const uint32_t* ks, int64_t sb, int64_t end, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = sb + 4 * (tid + 256 * u);
+        if (VEC) {
+            const u32x4 v = ld16(ks + min(i, end - 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * u + e] = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * u + e] = ks[min(i + e, end - 1)];
+        }
+    }
+}
+
+// ---- selection (one wavefront per query head, lane = chunk) -------------------
+// A window part [p0, p1) of a cut chunk, walked in steps of 64 positions (lane l
+// of step s holds p0 + 64*s + l); the first kPre steps are requested up front.
+struct Part {
+    int64_t p0, p1;
+    uint32_t x[kPre];
+};
+
+__device__ __forceinline__ void load_part(Part& pt, const uint32_t* ks, int lane) {
+    const int64_t last = pt.p1 > pt.p0 ? pt.p1 - 1 : 0;
+#pragma unroll
+    for (int s = 0; s < kPre; ++s) pt.x[s] = ks[min(pt.p0 + 64 * s + lane, last)];
+}
+
+// f(i, code) for every lane's position of every step, in step order (all lanes
+// call it; positions at or past p1 get some in-range code).
+template <class F>
+__device__ __forceinline__ void part_walk(const Part& pt, const uint32_t* ks, int lane, F&& f) {
+#pragma unroll
+    for (int s = 0; s < kPre; ++s)
+        if (pt.p0 + 64 * s < pt.p1) f(pt.p0 + 64 * s + lane, pt.x[s]);
+    for (int64_t p = pt.p0 + 64 * kPre; p < pt.p1; p += 64) f(p + lane, ks[min(p + lane, pt.p1 - 1)]);
+}
+
+// Ties (d == t) in a part.
+__device__ __forceinline__ int part_ties(const Part& pt, const uint32_t* ks, uint32_t q, int t, int lane) {
+    int ties = 0;
+    part_walk(pt, ks, lane, [&](int64_t i, uint32_t x) {
+        ties += __popcll(__ballot(i < pt.p1 && (int)__builtin_popcount(x ^ q) == t));
+    });
+    return ties;
+}
+
+// Positions of a part in the top m, given that tie_base ties of the chunk come
+// before the part and the chunk takes its first `taken` ties.
+__device__ __forceinline__ int part_top(const Part& pt, const uint32_t* ks, uint32_t q, int t, int tie_base, int taken,
+                                        int lane) {
+    int top = 0, carry = tie_base;
+    part_walk(pt, ks, lane, [&](int64_t i, uint32_t x) {
+        const int d = (int)__builtin_popcount(x ^ q);
+        const bool ok = i < pt.p1;
+        const uint64_t tm = __ballot(ok && d == t);
+        const int rank = carry + mbcnt64(tm);
+        top += __popcll(__ballot(ok && (d < t || (d == t && rank < taken))));
+        carry += __popcll(tm);
+    });
+    return top;
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ int wave_excl_scan_i(int x, int lane) {
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    return inc - x;
+}
+
+__device__ void select_head(const TopkArgs& a, int b, int h, int g, int lane, uint32_t* tr /*[kBins][65]*/) {
+    const int64_t row = (int64_t)b * a.Hq + h * a.G + g;
+    const int64_t n = a.n;
+    const int C = a.chunks;
+    const int64_t len = a.chunk_len;
+    const uint32_t q = a.q_sigs[row];
+    const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * n;
+    const int64_t s_end = min(a.n_sink, n);
+    const int64_t r_beg = max(max((int64_t)0, n - a.n_recent), s_end);
+
+    // Chunks cut by a window edge and the window part of each: the prefix
+    // [cs*len, s_end) of the sink-cut chunk and the suffix [r_beg, end of cr) of
+    // the recent-cut chunk.  Their codes do not depend on t: request them first.
+    const int cs = (s_end > 0 && s_end < n && s_end % len != 0) ? (int)(s_end / len) : -1;
+    const int cr = (r_beg < n && r_beg % len != 0) ? (int)(r_beg / len) : -1;
+    Part ps, pr;
+    ps.p0 = cs >= 0 ? cs * len : 0;
+    ps.p1 = cs >= 0 ? s_end : 0;
+    pr.p0 = cr >= 0 ? r_beg : 0;
+    pr.p1 = cr >= 0 ? min(n, (cr + 1) * len) : 0;
+    load_part(ps, ks, lane);
+    load_part(pr, ks, lane);
+
+    // This lane's chunk histogram.
+    uint32_t hv[kBins];
+    {
+        const u32x4* hrow = reinterpret_cast<const u32x4*>(a.hist + (row * C + min(lane, C - 1)) * kRow);
+#pragma unroll
+        for (int k = 0; k < kRow / 4; ++k) {
+            const u32x4 v = hrow[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * k + e < kBins) hv[4 * k + e] = lane < C ? v[e] : 0u;
+        }
+    }
+    // The head's histogram: bins transposed through LDS, lane d (< 33) sums bin d.
+#pragma unroll
+    for (int d = 0; d < kBins; ++d) tr[d * 65 + lane] = hv[d];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    int64_t hsum = 0;
+    if (lane < kBins) {
+#pragma unroll 8
+        for (int l = 0; l < 64; ++l) hsum += tr[lane * 65 + l];
+    }
+    // t = the first bin whose inclusive prefix reaches m; quota = what it must give (t = -1: m = 0).
+    const int64_t meff = min(a.m, n);
+    int64_t incl = hsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    const uint64_t reach = __ballot(lane < kBins && meff > 0 && incl >= meff);
+    const int t = reach ? (int)__builtin_ctzll(reach) : -1;
+    const int64_t quota = t >= 0 ? meff - (__shfl(incl, t, 64) - __shfl(hsum, t, 64)) : 0;
+    int below = 0, ties = 0;
+#pragma unroll
+    for (int d = 0; d < kBins; ++d) {
+        below += d < t ? (int)hv[d] : 0;
+        ties = d == t ? (int)hv[d] : ties;
+    }
+    const int ties_before = wave_excl_scan_i(ties, lane);
+    const int taken = t < 0 ? 0 : (int)min(max(quota - ties_before, (int64_t)0), (int64_t)ties);
+
+    // Window positions outside the top m in the cut chunks.
+    int extra_s = 0, extra_r = 0;
+    if (cs >= 0) {
+        const int tk = __shfl(taken, cs, 64);
+        extra_s = (int)(ps.p1 - ps.p0) - part_top(ps, ks, q, t, 0, tk, lane);
+    }
+    if (cr >= 0) {
+        const int tk = __shfl(taken, cr, 64);
+        const int tie_c = __shfl(ties, cr, 64);
+        const int tsuf = part_ties(pr, ks, q, t, lane);
+        extra_r = (int)(pr.p1 - pr.p0) - part_top(pr, ks, q, t, tie_c - tsuf, tk, lane);
+    }
+
+    const int64_t cb = lane * len, ce = min(n, cb + len);
+    int cnt = 0;
+    if (lane < C) {
+        if (ce <= s_end || cb >= r_beg) cnt = (int)(ce - cb);   // entirely inside a window
+        else cnt = below + taken + (lane == cs ? extra_s : 0) + (lane == cr ? extra_r : 0);
+    }
+    const int off = wave_excl_scan_i(cnt, lane);
+    const int total = wave_sum_i(cnt);
+    if (lane < C) {
+        int32_t* ci = a.chunk_info + (row * C + lane) * 4;
+        ci[0] = off;
+        ci[1] = taken;
+        ci[2] = ties;
+    }
+    if (lane == 0) {
+        a.count[row] = total;
+        a.head_info[2 * row] = t;
+        a.head_info[2 * row + 1] = (int32_t)quota;
+    }
+    for (int64_t i = total + lane; i < a.cap; i += 64) a.idx[row * a.cap + i] = -1;
+}
+
+// ---- 1. histogram ------------------------------------------------------------------
+// LDS cnt[lane][g][bin], with a spare bin 33 for positions past the end and an
+// odd row stride: the 64 lanes of one increment hit 64 different words spread
+// over the banks.
+template <int MAXG>
+struct HistSmem {
+    static constexpr int kStride = MAXG * (kBins + 1) + 1;
+    uint32_t cnt[64 * kStride];
+};
+
 template <int MAXG, bool VEC, bool SCORES>
-__global__ __launch_bounds__(64) void k_sig_hist(TopkArgs a) {
-    __shared__ uint32_t cnt[MAXG * (kBins + 1) * kBinStride];   // [g][bin][copy]
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
+    __shared__ HistSmem<MAXG> sm;
+    constexpr int S = HistSmem<MAXG>::kStride;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int G = a.G;
     const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * a.n;
-    const int beg = c * kChunk;
-    const int end = (int)min(a.n, (int64_t)beg + kChunk);
+    const int64_t beg = (int64_t)c * a.chunk_len;
+    const int64_t end = min(a.n, beg + a.chunk_len);
 
-    // Straight-line loads of clamped addresses (no branch between them, so
-    // they are all in flight at once).
-    u32x4 x[kPerLane / 4];
-#pragma unroll
-    for (int u = 0; u < kPerLane / 4; ++u) {
-        const int i = beg + 4 * (lane + 64 * u);
-        if (VEC) {
-            x[u] = ld16(ks + min(i, end - 4));
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[u][e] = ks[min(i + e, end - 1)];
-        }
-    }
-    for (int k = lane; k < G * (kBins + 1) * kBinStride; k += 64) cnt[k] = 0;
+    uint32_t x[16];
+    load_sub<VEC>(x, ks, beg, end, tid);
+    for (int k = tid; k < 64 * S; k += 256) sm.cnt[k] = 0;
     uint32_t qs[MAXG];
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) qs[g] = g < G ? a.q_sigs[(int64_t)b * a.Hq + h * G + g] : 0u;
     __syncthreads();
 
-    uint32_t* my = cnt + lane % kCopies;
-    const bool full = end - beg == kChunk;
+    uint32_t* my = sm.cnt + lane * S;
+    for (int64_t sb = beg; sb < end; sb += kSub) {
+        if (sb != beg) load_sub<VEC>(x, ks, sb, end, tid);
 #pragma unroll
-    for (int u = 0; u < kPerLane / 4; ++u) {
-        const int i = beg + 4 * (lane + 64 * u);
+        for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool ok = full || i + e < end;
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = sb + 4 * (tid + 256 * u) + e;
+                const bool ok = i < end;
 #pragma unroll
-            for (int g = 0; g < MAXG; ++g) {
-                if (g < G) {
-                    const uint32_t d = __builtin_popcount(x[u][e] ^ qs[g]);
-                    const uint32_t bin = ok ? d : (uint32_t)kBins;
-                    __hip_atomic_fetch_add(my + (g * (kBins + 1) + bin) * kBinStride, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-                    if (SCORES && ok) a.scores[((int64_t)b * a.Hq + h * G + g) * a.n + i + e] = (int8_t)(-(int)d);
+                for (int g = 0; g < MAXG; ++g) {
+                    if (g < G) {
+                        const uint32_t d = __builtin_popcount(x[4 * u + e] ^ qs[g]);
+                        __hip_atomic_fetch_add(my + g * (kBins + 1) + (ok ? d : (uint32_t)kBins), 1u,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if (SCORES && ok)
+                            a.scores[((int64_t)b * a.Hq + h * G + g) * a.n + i] = (int8_t)(-(int)d);
+                    }
                 }
             }
         }
     }
     __syncthreads();
-    for (int row = lane; row < G * kBins; row += 64) {
-        const int g = row / kBins, bin = row % kBins;
+    // Sum the 64 copies.
+    for (int k = tid; k < G * kBins; k += 256) {
+        const int g = k / kBins, bin = k % kBins;
         uint32_t sum = 0;
-#pragma unroll
-        for (int k = 0; k < kCopies; ++k) sum += cnt[(g * (kBins + 1) + bin) * kBinStride + k];
-        a.hist[(((int64_t)b * a.Hq + h * G + g) * a.chunks + c) * kBins + bin] = sum;
+#pragma unroll 8
+        for (int l = 0; l < 64; ++l) sum += sm.cnt[l * S + g * (kBins + 1) + bin];
+        a.hist[(((int64_t)b * a.Hq + h * G + g) * a.chunks + c) * kRow + bin] = sum;
     }
 }
 
-// ---- block-wide helpers (256 threads) -----------------------------------------
-__device__ int64_t block_exclusive_scan(int64_t x, int64_t* total, int64_t* sh /*[4]*/) {
+__global__ __launch_bounds__(256) void k_topk_select(TopkArgs a) {
+    __shared__ uint32_t tr[4][kBins * 65];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int64_t inc = x;
+    const int h = blockIdx.x, b = blockIdx.y;
+    for (int g = w; g < a.G; g += 4) select_head(a, b, h, g, lane, tr[w]);
+}
+
+// n == 0: no positions; every row gets count 0 and is padded with -1.
+__global__ __launch_bounds__(64) void k_topk_empty(TopkArgs a) {
+    const int64_t row = (int64_t)blockIdx.y * a.Hq + blockIdx.x;
+    if (threadIdx.x == 0) a.count[row] = 0;
+    for (int64_t i = threadIdx.x; i < a.cap; i += 64) a.idx[row * a.cap + i] = -1;
+}
+
+// ---- 3. ordered compaction -------------------------------------------------------
+// Thread tid owns the 16 consecutive positions sb + 16*tid + j of a sub-chunk.
+// Per query head it forms 16-bit masks (below t, ties, and, for a chunk a
+// window meets, window positions), the selection mask, and its popcount; one
+// block-wide exclusive scan of the counts (four heads packed in 16-bit fields of
+// a 64-bit word) places every thread's positions, which it then stores in order.
+// A head that takes only some of the chunk's ties first needs the ties before
+// each thread: a second packed scan, run only when some head does.
+template <bool VEC>
+__device__ __forceinline__ void load_run(uint32_t (&x)[16], const uint32_t* ks, int64_t sb, int64_t end, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = sb + 16 * tid + 4 * u;
+        if (VEC) {
+            const u32x4 v = ld16(ks + min(i, end - 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * u + e] = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * u + e] = ks[min(i + e, end - 1)];
+        }
+    }
+}
+
+// Block-wide (256 threads) exclusive scan of a 64-bit word of four 16-bit
+// counts; total gets the block sums.  sh: 4 words of LDS.
+__device__ __forceinline__ uint64_t block_scan_packed(uint64_t v, uint64_t* total, uint64_t* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint64_t inc = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = __shfl_up(inc, o, 64);
+        const uint64_t y = __shfl_up(inc, o, 64);
         if (lane >= o) inc += y;
     }
     if (lane == 63) sh[w] = inc;
     __syncthreads();
-    int64_t base = 0, all = 0;
-    for (int ww = 0; ww < 4; ++ww) {
-        if (ww < w) base += sh[ww];
-        all += sh[ww];
+    uint64_t base = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint64_t t = sh[k];
+        base += k < w ? t : 0;
+        all += t;
     }
-    __syncthreads();
+    __syncthreads();   // sh is reused by the next scan
     *total = all;
-    return base + inc - x;
+    return base + inc - v;
 }
 
-// The 16 codes [i0, i0 + 16) (zeros at and past end).
-// The 16 codes [i0, i0 + 16) of a chunk [.., end) with end > 0; entries at or
-// past end hold some in-range code and must be ignored by the caller.
-__device__ __forceinline__ void load16(const uint32_t* ks, int64_t i0, int64_t end, bool vec, uint32_t (&x)[16]) {
-    if (vec) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const u32x4 v = ld16(ks + min(i0 + 4 * u, end - 4));
-            x[4 * u] = v[0];
-            x[4 * u + 1] = v[1];
-            x[4 * u + 2] = v[2];
-            x[4 * u + 3] = v[3];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = ks[min(i0 + e, end - 1)];
+__device__ __forceinline__ uint32_t field16(uint64_t v, int k) { return (uint32_t)(v >> (16 * k)) & 0xFFFFu; }
+
+// The lowest `take` set bits of m.
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t m, int take) {
+    uint32_t r = 0;
+    for (int j = 0; j < take && m; ++j) {
+        const uint32_t low = m & (0u - m);
+        r |= low;
+        m ^= low;
     }
+    return r;
 }
 
-// ---- 2. threshold, windows, offsets -----------------------------------------
-constexpr int kSelHist = 8448;   // histogram words staged in LDS (256 chunks x 33 bins)
-
-__global__ __launch_bounds__(256) void k_topk_select(TopkArgs a) {
-    __shared__ uint32_t H[kBins];
-    __shared__ uint32_t s_hist[kSelHist];
-    __shared__ int64_t scan_sh[4];
-    __shared__ int s_t;
-    __shared__ int64_t s_quota, s_cstar, s_rank, s_pt, s_extra[2];
+template <int MAXG, bool VEC>
+__global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
+    constexpr int kPacks = (MAXG + 3) / 4;
+    __shared__ uint64_t scan_sh[4];
     const int tid = threadIdx.x;
-    const int hq = blockIdx.x, b = blockIdx.y;
-    const int h = hq / a.G;
-    const int64_t row = (int64_t)b * a.Hq + hq;
-    const uint32_t* hist = a.hist + row * a.chunks * kBins;
-    const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * a.n;
-    const uint32_t qsig = a.q_sigs[row];
-    const int C = a.chunks;
-    const int64_t n = a.n;
-    const bool vec = (n % 4) == 0;
-    const bool staged = C * kBins <= kSelHist;
-
-    // Windows [0, s_end) and [r_beg, n).  A chunk entirely inside a window is
-    // selected whole; a chunk cut by a window edge gets the window positions it
-    // holds outside the top m added (at most two such chunks).  Their codes are
-    // requested first: they do not depend on the threshold.
-    const int64_t s_end = min(a.n_sink, n);
-    const int64_t r_beg = max(max((int64_t)0, n - a.n_recent), s_end);
-    int64_t cut[2] = {-1, -1};
-    if (s_end > 0 && s_end % kChunk != 0 && s_end < n) cut[0] = s_end / kChunk;
-    if (r_beg < n && r_beg % kChunk != 0) cut[1] = r_beg / kChunk;
-    if (cut[1] == cut[0]) cut[1] = -1;
-    uint32_t xcut[2][16];
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-        if (cut[k] >= 0) load16(ks, cut[k] * kChunk + 16 * tid, min(n, cut[k] * kChunk + (int64_t)kChunk), vec, xcut[k]);
-
-    if (tid < kBins) H[tid] = 0;
-    __syncthreads();
-    for (int e = tid; e < C * kBins; e += 256) {
-        const uint32_t v = hist[e];
-        if (staged) s_hist[e] = v;
-        atomicAdd(&H[e % kBins], v);
-    }
-    __syncthreads();
-    auto hist_at = [&](int64_t c, int d) -> uint32_t {
-        return staged ? s_hist[c * kBins + d] : hist[c * kBins + d];
-    };
-    if (tid == 0) {
-        const int64_t meff = min(a.m, n);
-        int t = -1;
-        int64_t cum = 0, quota = 0;
-        if (meff > 0) {
-            for (int d = 0; d < kBins; ++d) {
-                if (cum + (int64_t)H[d] >= meff) {
-                    t = d;
-                    quota = meff - cum;
-                    break;
-                }
-                cum += H[d];
-            }
-        }
-        s_t = t;
-        s_quota = quota;
-        s_cstar = -1;
-        s_rank = 0;
-        s_pt = -1;
-        s_extra[0] = 0;
-        s_extra[1] = 0;
-    }
-    __syncthreads();
-    const int t = s_t;
-    const int64_t quota = s_quota;
-
-    // Chunk c* holding the quota-th tie (distance t), its rank there, and its position p.
-    if (t >= 0) {
-        int64_t carry = 0;
-        for (int c0 = 0; c0 < C; c0 += 256) {
-            const int c = c0 + tid;
-            const int64_t eq = c < C ? hist_at(c, t) : 0;
-            int64_t tot;
-            const int64_t pre = carry + block_exclusive_scan(eq, &tot, scan_sh);
-            if (c < C && pre < quota && quota <= pre + eq) {
-                s_cstar = c;
-                s_rank = quota - pre;   // 1-based rank inside chunk c
-            }
-            carry += tot;
-        }
-        __syncthreads();
-        const int64_t cs = s_cstar;
-        int64_t cnt = 0;
-        uint32_t x[16];
-        const int64_t i0 = cs * kChunk + 16 * tid;
-        const int64_t cend = min(n, cs * kChunk + (int64_t)kChunk);
-        if (cs >= 0) {
-            load16(ks, i0, cend, vec, x);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) cnt += (i0 + e < cend) && (__builtin_popcount(x[e] ^ qsig) == (uint32_t)t);
-        }
-        int64_t tot;
-        const int64_t pre = block_exclusive_scan(cnt, &tot, scan_sh);
-        const int64_t want = s_rank;
-        if (cs >= 0 && pre < want && want <= pre + cnt) {
-            int64_t r = pre;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                if (i0 + e < cend && __builtin_popcount(x[e] ^ qsig) == (uint32_t)t) {
-                    ++r;
-                    if (r == want) s_pt = i0 + e;
-                }
-            }
-        }
-        __syncthreads();
-    }
-    const int64_t cstar = s_cstar, rank_in = s_rank;
-    const int64_t p1 = s_pt + 1;   // ties at positions < p1 are taken
-
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (cut[k] < 0) continue;   // uniform across the block
-        const int64_t cb = cut[k] * kChunk;
-        const int64_t ce = min(n, cb + (int64_t)kChunk);
-        const int64_t i0 = cb + 16 * tid;
-        int64_t ex = 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t i = i0 + e;
-            const int d = __builtin_popcount(xcut[k][e] ^ qsig);
-            const bool top = d < t || (d == t && i < p1);
-            if (i < ce && (i < s_end || i >= r_beg) && !top) ++ex;
-        }
-        int64_t tot;
-        block_exclusive_scan(ex, &tot, scan_sh);
-        if (tid == 0) s_extra[k] = tot;
-        __syncthreads();
-    }
-
-    int64_t carry = 0;
-    for (int c0 = 0; c0 < C; c0 += 256) {
-        const int c = c0 + tid;
-        int64_t cnt = 0;
-        if (c < C) {
-            const int64_t cb = (int64_t)c * kChunk, ce = min(n, cb + (int64_t)kChunk);
-            if (ce <= s_end || cb >= r_beg) {
-                cnt = ce - cb;   // entirely inside a window
-            } else {
-                for (int d = 0; d < t; ++d) cnt += hist_at(c, d);
-                if (t >= 0) cnt += (c < cstar) ? (int64_t)hist_at(c, t) : (c == cstar ? rank_in : 0);
-                if (c == cut[0]) cnt += s_extra[0];
-                if (c == cut[1]) cnt += s_extra[1];
-            }
-        }
-        int64_t tot;
-        const int64_t off = carry + block_exclusive_scan(cnt, &tot, scan_sh);
-        if (c < C) a.chunk_info[row * C + c] = (int32_t)off;
-        carry += tot;
-    }
-    if (tid == 0) {
-        a.count[row] = (int32_t)carry;
-        a.head_info[2 * row] = t;
-        a.head_info[2 * row + 1] = (int32_t)p1;
-    }
-    for (int64_t i = carry + tid; i < a.cap; i += 256) a.idx[row * a.cap + i] = -1;
-}
-
-// ---- 3. ordered compaction ----------------------------------------------------
-// The chunk is walked in 4 quarters of 1024 positions; in a quarter lane l holds
-// positions base + l + 64*u, u < 16.  The next quarter is requested before the
-// current one is processed.  Positions are 32-bit.
-constexpr int kQuarter = kChunk / 4;
-
-template <int MAXG>
-struct CompactState {
-    uint32_t qs[MAXG];
-    int tt[MAXG];
-    int p1[MAXG], off[MAXG];
-};
-
-__device__ __forceinline__ void load_quarter(uint32_t (&x)[16], const uint32_t* ks, int base, int end, int lane) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) x[u] = ks[min(base + lane + 64 * u, end - 1)];   // clamped; masked by the caller
-}
-
-template <int MAXG>
-__device__ __forceinline__ void compact_quarter(const TopkArgs& a, CompactState<MAXG>& st, const uint32_t (&x)[16],
-                                                int base, int end, int64_t row0, int s_end, int r_beg, int lane) {
-    const int G = a.G;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int i = base + lane + 64 * u;
-        const bool valid = i < end;
-        const bool win = i < s_end || i >= r_beg;
-#pragma unroll
-        for (int g = 0; g < MAXG; ++g) {
-            if (g < G) {
-                const int d = __builtin_popcount(x[u] ^ st.qs[g]);
-                const int t_eff = st.tt[g] + (i < st.p1[g] ? 1 : 0);   // ties before p1 are in the top m
-                const bool sel = valid && (win || d < t_eff);
-                const uint64_t mask = __ballot(sel);
-                if (mask) {
-                    const int pos = st.off[g] + (int)__builtin_amdgcn_mbcnt_hi(
-                                                    (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                    if (sel && pos < a.cap) a.idx[(row0 + g) * a.cap + pos] = i;
-                    st.off[g] += __popcll(mask);
-                }
-            }
-        }
-    }
-}
-
-template <int MAXG>
-__global__ __launch_bounds__(64) void k_sig_compact(TopkArgs a) {
-    const int lane = threadIdx.x;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int G = a.G;
-    const int64_t row0 = (int64_t)b * a.Hq + h * G;
     const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * a.n;
-    const int beg = c * kChunk;
-    const int end = (int)min(a.n, (int64_t)beg + kChunk);
+    const int64_t beg = (int64_t)c * a.chunk_len;
+    const int64_t end = min(a.n, beg + a.chunk_len);
+    const int64_t s_end = min(a.n_sink, a.n);
+    const int64_t r_beg = max((int64_t)0, a.n - a.n_recent);
+    const bool meets_win = beg < s_end || end > r_beg;   // uniform
+    const int64_t row0 = (int64_t)b * a.Hq + h * G;
 
-    uint32_t xa[16], xb[16];
-    load_quarter(xa, ks, beg, end, lane);
-    CompactState<MAXG> st;
+    uint32_t x[16];
+    load_run<VEC>(x, ks, beg, end, tid);
+    uint32_t q[MAXG];
+    int t[MAXG], off[MAXG], taken[MAXG], mode[MAXG];   // mode: 0 no ties, 1 all ties, 2 some ties
+    int tie_carry[MAXG];
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
-        if (g < G) {
-            st.qs[g] = a.q_sigs[row0 + g];
-            st.tt[g] = a.head_info[2 * (row0 + g)];
-            st.p1[g] = a.head_info[2 * (row0 + g) + 1];
-            st.off[g] = a.chunk_info[(row0 + g) * a.chunks + c];
-        } else {
-            st.qs[g] = 0;
-            st.tt[g] = -1;
-            st.p1[g] = 0;
-            st.off[g] = 0;
-        }
+        const int gg = min(g, G - 1);
+        const int32_t* ci = a.chunk_info + ((row0 + gg) * a.chunks + c) * 4;
+        q[g] = a.q_sigs[row0 + gg];
+        t[g] = a.head_info[2 * (row0 + gg)];
+        off[g] = ci[0];
+        taken[g] = ci[1];
+        const int ties = ci[2];
+        mode[g] = (t[g] < 0 || taken[g] == 0) ? 0 : (taken[g] == ties ? 1 : 2);
+        tie_carry[g] = 0;
     }
-    const int s_end = (int)min(a.n_sink, a.n), r_beg = (int)max((int64_t)0, a.n - a.n_recent);
-    for (int q = 0; q < 4; q += 2) {
-        const int b0 = beg + q * kQuarter, b1 = b0 + kQuarter;
-        load_quarter(xb, ks, b1, end, lane);
-        compact_quarter<MAXG>(a, st, xa, b0, end, row0, s_end, r_beg, lane);
-        if (q + 2 < 4) load_quarter(xa, ks, b1 + kQuarter, end, lane);
-        compact_quarter<MAXG>(a, st, xb, b1, end, row0, s_end, r_beg, lane);
+    bool partial = false;   // uniform: every thread read the same chunk records
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) partial |= g < G && mode[g] == 2;
+    for (int64_t sb = beg; sb < end; sb += kSub) {
+        if (sb != beg) load_run<VEC>(x, ks, sb, end, tid);
+        const int64_t i0 = sb + 16 * tid;
+        const int nv = (int)max((int64_t)0, min((int64_t)16, end - i0));   // valid positions of this thread
+        const uint32_t valid = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
+        uint32_t win = 0;
+        if (meets_win) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) win |= (uint32_t)(i0 + j < s_end || i0 + j >= r_beg) << j;
+            win &= valid;
+        }
+        uint32_t lt[MAXG], tie[MAXG];
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g) {
+            lt[g] = 0;
+            tie[g] = 0;
+            if (g < G) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int d = (int)__builtin_popcount(x[j] ^ q[g]);
+                    lt[g] |= (uint32_t)(d < t[g]) << j;
+                    tie[g] |= (uint32_t)(d == t[g]) << j;
+                }
+                lt[g] &= valid;
+                tie[g] &= valid;
+            }
+        }
+        // Ties before this thread in the chunk, for heads taking only some of them.
+        int tie_before[MAXG];
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g) tie_before[g] = tie_carry[g];
+        if (partial) {
+#pragma unroll
+            for (int p = 0; p < kPacks; ++p) {
+                uint64_t v = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (4 * p + k < MAXG) v |= (uint64_t)__builtin_popcount(tie[4 * p + k]) << (16 * k);
+                uint64_t tot;
+                const uint64_t ex = block_scan_packed(v, &tot, scan_sh);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (4 * p + k < MAXG) {
+                        tie_before[4 * p + k] += (int)field16(ex, k);
+                        tie_carry[4 * p + k] += (int)field16(tot, k);
+                    }
+                }
+            }
+        }
+        uint32_t sel[MAXG];
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g) {
+            uint32_t tk = 0;
+            if (mode[g] == 1) tk = tie[g];
+            else if (mode[g] == 2) tk = lowest_bits(tie[g], min(max(taken[g] - tie_before[g], 0), 16));
+            sel[g] = g < G ? (win | lt[g] | tk) : 0u;
+        }
+#pragma unroll
+        for (int p = 0; p < kPacks; ++p) {
+            uint64_t v = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (4 * p + k < MAXG) v |= (uint64_t)__builtin_popcount(sel[4 * p + k]) << (16 * k);
+            uint64_t tot;
+            const uint64_t ex = block_scan_packed(v, &tot, scan_sh);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int g = 4 * p + k;
+                if (g < G) {
+                    int32_t* out = a.idx + (row0 + g) * a.cap;
+                    int pos = off[g] + (int)field16(ex, k);
+                    uint32_t m = sel[g];
+                    while (m) {
+                        const int j = __builtin_ctz(m);
+                        if (pos < a.cap) out[pos] = (int32_t)(i0 + j);
+                        ++pos;
+                        m &= m - 1u;
+                    }
+                    off[g] += (int)field16(tot, k);
+                }
+            }
+        }
     }
 }
 
 }  // namespace
 
-int topk_chunk_len(int64_t) { return kChunk; }
+int topk_chunk_len(int64_t n) {
+    const int64_t per = (int64_t)kSub * kMaxChunks;
+    const int64_t subs = n > 0 ? (n + per - 1) / per : 1;
+    return (int)(subs * kSub);
+}
+
+int topk_hist_row() { return kRow; }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     if (a.B <= 0) return hipSuccess;
-    if (a.G > kMaxG) return hipErrorInvalidValue;
-    const dim3 gc(a.chunks, a.Hkv, a.B);
-    hipError_t e;
-    if (a.chunks > 0) {
-        const bool vec = a.n % 4 == 0;
-        const bool sc = a.scores != nullptr;
-#define LCDA_HIST(MG, V, S) hipLaunchKernelGGL((k_sig_hist<MG, V, S>), gc, dim3(64), 0, st, a)
-        if (a.G <= 4) {
-            if (vec) { if (sc) LCDA_HIST(4, true, true); else LCDA_HIST(4, true, false); }
-            else { if (sc) LCDA_HIST(4, false, true); else LCDA_HIST(4, false, false); }
-        } else {
-            if (vec) { if (sc) LCDA_HIST(8, true, true); else LCDA_HIST(8, true, false); }
-            else { if (sc) LCDA_HIST(8, false, true); else LCDA_HIST(8, false, false); }
-        }
-#undef LCDA_HIST
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    if (a.G > 8 || a.chunks > kMaxChunks) return hipErrorInvalidValue;
+    if (a.chunks == 0) {
+        hipLaunchKernelGGL(k_topk_empty, dim3(a.Hq, a.B), dim3(64), 0, st, a);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_topk_select, dim3(a.Hq, a.B), dim3(256), 0, st, a);
+    const dim3 grid(a.chunks, a.Hkv, a.B), block(256);
+    const bool vec = a.n % 4 == 0;
+    const bool sc = a.scores != nullptr;
+#define LCDA_HIST(MG, V, S) hipLaunchKernelGGL((k_topk_hist<MG, V, S>), grid, block, 0, st, a)
+    if (a.G <= 4) {
+        if (vec) { if (sc) LCDA_HIST(4, true, true); else LCDA_HIST(4, true, false); }
+        else { if (sc) LCDA_HIST(4, false, true); else LCDA_HIST(4, false, false); }
+    } else {
+        if (vec) { if (sc) LCDA_HIST(8, true, true); else LCDA_HIST(8, true, false); }
+        else { if (sc) LCDA_HIST(8, false, true); else LCDA_HIST(8, false, false); }
+    }
+#undef LCDA_HIST
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_topk_select, dim3(a.Hkv, a.B), dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.chunks > 0) {
-        if (a.G <= 4) hipLaunchKernelGGL(k_sig_compact<4>, gc, dim3(64), 0, st, a);
-        else hipLaunchKernelGGL(k_sig_compact<8>, gc, dim3(64), 0, st, a);
+    if (a.G <= 4) {
+        if (vec) hipLaunchKernelGGL((k_topk_compact<4, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_topk_compact<4, false>), grid, block, 0, st, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_topk_compact<8, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_topk_compact<8, false>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }

@@ -89,18 +89,21 @@ constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format,
 
 // Block of 32 tokens starting at unified token t: returns the rows of it that
 // hold tokens (1..32) and requests all 32 rows; rows past the segment's end
-// read as zero.  koff = 256*c16 + 16*j (K row c16 of each 16-token half);
-// voff = 1024*j + 16*c16 (V row 4j): the V rows tok_of(j, e) are 4j + e and
-// 16 + 4j + (e - 4).
+// read as zero.  With live == false (a request past the end of the wave's
+// range, issued so that every loop step has the same loads outstanding) the
+// resource is empty: the loads return zeros and touch no memory.
+// koff = 256*c16 + 16*j (K row c16 of each 16-token half); voff = 1024*j +
+// 16*c16 (V row 4j): the V rows tok_of(j, e) are 4j + e and 16 + 4j + (e - 4).
 template <bool NTL, bool FUSED>
-__device__ __forceinline__ int load_block(BlockRegs& r, const Segs& sg, int64_t t, uint32_t koff, uint32_t voff) {
+__device__ __forceinline__ int load_block(BlockRegs& r, const Segs& sg, int64_t t, bool live, uint32_t koff,
+                                          uint32_t voff) {
     const bool second = FUSED && t >= sg.n_c_al;
     const uint16_t* kseg = second ? sg.kh2 : sg.kh;
     const uint16_t* vseg = second ? sg.vh2 : sg.vh;
     const int64_t row = second ? t - sg.n_c_al : t;
     const int64_t left = (second ? sg.n_eff - sg.n_c_al : (FUSED ? sg.n_c : sg.n_eff)) - row;
     const int valid = (int)(left < kBlock ? left : kBlock);
-    const int nrec = valid * kD * 2;
+    const int nrec = live ? valid * kD * 2 : 0;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kseg + row * kD), 0, nrec, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv =
@@ -292,15 +295,15 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_mfma(SplitArgs a) {
     // Request the first DEPTH blocks, then drain everything issued so far (the
     // query fragments, the merge inputs and these blocks), so that inside the
     // loop only the loop's own block loads are ever outstanding.  Past the end
-    // of the range the current block is requested again (cache-resident),
-    // which keeps the number of loads per step uniform.
+    // of the range an empty request is issued (no memory is read), which keeps
+    // the number of loads per step uniform.
     BlockRegs buf[DEPTH + 1];
     int valid[DEPTH + 1];
     if (t < t_end) {
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) {
             const int64_t tu = t + u * step;
-            valid[u] = load_block<NTL, FUSED>(buf[u], sg, tu < t_end ? tu : t, koff, voff);
+            valid[u] = load_block<NTL, FUSED>(buf[u], sg, tu < t_end ? tu : t, tu < t_end, koff, voff);
         }
     }
     wait_vm_all();
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_mfma(SplitArgs a) {
                 if (!done) {
                     const int64_t tn = t + DEPTH * step;
                     const int nx = (u + DEPTH) % (DEPTH + 1);
-                    valid[nx] = load_block<NTL, FUSED>(buf[nx], sg, tn < t_end ? tn : t, koff, voff);
+                    valid[nx] = load_block<NTL, FUSED>(buf[nx], sg, tn < t_end ? tn : t, tn < t_end, koff, voff);
                     // Keep every load of the block ahead above the first use of the current one.
                     __builtin_amdgcn_sched_barrier(0);
                     compute_block<NT>(st, buf[u], valid[u], a.scale_log2, j, c16);

@@ -56,6 +56,14 @@ def test_topk_shapes(orc, n, m, s, r):
     _topk_case(orc, 2, 8, 2, n, m, s, r, 10 + n + m)
 
 
+@pytest.mark.parametrize("n,m,s,r", [(300001, 5000, 5000, 3000), (270000, 4096, 128, 128), (524288, 8192, 128, 128),
+                                     (524288, 100, 9000, 70000)])
+def test_topk_long(orc, n, m, s, r):
+    """Chunks of several 4096-position sub-chunks (n > 262,144), the 64-chunk maximum, and window parts
+    longer than the prefetched 512 positions."""
+    _topk_case(orc, 1, 8, 2, n, m, s, r, 20 + n % 97, scores=False)
+
+
 @pytest.mark.parametrize("pool", [1, 2, 5])
 def test_topk_massive_ties(orc, pool):
     """Few distinct signatures: almost every position ties; the lower position must win."""
