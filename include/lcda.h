@@ -187,6 +187,12 @@ const char* lcda_version(void);
  *   "dense_wgs_nt4"  target workgroups of the MFMA split with 64-row tiles (256)
  *   "valu_wgs"       target workgroups of the fp32 dense split (512)
  *   "gather_wgs"     target workgroups of the GATHER-ATT split (2048)
+ *   "rows_wgs"       target workgroups of the MFMA split with 64 rows per workgroup,
+ *                    used when more than 16 query rows read one KV head (512)
+ *   "rows_kernel"    more than 16 rows per KV head: 1 = 64-row workgroups sharing
+ *                    each block through LDS, 0 = one wavefront per 32 / 64 rows (1)
+ *   "rows_variant"   64-row workgroups: 0 = 4-slot LDS ring, 2 workgroups per CU;
+ *                    1 = 3 slots, 3 per CU; 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU (0)
  *   "direct_blocks"  units with at most this many token blocks run as one split
  *                    that writes its rows directly, without a combine pass (16)
  *   "dense_variant"  MFMA split K/V pipeline (16-row tiles): 0 = nontemporal

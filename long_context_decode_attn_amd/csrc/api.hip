@@ -12,7 +12,6 @@
 
 namespace lcda {
 
-hipError_t launch_split_mfma(const SplitPlan& p, const SplitArgs& a, hipStream_t st);
 hipError_t launch_split_valu(const SplitPlan& p, const SplitArgs& a, int dtype, bool gather, hipStream_t st);
 int valu_step_tokens();
 
@@ -99,8 +98,9 @@ int hip_status(const char* fn, hipError_t e) {
 
 // Launch the split pass, then the combine pass unless the plan has a single
 // split (the split kernel then writes the final rows itself) or the split
-// kernel combines each unit itself (MFMA: the last workgroup of a unit to
-// finish merges its rows).
+// kernel combines each unit itself (kMfma16: the last workgroup of a unit to
+// finish merges its rows; kRows units are too large for that and use the
+// combine pass).
 int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows, float* out, float* alpha,
            const float* a_in, const float* alpha_in, hipStream_t st) {
     a.direct = p.splits == 1 ? 1 : 0;
@@ -168,6 +168,18 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         target = (int)tuning().gather_wgs;
         p.grid_y = Hq;
         p.grid_z = B;
+    } else if (dtype == LCDA_BF16 && rows > 16 && tuning().rows_kernel) {
+        // Many rows per KV head (a shared document): 64 rows per workgroup, every block read once.
+        p.kernel = kRows;
+        p.nt = 1;
+        p.waves = 1;   // the wavefronts split rows, not tokens
+        p.rows_per_group = split_rows_per_group();
+        p.row_groups = (int)ceil_div(rows, p.rows_per_group);
+        p.block = 32;
+        units = bkv * Hkv * p.row_groups;
+        target = (int)tuning().rows_wgs;
+        p.grid_y = Hkv;
+        p.grid_z = bkv * p.row_groups;
     } else if (dtype == LCDA_BF16) {
         p.kernel = kMfma16;
         p.nt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
@@ -205,6 +217,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
 hipError_t launch_split(const SplitPlan& p, const SplitArgs& a, int dtype, hipStream_t st) {
     if (p.grid_x <= 0 || p.grid_y <= 0 || p.grid_z <= 0) return hipSuccess;
     if (p.kernel == kMfma16) return launch_split_mfma(p, a, st);
+    if (p.kernel == kRows) return launch_split_rows(p, a, st);
     return launch_split_valu(p, a, dtype, a.idx != nullptr, st);
 }
 
@@ -226,6 +239,9 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "dense_wgs_nt4") && value > 0) t.dense_wgs_nt4 = value;
     else if (!strcmp(key, "valu_wgs") && value > 0) t.valu_wgs = value;
     else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
+    else if (!strcmp(key, "rows_wgs") && value > 0) t.rows_wgs = value;
+    else if (!strcmp(key, "rows_kernel") && value <= 1) t.rows_kernel = value;
+    else if (!strcmp(key, "rows_variant") && value <= 3) t.rows_variant = value;
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
     else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
@@ -240,6 +256,9 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "dense_wgs_nt4")) return t.dense_wgs_nt4;
     if (!strcmp(key, "valu_wgs")) return t.valu_wgs;
     if (!strcmp(key, "gather_wgs")) return t.gather_wgs;
+    if (!strcmp(key, "rows_wgs")) return t.rows_wgs;
+    if (!strcmp(key, "rows_kernel")) return t.rows_kernel;
+    if (!strcmp(key, "rows_variant")) return t.rows_variant;
     if (!strcmp(key, "direct_blocks")) return t.direct_blocks;
     if (!strcmp(key, "dense_variant")) return t.dense_variant;
     if (!strcmp(key, "gather_variant")) return t.gather_variant;

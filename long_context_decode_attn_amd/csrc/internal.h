@@ -60,6 +60,10 @@ struct Tuning {
     int64_t valu_wgs = 512;        // target workgroups, VALU dense split
     int64_t gather_wgs = 2048;     // target workgroups, GATHER-ATT split
     int64_t direct_blocks = 16;    // at most this many blocks per unit: one split, no combine pass
+    int64_t rows_wgs = 512;        // target workgroups, MFMA split with 64 rows per workgroup (shared document)
+    int64_t rows_kernel = 1;       // bf16 with more than 16 rows per KV head: 1 = 64-row workgroups, 0 = 32/64-row wavefronts
+    int64_t rows_variant = 0;      // 64-row workgroups: 0 = 4-slot ring, 2 per CU; 1 = 3 slots, 3 per CU;
+                                   // 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU
     int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads,
                                    // 2 = two blocks ahead, 3 = nontemporal with two waves per SIMD
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads
@@ -67,7 +71,10 @@ struct Tuning {
 Tuning& tuning();
 
 // Kernel variants for the split partial.
-enum SplitKernel { kMfma16 = 0, kValu = 1 };
+// kMfma16: split_mfma.hip, one wavefront per 16 / 32 query rows, the 4 wavefronts of a workgroup on
+// different blocks.  kRows: split_rows.hip, 64 query rows per workgroup (one 16-row tile per
+// wavefront), every block read once into LDS for all of them.  kValu: split_valu.hip.
+enum SplitKernel { kMfma16 = 0, kValu = 1, kRows = 2 };
 
 struct SplitPlan {
     int kernel;       // SplitKernel
@@ -86,6 +93,9 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
                      bool shared);
 
 hipError_t launch_split(const SplitPlan& p, const SplitArgs& a, int dtype, hipStream_t st);
+hipError_t launch_split_mfma(const SplitPlan& p, const SplitArgs& a, hipStream_t st);
+hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t st);
+int split_rows_per_group();
 
 // LSE combine of `slots` partial states per row (+ an optional virtual pair
 // (a_in, alpha_in) per row) into out [rows, d] and alpha [rows].

@@ -1,0 +1,230 @@
+// split_rows.hip - split-KV partials when many query rows read one KV head: a
+// shared document whose K/V every batch item's G query heads attend to
+// ("Nectar: Neural Estimation of Cached-Token Attention via Regression", slide
+// "A fixed document is expensive to read repeatedly": the document's K/V are
+// fixed and read for every new query).
+//
+// A workgroup owns 64 query rows (4 wavefronts x 16) of one KV head and one
+// token range.  Each 32-token block of that range is brought into an LDS ring
+// once (buffer loads straight to LDS, no registers held while in flight), then
+// every wavefront reads the whole block back in the MFMA lane layout and runs
+// the 16-row tile on its own rows: HBM reads each block once for all 64 rows,
+// and each wavefront keeps only one 16-row tile of state.
+//
+// Ring: kSlots slots of one block; the block kSlots - 1 ahead is requested
+// while the current one is computed.  Each wavefront requests 4 of the block's
+// 16 pieces (lane l of piece i lands at slot + 1024*i + 16*l, the place every
+// wavefront's lane l later reads it from).  The loop's barrier is a bare
+// s_barrier: completion of the ring's own requests is tracked with explicit
+// vmcnt waits, and every other memory operation of the loop is an LDS read
+// that waits for itself.  A block is ready when every
+// wavefront's own pieces have landed (vmcnt) and all have passed the barrier;
+// a slot is refilled only after that barrier, when every wavefront has
+// finished reading the block it held.  Requests past the end of the range use
+// an empty buffer resource, so every step has the same requests outstanding
+// and none of them reads memory.
+
+#include "common.h"
+#include "internal.h"
+#include "mfma_tile.h"
+
+namespace lcda {
+namespace {
+
+constexpr int kSlotBytes = 16384;
+constexpr int kPieces = 4;           // pieces (of 16) each wavefront requests per block
+constexpr int kRowsPerGroup = 16 * kWaves;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt vmcnt(kPieces * (ahead - 1)): this wavefront's pieces of the
+// current block have landed; those of the ahead - 1 younger blocks may still
+// be in flight.  (gfx9 encoding; expcnt and lgkmcnt at their maxima.)
+template <int AHEAD>
+constexpr int vmcnt_ring() {
+    static_assert(kPieces * (AHEAD - 1) < 16, "vmcnt low field");
+    return 0x0F70 | (kPieces * (AHEAD - 1));
+}
+
+// This wavefront's pieces of block t (rows [t, t + 32) of the head) into `slot`.
+template <bool NTL>
+__device__ __forceinline__ void request_block(char* slot, const uint16_t* kh, const uint16_t* vh, int64_t t,
+                                              int64_t n_eff, bool live, int w, uint32_t koff, uint32_t voff) {
+    const int64_t left = n_eff - t;
+    const int nrec = live ? (int)(left < kBlock ? left : kBlock) * kD * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh + t * kD), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vh + t * kD), 0, nrec, kRsrcWord3);
+    constexpr int aux = NTL ? 2 : 0;   // nontemporal
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+        const int i = kPieces * w + p;   // piece 0..7: K (half tb = i / 4, d chunk i % 4); 8..15: V row set e = i - 8
+        lds_ptr_t dst = (lds_ptr_t)(slot + 1024 * i);
+        if (i < 8) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, koff + 4096 * (i / 4) + 64 * (i % 4), 0, 0, aux);
+        } else {
+            const int e = i - 8;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, voff + (e < 4 ? 0 : 4096) + 256 * (e & 3), 0, 0,
+                                                     aux);
+        }
+    }
+}
+
+// This lane's 16 pieces of a slot (addr = slot + 16*lane) into registers; the
+// asm waits for its own LDS reads.  The outputs are early-clobber: a read's
+// destination must never be the address register a later read of the block
+// still uses (the reads complete asynchronously).
+__device__ __forceinline__ void read_block(BlockRegs& r, uint32_t addr) {
+    asm volatile(
+        "ds_read_b128 %0, %16 offset:0\n\t"
+        "ds_read_b128 %1, %16 offset:1024\n\t"
+        "ds_read_b128 %2, %16 offset:2048\n\t"
+        "ds_read_b128 %3, %16 offset:3072\n\t"
+        "ds_read_b128 %4, %16 offset:4096\n\t"
+        "ds_read_b128 %5, %16 offset:5120\n\t"
+        "ds_read_b128 %6, %16 offset:6144\n\t"
+        "ds_read_b128 %7, %16 offset:7168\n\t"
+        "ds_read_b128 %8, %16 offset:8192\n\t"
+        "ds_read_b128 %9, %16 offset:9216\n\t"
+        "ds_read_b128 %10, %16 offset:10240\n\t"
+        "ds_read_b128 %11, %16 offset:11264\n\t"
+        "ds_read_b128 %12, %16 offset:12288\n\t"
+        "ds_read_b128 %13, %16 offset:13312\n\t"
+        "ds_read_b128 %14, %16 offset:14336\n\t"
+        "ds_read_b128 %15, %16 offset:15360\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r.k[0][0]), "=&v"(r.k[0][1]), "=&v"(r.k[0][2]), "=&v"(r.k[0][3]), "=&v"(r.k[1][0]),
+          "=&v"(r.k[1][1]), "=&v"(r.k[1][2]), "=&v"(r.k[1][3]), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.v[2]),
+          "=&v"(r.v[3]), "=&v"(r.v[4]), "=&v"(r.v[5]), "=&v"(r.v[6]), "=&v"(r.v[7])
+        : "v"(addr)
+        : "memory");
+}
+
+// SLOTS: ring slots (SLOTS - 1 blocks ahead).  WPE: waves per SIMD the
+// register allocation leaves room for.  DIRECT: one split per unit, rows
+// finished in place.
+template <int SLOTS, bool NTL, int WPE, bool DIRECT>
+__global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
+    constexpr int kSlots = SLOTS, kAhead = SLOTS - 1;
+    __shared__ __attribute__((aligned(16))) char ring[kSlots][kSlotBytes];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane >> 4, c16 = lane & 15;
+    const uint32_t koff = 256u * c16 + 16u * j;
+    const uint32_t voff = 1024u * j + 16u * c16;
+    const int split = blockIdx.x, h = blockIdx.y;
+    const int bkv = blockIdx.z / a.row_groups, rg = blockIdx.z % a.row_groups;
+    const int rows_w = rg * kRowsPerGroup + 16 * w;   // this wavefront's first row
+
+    const int64_t n_eff = a.n_b ? min((int64_t)a.n_b[bkv], a.n) : a.n;
+    const int64_t head_off = (int64_t)bkv * a.kv_batch_stride + (int64_t)h * a.n * kD;
+    const uint16_t* kh = static_cast<const uint16_t*>(a.k) + head_off;
+    const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_off;
+    const int64_t t_begin = (int64_t)split * a.blocks_per_split * kBlock;
+    const int64_t t_end = min(n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
+    const int nblk = t_end > t_begin ? (int)((t_end - t_begin + kBlock - 1) / kBlock) : 0;
+
+    // Query fragments of this wavefront's 16 rows (row c16 of the tile).
+    WaveState<1> st;
+    {
+        const int r = rows_w + c16;
+        if (r < a.rows) {
+            const int b = a.shared ? r / a.G : bkv;
+            const int g = a.shared ? r % a.G : r;
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.G + g) * kD + 8 * j;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(ld16(qp + 32 * c));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) st.o[0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m[0] = kNoMax;
+        st.l[0] = 0.f;
+    }
+    wait_vm_all();   // only the ring's requests are outstanding from here on
+
+    const uint32_t lane_off = lds_addr(ring[0]) + 16 * lane;
+    if (nblk > 0) {
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) {
+            const int kk = min(k, nblk - 1);
+            request_block<NTL>(ring[k], kh, vh, t_begin + (int64_t)kBlock * kk, n_eff, k < nblk, w, koff, voff);
+        }
+        for (int k = 0; k < nblk; ++k) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_ring<kAhead>());   // this wavefront's pieces of block k
+            // Everyone's pieces of block k have landed, and every wavefront has read block k - 1.  A bare
+            // barrier: a fenced one would also wait for the blocks still in flight.
+            __builtin_amdgcn_s_barrier();
+            const int kn = k + kAhead;
+            request_block<NTL>(ring[kn % kSlots], kh, vh, t_begin + (int64_t)kBlock * min(kn, nblk - 1), n_eff,
+                               kn < nblk, w, koff, voff);
+            BlockRegs r;
+            read_block(r, lane_off + (k % kSlots) * kSlotBytes);
+            const int64_t t = t_begin + (int64_t)kBlock * k;
+            const int64_t left = n_eff - t;
+            compute_block<1>(st, r, (int)(left < kBlock ? left : kBlock), a.scale_log2, j, c16);
+        }
+    }
+    wait_vm_all();   // the empty requests past the end
+
+    // This wavefront's rows: m per row c16 (shared by the lane groups), l summed over them;
+    // o[nb][i] is row 4j + i, column 8*c16 + nb.
+    float l = st.l[0];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float m = st.m[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * j + i;
+        const int r = rows_w + rr;
+        const float M = __shfl(m, rr, 64);   // row rr's state lives in lane rr (j = 0)
+        const float L = __shfl(l, rr, 64);
+        if (r >= a.rows) continue;
+        const int b = a.shared ? r / a.G : bkv;
+        const int g = a.shared ? r % a.G : r;
+        const int64_t bhq = (int64_t)b * a.Hq + h * a.G + g;
+        if (DIRECT) {
+            const bool virt = a.alpha_in != nullptr && a.alpha_in[bhq] > -INFINITY;
+            const float al = virt ? a.alpha_in[bhq] : -INFINITY;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int c = 8 * c16 + nb;
+                finish_row(a, bhq, c, M, L, st.o[0][nb][i], virt, al, virt ? a.a_in[bhq * kD + c] : 0.f);
+            }
+        } else {
+            const int64_t slot = bhq * a.splits + split;
+            float* dst = a.acc + slot * kD + 8 * c16;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{st.o[0][0][i], st.o[0][1][i], st.o[0][2][i], st.o[0][3][i]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.o[0][4][i], st.o[0][5][i], st.o[0][6][i], st.o[0][7][i]};
+            if (c16 == 0) a.ml[slot] = make_float2(M, L);
+        }
+    }
+
+    // Several splits: the combine pass merges them (a unit here has 64 rows x
+    // splits partial states, too many for the one workgroup that would finish
+    // last to gather quickly).
+}
+
+}  // namespace
+
+int split_rows_per_group() { return kRowsPerGroup; }
+
+hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
+    dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
+    const int variant = (int)tuning().rows_variant;
+    if (a.direct) hipLaunchKernelGGL((k_split_rows<4, true, 1, true>), grid, block, 0, st, a);
+    else if (variant == 1) hipLaunchKernelGGL((k_split_rows<3, true, 3, false>), grid, block, 0, st, a);
+    else if (variant == 2) hipLaunchKernelGGL((k_split_rows<3, true, 2, false>), grid, block, 0, st, a);
+    else if (variant == 3) hipLaunchKernelGGL((k_split_rows<2, true, 3, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_split_rows<4, true, 2, false>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace lcda

@@ -54,6 +54,38 @@ def test_dense_shared_document(orc, B):
     _dense_case(B, 8, 2, 3000, torch.bfloat16, 500 + B, shared=True, orc=orc)
 
 
+@pytest.mark.parametrize("B,n", [(5, 100), (8, 300), (16, 33), (16, 3000), (20, 5003), (32, 2048)])
+def test_dense_shared_rows_kernel(orc, B, n):
+    """More than 16 rows per KV head (B*G rows on one shared document): 64-row workgroups that read each block
+    once into LDS; one split (rows finished in place, n <= 512) and several (in-kernel combine)."""
+    _dense_case(B, 8, 2, n, torch.bfloat16, 700 + B + n, shared=True, orc=orc)
+
+
+def test_dense_shared_rows_kernel_off(orc):
+    """The same shapes through one-wavefront-per-32/64-rows tiles (rows_kernel = 0)."""
+    old = ops.get_tuning("rows_kernel")
+    ops.set_tuning("rows_kernel", 0)
+    try:
+        for B in (8, 16):
+            _dense_case(B, 8, 2, 3000, torch.bfloat16, 760 + B, shared=True, orc=orc)
+    finally:
+        ops.set_tuning("rows_kernel", old)
+
+
+def test_config3_reduced(orc):
+    """Config 3 recipe (one shared document, 16 queries, 512 private local tokens each), one layer at
+    n = 7,680: the decode step (document pass + local merge) against the oracle, every row."""
+    cfg = synth.CONFIGS[3]
+    x = synth.make_inputs(cfg, n=7680)
+    print("case config 3 reduced", flush=True)
+    out, alpha = ops.dense_decode_step(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["k_loc"].to(DEV),
+                                       x["v_loc"].to(DEV), x["n_loc"].to(DEV))
+    torch.cuda.synchronize()
+    ro, ra = orc.dense_attn(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]))
+    mo, ma = orc.merge_local(to_np(x["q"]), ro, ra, to_np(x["k_loc"]), to_np(x["v_loc"]), to_np(x["n_loc"]))
+    assert_close(out, alpha, mo, ma, torch.bfloat16, "config 3 reduced step")
+
+
 def test_dense_fp32_shared_document(orc):
     _dense_case(3, 8, 2, 2000, torch.float32, 600, shared=True, orc=orc)
 
