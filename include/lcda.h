@@ -192,7 +192,9 @@ const char* lcda_version(void);
  *   "rows_kernel"    more than 16 rows per KV head: 1 = 64-row workgroups sharing
  *                    each block through LDS, 0 = one wavefront per 32 / 64 rows (1)
  *   "rows_variant"   64-row workgroups: 0 = 4-slot LDS ring, 2 workgroups per CU;
- *                    1 = 3 slots, 3 per CU; 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU (0)
+ *                    1 = 3 slots, 3 per CU; 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU;
+ *                    4-6 = every wavefront loads the block into registers (4: cached
+ *                    loads, 2 workgroups per CU; 5: nontemporal; 6: cached, 1 per CU) (0)
  *   "direct_blocks"  units with at most this many token blocks run as one split
  *                    that writes its rows directly, without a combine pass (16)
  *   "dense_variant"  MFMA split K/V pipeline (16-row tiles): 0 = nontemporal

@@ -50,6 +50,63 @@ constexpr int vmcnt_ring() {
     return 0x0F70 | (kPieces * (AHEAD - 1));
 }
 
+// Query fragments of a wavefront's 16 rows (row c16 of the tile) and a fresh state.
+__device__ __forceinline__ void load_rows_q(WaveState<1>& st, const SplitArgs& a, int rows_w, int bkv, int h, int j,
+                                            int c16) {
+    const int r = rows_w + c16;
+    if (r < a.rows) {
+        const int b = a.shared ? r / a.G : bkv;
+        const int g = a.shared ? r % a.G : r;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.G + g) * kD + 8 * j;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(ld16(qp + 32 * c));
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st.o[0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m[0] = kNoMax;
+    st.l[0] = 0.f;
+}
+
+// A wavefront's 16 rows out: m per row c16 (shared by the lane groups), l summed
+// over them; o[nb][i] is row 4j + i, column 8*c16 + nb.  Direct: finished rows
+// (with the optional virtual pair); else the (row, split) partial state.
+__device__ __forceinline__ void write_rows(const WaveState<1>& st, const SplitArgs& a, int rows_w, int bkv, int h,
+                                           int split, int j, int c16, int lane, bool direct) {
+    float l = st.l[0];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float m = st.m[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * j + i;
+        const int r = rows_w + rr;
+        const float M = __shfl(m, rr, 64);   // row rr's state lives in lane rr (j = 0)
+        const float L = __shfl(l, rr, 64);
+        if (r >= a.rows) continue;
+        const int b = a.shared ? r / a.G : bkv;
+        const int g = a.shared ? r % a.G : r;
+        const int64_t bhq = (int64_t)b * a.Hq + h * a.G + g;
+        if (direct) {
+            const bool virt = a.alpha_in != nullptr && a.alpha_in[bhq] > -INFINITY;
+            const float al = virt ? a.alpha_in[bhq] : -INFINITY;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int c = 8 * c16 + nb;
+                finish_row(a, bhq, c, M, L, st.o[0][nb][i], virt, al, virt ? a.a_in[bhq * kD + c] : 0.f);
+            }
+        } else {
+            const int64_t slot = bhq * a.splits + split;
+            float* dst = a.acc + slot * kD + 8 * c16;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{st.o[0][0][i], st.o[0][1][i], st.o[0][2][i], st.o[0][3][i]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.o[0][4][i], st.o[0][5][i], st.o[0][6][i], st.o[0][7][i]};
+            if (c16 == 0) a.ml[slot] = make_float2(M, L);
+        }
+    }
+}
+
 // This wavefront's pieces of block t (rows [t, t + 32) of the head) into `slot`.
 template <bool NTL>
 __device__ __forceinline__ void request_block(char* slot, const uint16_t* kh, const uint16_t* vh, int64_t t,
@@ -61,18 +118,13 @@ __device__ __forceinline__ void request_block(char* slot, const uint16_t* kh, co
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vh + t * kD), 0, nrec, kRsrcWord3);
     constexpr int aux = NTL ? 2 : 0;   // nontemporal
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-        const int i = kPieces * w + p;   // piece 0..7: K (half tb = i / 4, d chunk i % 4); 8..15: V row set e = i - 8
-        lds_ptr_t dst = (lds_ptr_t)(slot + 1024 * i);
-        if (i < 8) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, koff + 4096 * (i / 4) + 64 * (i % 4), 0, 0, aux);
-        } else {
-            const int e = i - 8;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, voff + (e < 4 ? 0 : 4096) + 256 * (e & 3), 0, 0,
-                                                     aux);
-        }
-    }
+    // Wavefront w requests pieces w + 4p: K (half p, d chunk w) for p = 0, 1 and
+    // V (row set e = w + 4(p - 2)) for p = 2, 3, the same code in every wavefront.
+    const uint32_t kw = koff + 64u * w, vw = voff + 256u * w;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(slot + 1024 * w), 16, kw, 0, 0, aux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(slot + 1024 * (w + 4)), 16, kw + 4096, 0, 0, aux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(slot + 1024 * (w + 8)), 16, vw, 0, 0, aux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(slot + 1024 * (w + 12)), 16, vw + 4096, 0, 0, aux);
 }
 
 // This lane's 16 pieces of a slot (addr = slot + 16*lane) into registers; the
@@ -129,25 +181,8 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
     const int64_t t_end = min(n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
     const int nblk = t_end > t_begin ? (int)((t_end - t_begin + kBlock - 1) / kBlock) : 0;
 
-    // Query fragments of this wavefront's 16 rows (row c16 of the tile).
     WaveState<1> st;
-    {
-        const int r = rows_w + c16;
-        if (r < a.rows) {
-            const int b = a.shared ? r / a.G : bkv;
-            const int g = a.shared ? r % a.G : r;
-            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.G + g) * kD + 8 * j;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(ld16(qp + 32 * c));
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-        }
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) st.o[0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.m[0] = kNoMax;
-        st.l[0] = 0.f;
-    }
+    load_rows_q(st, a, rows_w, bkv, h, j, c16);
     wait_vm_all();   // only the ring's requests are outstanding from here on
 
     const uint32_t lane_off = lds_addr(ring[0]) + 16 * lane;
@@ -174,42 +209,82 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
     }
     wait_vm_all();   // the empty requests past the end
 
-    // This wavefront's rows: m per row c16 (shared by the lane groups), l summed over them;
-    // o[nb][i] is row 4j + i, column 8*c16 + nb.
-    float l = st.l[0];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float m = st.m[0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * j + i;
-        const int r = rows_w + rr;
-        const float M = __shfl(m, rr, 64);   // row rr's state lives in lane rr (j = 0)
-        const float L = __shfl(l, rr, 64);
-        if (r >= a.rows) continue;
-        const int b = a.shared ? r / a.G : bkv;
-        const int g = a.shared ? r % a.G : r;
-        const int64_t bhq = (int64_t)b * a.Hq + h * a.G + g;
-        if (DIRECT) {
-            const bool virt = a.alpha_in != nullptr && a.alpha_in[bhq] > -INFINITY;
-            const float al = virt ? a.alpha_in[bhq] : -INFINITY;
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int c = 8 * c16 + nb;
-                finish_row(a, bhq, c, M, L, st.o[0][nb][i], virt, al, virt ? a.a_in[bhq * kD + c] : 0.f);
-            }
-        } else {
-            const int64_t slot = bhq * a.splits + split;
-            float* dst = a.acc + slot * kD + 8 * c16;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{st.o[0][0][i], st.o[0][1][i], st.o[0][2][i], st.o[0][3][i]};
-            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.o[0][4][i], st.o[0][5][i], st.o[0][6][i], st.o[0][7][i]};
-            if (c16 == 0) a.ml[slot] = make_float2(M, L);
-        }
-    }
+    write_rows(st, a, rows_w, bkv, h, split, j, c16, lane, DIRECT);
 
     // Several splits: the combine pass merges them (a unit here has 64 rows x
     // splits partial states, too many for the one workgroup that would finish
     // last to gather quickly).
+}
+
+// ---- register variant ---------------------------------------------------------
+// The same split of rows over wavefronts, without LDS: every wavefront requests
+// the whole block into its own registers (buffer loads, one block ahead); the
+// four requests of a block go to the same addresses at about the same time and
+// are served once from the caches (cached loads), so HBM still reads each
+// block once.
+template <bool NTL>
+__device__ __forceinline__ int load_rows_block(BlockRegs& r, const uint16_t* kh, const uint16_t* vh, int64_t t,
+                                               int64_t n_eff, bool live, uint32_t koff, uint32_t voff) {
+    const int64_t left = n_eff - t;
+    const int valid = (int)(left < kBlock ? left : kBlock);
+    const int nrec = live ? valid * kD * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh + t * kD), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vh + t * kD), 0, nrec, kRsrcWord3);
+    constexpr int aux = NTL ? 2 : 0;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            r.k[tb][c] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 4096 * tb + 64 * c, 0, aux);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        r.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + (e < 4 ? 0 : 4096) + 256 * (e & 3), 0, aux);
+    return valid;
+}
+
+template <bool NTL, int WPE, bool DIRECT>
+__global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows_regs(SplitArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane >> 4, c16 = lane & 15;
+    const uint32_t koff = 256u * c16 + 16u * j;
+    const uint32_t voff = 1024u * j + 16u * c16;
+    const int split = blockIdx.x, h = blockIdx.y;
+    const int bkv = blockIdx.z / a.row_groups, rg = blockIdx.z % a.row_groups;
+    const int rows_w = rg * kRowsPerGroup + 16 * w;
+
+    const int64_t n_eff = a.n_b ? min((int64_t)a.n_b[bkv], a.n) : a.n;
+    const int64_t head_off = (int64_t)bkv * a.kv_batch_stride + (int64_t)h * a.n * kD;
+    const uint16_t* kh = static_cast<const uint16_t*>(a.k) + head_off;
+    const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_off;
+    const int64_t t_begin = (int64_t)split * a.blocks_per_split * kBlock;
+    const int64_t t_end = min(n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
+    const int nblk = t_end > t_begin ? (int)((t_end - t_begin + kBlock - 1) / kBlock) : 0;
+
+    WaveState<1> st;
+    load_rows_q(st, a, rows_w, bkv, h, j, c16);
+    BlockRegs buf[2];
+    int valid[2] = {0, 0};
+    if (nblk > 0) valid[0] = load_rows_block<NTL>(buf[0], kh, vh, t_begin, n_eff, true, koff, voff);
+    wait_vm_all();   // the query fragments and the first block
+
+    for (int k = 0; k < nblk;) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (k < nblk) {
+                const int kn = k + 1;
+                valid[u ^ 1] = load_rows_block<NTL>(buf[u ^ 1], kh, vh, t_begin + (int64_t)kBlock * min(kn, nblk - 1),
+                                                    n_eff, kn < nblk, koff, voff);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_block<1>(st, buf[u], valid[u], a.scale_log2, j, c16);
+                ++k;
+            }
+        }
+    }
+    wait_vm_all();
+    write_rows(st, a, rows_w, bkv, h, split, j, c16, lane, DIRECT);
 }
 
 }  // namespace
@@ -223,6 +298,9 @@ hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t
     else if (variant == 1) hipLaunchKernelGGL((k_split_rows<3, true, 3, false>), grid, block, 0, st, a);
     else if (variant == 2) hipLaunchKernelGGL((k_split_rows<3, true, 2, false>), grid, block, 0, st, a);
     else if (variant == 3) hipLaunchKernelGGL((k_split_rows<2, true, 3, false>), grid, block, 0, st, a);
+    else if (variant == 4) hipLaunchKernelGGL((k_split_rows_regs<false, 2, false>), grid, block, 0, st, a);
+    else if (variant == 5) hipLaunchKernelGGL((k_split_rows_regs<true, 2, false>), grid, block, 0, st, a);
+    else if (variant == 6) hipLaunchKernelGGL((k_split_rows_regs<false, 1, false>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_split_rows<4, true, 2, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }

@@ -61,6 +61,19 @@ def test_dense_shared_rows_kernel(orc, B, n):
     _dense_case(B, 8, 2, n, torch.bfloat16, 700 + B + n, shared=True, orc=orc)
 
 
+@pytest.mark.parametrize("variant", list(range(7)))
+def test_dense_shared_rows_variants(orc, variant):
+    """Every 64-row workgroup variant (LDS ring depths and occupancies, blocks in registers) gives the
+    oracle's result, several blocks per workgroup and a ragged tail."""
+    old = ops.get_tuning("rows_variant")
+    ops.set_tuning("rows_variant", variant)
+    try:
+        _dense_case(16, 8, 2, 7680 + 5, torch.bfloat16, 780 + variant, shared=True, orc=orc)
+        _dense_case(20, 8, 2, 3001, torch.bfloat16, 790 + variant, shared=True, orc=orc)
+    finally:
+        ops.set_tuning("rows_variant", old)
+
+
 def test_dense_shared_rows_kernel_off(orc):
     """The same shapes through one-wavefront-per-32/64-rows tiles (rows_kernel = 0)."""
     old = ops.get_tuning("rows_kernel")
