@@ -196,12 +196,16 @@ const char* lcda_version(void);
  *                    4-6 = every wavefront loads the block into registers (4: cached
  *                    loads, 2 workgroups per CU; 5: nontemporal; 6: cached, 1 per CU) (0)
  *   "direct_blocks"  units with at most this many token blocks run as one split
- *                    that writes its rows directly, without a combine pass (16)
+ *                    that writes its rows directly, without a combine pass, when
+ *                    the units alone reach the workgroup target (16)
  *   "dense_variant"  MFMA split K/V pipeline (16-row tiles): 0 = nontemporal
  *                    loads one block ahead, 1 = cached loads one block ahead,
  *                    2 = nontemporal two blocks ahead, 3 = as 0 with registers
  *                    capped so two workgroups share a CU (0)
  *   "gather_variant" GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads (0)
+ *   "topk_subs"      TOPK scans: at least this many 4096-position sub-chunks per
+ *                    workgroup (1..64; more where a head would otherwise exceed 64
+ *                    chunks) (4)
  * Returns LCDA_EINVAL for an unknown key or a negative (or, except
  * direct_blocks, zero) value.  lcda_get_tuning returns -1 for an unknown key. */
 int lcda_set_tuning(const char* key, int64_t value);

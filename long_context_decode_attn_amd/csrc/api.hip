@@ -99,8 +99,9 @@ int hip_status(const char* fn, hipError_t e) {
 // Launch the split pass, then the combine pass unless the plan has a single
 // split (the split kernel then writes the final rows itself) or the split
 // kernel combines each unit itself (kMfma16: the last workgroup of a unit to
-// finish merges its rows; kRows units are too large for that and use the
-// combine pass).
+// finish merges its rows).  kRows units are too large for that, and for the
+// short gather units of kValu the arrival at the end of every workgroup costs
+// more than the separate pass.
 int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows, float* out, float* alpha,
            const float* a_in, const float* alpha_in, hipStream_t st) {
     a.direct = p.splits == 1 ? 1 : 0;
@@ -204,7 +205,9 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
     const int64_t nblocks = n_tokens > 0 ? ceil_div(n_tokens, p.block) : 0;
     const int64_t max_splits = nblocks > 0 ? ceil_div(nblocks, p.waves) : 1;
     int64_t splits = ceil_div(target, units > 0 ? units : 1);
-    if (nblocks <= tuning().direct_blocks) splits = 1;   // short: one split, finished in place
+    // Short ranges run as one split finished in place, unless there are too few
+    // units to fill the chip that way.
+    if (nblocks <= tuning().direct_blocks && units >= target) splits = 1;
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
     const int64_t bps = nblocks > 0 ? ceil_div(nblocks, splits) : 1;
     splits = nblocks > 0 ? ceil_div(nblocks, bps) : 1;
@@ -245,6 +248,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
     else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
+    else if (!strcmp(key, "topk_subs") && value <= 64) t.topk_subs = value;
     else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
     return LCDA_OK;
 }
@@ -262,6 +266,7 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "direct_blocks")) return t.direct_blocks;
     if (!strcmp(key, "dense_variant")) return t.dense_variant;
     if (!strcmp(key, "gather_variant")) return t.gather_variant;
+    if (!strcmp(key, "topk_subs")) return t.topk_subs;
     return -1;
 }
 

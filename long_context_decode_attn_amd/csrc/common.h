@@ -32,12 +32,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-lane butterfly sum (lanes l, l^1, l^2, l^4, l^8 of one row of 16).
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), returned in all
+// of them: swaps of neighbours and of pairs inside each group of four
+// (quad_perm [1,0,3,2] and [2,3,0,1]), then rotations of the row by 4 and by 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x124>(x);   // row_ror:4
+    x += dpp_mov<0x128>(x);   // row_ror:8
     return x;
 }
 

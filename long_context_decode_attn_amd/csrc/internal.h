@@ -68,6 +68,7 @@ struct Tuning {
     int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads,
                                    // 2 = two blocks ahead, 3 = nontemporal with two waves per SIMD
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads
+    int64_t topk_subs = 4;         // TOPK: at least this many 4096-position sub-chunks per chunk
 };
 Tuning& tuning();
 

@@ -17,8 +17,8 @@
 // (one xor + popcount per position and query head, plus bookkeeping), so the
 // per-position work is kept to a few vector instructions.
 //   1. k_topk_hist    - per chunk: the 33-bin distance histogram of each query
-//                       head, in 64 lane-private LDS copies (the increments of
-//                       one instruction never collide).
+//                       head, in 64 per-lane LDS copies laid out so that the
+//                       increments of one instruction hit distinct banks.
 //   2. k_topk_select  - per query head (one wavefront, lane = chunk): t and the
 //                       quota from the summed histograms, each chunk's ties
 //                       taken, the window positions outside the top m in the
@@ -223,10 +223,12 @@ __device__ void select_head(const TopkArgs& a, int b, int h, int g, int lane, ui
     const int off = wave_excl_scan_i(cnt, lane);
     const int total = wave_sum_i(cnt);
     if (lane < C) {
-        int32_t* ci = a.chunk_info + (row * C + lane) * 4;
+        // Records of one chunk for all G heads of the group sit together.
+        int32_t* ci = a.chunk_info + ((((int64_t)b * a.Hkv + h) * C + lane) * a.G + g) * 4;
         ci[0] = off;
         ci[1] = taken;
         ci[2] = ties;
+        ci[3] = t;
     }
     if (lane == 0) {
         a.count[row] = total;
@@ -237,63 +239,104 @@ __device__ void select_head(const TopkArgs& a, int b, int h, int g, int lane, ui
 }
 
 // ---- 1. histogram ------------------------------------------------------------------
-// LDS cnt[lane][g][bin], with a spare bin 33 for positions past the end and an
-// odd row stride: the 64 lanes of one increment hit 64 different words spread
-// over the banks.
+// LDS cnt[g][bin][lane]: one copy per lane of the wavefront (the four
+// wavefronts share them through atomic adds), with a spare bin 33 for
+// positions past the end.  An increment's address is bin * 64 + lane, so the
+// 64 lanes of one instruction fall into distinct banks whatever their bins.
 template <int MAXG>
 struct HistSmem {
-    static constexpr int kStride = MAXG * (kBins + 1) + 1;
-    uint32_t cnt[64 * kStride];
+    static constexpr int kWords = MAXG * (kBins + 1) * 64;
+    uint32_t cnt[kWords];
 };
+
+// The increments of one chunk.  All MAXG heads are counted; heads at or past
+// G count the codes of head G - 1 into rows that are never read, so the loop
+// has no per-head branches.  FULL: the chunk is whole (every position is
+// below end); otherwise positions at or past end go to the spare bin.
+// The codes of kGrp sub-chunks are requested together: the ring xr holds
+// them, and each slot is refilled with the sub-chunk kGrp ahead as soon as it
+// has been counted, so that a group's loads are in flight at once.
+constexpr int kGrp = 4;
+
+template <bool VEC>
+__device__ __forceinline__ void load_group(uint32_t (&xr)[kGrp][16], const uint32_t* ks, int64_t gb, int64_t end,
+                                           int tid) {
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u)
+        if (gb + (int64_t)u * kSub < end) load_sub<VEC>(xr[u], ks, gb + (int64_t)u * kSub, end, tid);
+}
+
+template <int MAXG, bool VEC, bool FULL, bool SCORES>
+__device__ __forceinline__ void hist_chunk(const TopkArgs& a, uint32_t* my, const uint32_t* ks,
+                                           const uint32_t (&qs)[MAXG], uint32_t (&xr)[kGrp][16], int64_t beg,
+                                           int64_t end, int tid, int64_t row0) {
+    for (int64_t gb = beg; gb < end; gb += (int64_t)kGrp * kSub) {
+#pragma unroll
+        for (int u = 0; u < kGrp; ++u) {
+            const int64_t sb = gb + (int64_t)u * kSub;
+            if (sb < end) {   // uniform
+                uint32_t x[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) x[k] = xr[u][k];
+                const int64_t nb = sb + (int64_t)kGrp * kSub;
+                if (nb < end) load_sub<VEC>(xr[u], ks, nb, end, tid);
+                const int rem = FULL ? kSub : (int)min(end - sb, (int64_t)kSub);
+#pragma unroll
+                for (int uu = 0; uu < 4; ++uu) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = 4 * (tid + 256 * uu) + e;
+                        const bool ok = FULL || k < rem;
+#pragma unroll
+                        for (int g = 0; g < MAXG; ++g) {
+                            const uint32_t d = __builtin_popcount(x[4 * uu + e] ^ qs[g]);
+                            const uint32_t bin = ok ? d : (uint32_t)kBins;
+                            uint32_t* p = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(my) + (bin << 8)) +
+                                          g * (kBins + 1) * 64;
+                            __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                            if (SCORES && ok && g < a.G)
+                                a.scores[(row0 + g) * a.n + sb + k] = (int8_t)(-(int)d);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
 
 template <int MAXG, bool VEC, bool SCORES>
 __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
     __shared__ HistSmem<MAXG> sm;
-    constexpr int S = HistSmem<MAXG>::kStride;
     const int tid = threadIdx.x, lane = tid & 63;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int G = a.G;
     const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * a.n;
     const int64_t beg = (int64_t)c * a.chunk_len;
     const int64_t end = min(a.n, beg + a.chunk_len);
+    const int64_t row0 = (int64_t)b * a.Hq + h * G;
 
-    uint32_t x[16];
-    load_sub<VEC>(x, ks, beg, end, tid);
-    for (int k = tid; k < 64 * S; k += 256) sm.cnt[k] = 0;
+    uint32_t xr[kGrp][16];
+    load_group<VEC>(xr, ks, beg, end, tid);
+    static_assert(HistSmem<MAXG>::kWords % 4 == 0, "zeroed in 16-byte stores");
+    for (int k = 4 * tid; k < HistSmem<MAXG>::kWords; k += 4 * 256)
+        *reinterpret_cast<u32x4*>(sm.cnt + k) = u32x4{0u, 0u, 0u, 0u};
     uint32_t qs[MAXG];
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) qs[g] = g < G ? a.q_sigs[(int64_t)b * a.Hq + h * G + g] : 0u;
+    for (int g = 0; g < MAXG; ++g) qs[g] = a.q_sigs[row0 + min(g, G - 1)];
     __syncthreads();
 
-    uint32_t* my = sm.cnt + lane * S;
-    for (int64_t sb = beg; sb < end; sb += kSub) {
-        if (sb != beg) load_sub<VEC>(x, ks, sb, end, tid);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t i = sb + 4 * (tid + 256 * u) + e;
-                const bool ok = i < end;
-#pragma unroll
-                for (int g = 0; g < MAXG; ++g) {
-                    if (g < G) {
-                        const uint32_t d = __builtin_popcount(x[4 * u + e] ^ qs[g]);
-                        __hip_atomic_fetch_add(my + g * (kBins + 1) + (ok ? d : (uint32_t)kBins), 1u,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                        if (SCORES && ok)
-                            a.scores[((int64_t)b * a.Hq + h * G + g) * a.n + i] = (int8_t)(-(int)d);
-                    }
-                }
-            }
-        }
-    }
+    uint32_t* my = sm.cnt + lane;
+    if (end - beg == a.chunk_len) hist_chunk<MAXG, VEC, true, SCORES>(a, my, ks, qs, xr, beg, end, tid, row0);
+    else hist_chunk<MAXG, VEC, false, SCORES>(a, my, ks, qs, xr, beg, end, tid, row0);
     __syncthreads();
-    // Sum the 64 copies.
+    // Sum the 64 copies of each (head, bin); each thread starts at its own
+    // lane copy so that the reads of one instruction fall into distinct banks.
     for (int k = tid; k < G * kBins; k += 256) {
         const int g = k / kBins, bin = k % kBins;
+        const uint32_t* row = sm.cnt + (g * (kBins + 1) + bin) * 64;
         uint32_t sum = 0;
 #pragma unroll 8
-        for (int l = 0; l < 64; ++l) sum += sm.cnt[l * S + g * (kBins + 1) + bin];
+        for (int l = 0; l < 64; ++l) sum += row[(l + tid) & 63];
         a.hist[(((int64_t)b * a.Hq + h * G + g) * a.chunks + c) * kRow + bin] = sum;
     }
 }
@@ -314,12 +357,13 @@ __global__ __launch_bounds__(64) void k_topk_empty(TopkArgs a) {
 
 // ---- 3. ordered compaction -------------------------------------------------------
 // Thread tid owns the 16 consecutive positions sb + 16*tid + j of a sub-chunk.
-// Per query head it forms 16-bit masks (below t, ties, and, for a chunk a
-// window meets, window positions), the selection mask, and its popcount; one
-// block-wide exclusive scan of the counts (four heads packed in 16-bit fields of
-// a 64-bit word) places every thread's positions, which it then stores in order.
-// A head that takes only some of the chunk's ties first needs the ties before
-// each thread: a second packed scan, run only when some head does.
+// Per query head it forms a 16-bit selection mask; the exclusive prefix of the
+// masks' popcounts over the threads (two heads packed in the 16-bit fields of
+// a word) places every thread's positions, which it then stores in order.
+// The prefix is a DPP scan inside each wavefront plus the wavefront totals
+// exchanged through LDS.  A head that takes only some of the chunk's ties
+// first needs the ties before each thread: the same scan over the tie counts,
+// run only when some head does.
 template <bool VEC>
 __device__ __forceinline__ void load_run(uint32_t (&x)[16], const uint32_t* ks, int64_t sb, int64_t end, int tid) {
 #pragma unroll
@@ -336,31 +380,21 @@ __device__ __forceinline__ void load_run(uint32_t (&x)[16], const uint32_t* ks, 
     }
 }
 
-// Block-wide (256 threads) exclusive scan of a 64-bit word of four 16-bit
-// counts; total gets the block sums.  sh: 4 words of LDS.
-__device__ __forceinline__ uint64_t block_scan_packed(uint64_t v, uint64_t* total, uint64_t* sh) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint64_t inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += y;
-    }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    uint64_t base = 0, all = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint64_t t = sh[k];
-        base += k < w ? t : 0;
-        all += t;
-    }
-    __syncthreads();   // sh is reused by the next scan
-    *total = all;
-    return base + inc - v;
+// Inclusive scan over the 64 lanes of a wavefront: sums within rows of 16 by
+// shifts of 1, 2, 4 and 8 lanes (zero filled at the row start), then the last
+// lane of row 0 (of row 2) is added to row 1 (row 3), and the last lane of
+// row 1 to rows 2 and 3.  Words hold two 16-bit counts that never carry.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+    return x;
 }
 
-__device__ __forceinline__ uint32_t field16(uint64_t v, int k) { return (uint32_t)(v >> (16 * k)) & 0xFFFFu; }
+__device__ __forceinline__ int field16(uint32_t v, int k) { return (int)((v >> (16 * k)) & 0xFFFFu); }
 
 // The lowest `take` set bits of m.
 __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, int take) {
@@ -373,11 +407,46 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, int take) {
     return r;
 }
 
+// Bit j of the result: position j of the thread's 16 has popcount(code ^ q) <
+// thr.  The bits are shifted in from the top position down, each as the sign
+// of popcount + nthr (nthr = -thr, kept opaque so that the add folds into the
+// popcount), funnelled in by one alignbit.
+__device__ __forceinline__ uint32_t below_mask(const uint32_t (&x)[16], uint32_t q, uint32_t nthr) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 15; j >= 0; --j)
+        m = __builtin_amdgcn_alignbit(m, (uint32_t)__builtin_popcount(x[j] ^ q) + nthr, 31);
+    return m;
+}
+
+// Window positions among the thread's 16 positions i0 .. i0 + 15: below s_end
+// or at / past r_beg.
+__device__ __forceinline__ uint32_t window_mask(int64_t i0, int64_t s_end, int64_t r_beg) {
+    const int lo = (int)min(max(s_end - i0, (int64_t)0), (int64_t)16);   // positions below s_end
+    const int hi = (int)min(max(r_beg - i0, (int64_t)0), (int64_t)16);   // positions below r_beg
+    const uint32_t below_s = lo >= 16 ? 0xFFFFu : ((1u << lo) - 1u);
+    const uint32_t from_r = hi >= 16 ? 0u : (0xFFFFu & ~((1u << hi) - 1u));
+    return below_s | from_r;
+}
+
+// Sub-chunks are handled in groups of kGrp: the masks and in-wavefront scans
+// of the whole group first, then one exchange of the wavefront totals (one
+// barrier; a second one for the tie ranks of a head taking only some of the
+// chunk's ties), then the stores.  The codes come through a ring of kGrp
+// sub-chunks, as in the histogram.
+template <bool VEC>
+__device__ __forceinline__ void load_run_group(uint32_t (&xr)[kGrp][16], const uint32_t* ks, int64_t gb, int64_t end,
+                                               int tid) {
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u)
+        if (gb + (int64_t)u * kSub < end) load_run<VEC>(xr[u], ks, gb + (int64_t)u * kSub, end, tid);
+}
+
 template <int MAXG, bool VEC>
 __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
-    constexpr int kPacks = (MAXG + 3) / 4;
-    __shared__ uint64_t scan_sh[4];
-    const int tid = threadIdx.x;
+    constexpr int kW = MAXG / 2;                 // words of packed 16-bit counts
+    __shared__ uint32_t sh[2][2][kGrp][4][kW];   // [parity][selection, ties][sub][wavefront][word]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int G = a.G;
     const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * a.n;
@@ -388,107 +457,144 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
     const bool meets_win = beg < s_end || end > r_beg;   // uniform
     const int64_t row0 = (int64_t)b * a.Hq + h * G;
 
-    uint32_t x[16];
-    load_run<VEC>(x, ks, beg, end, tid);
-    uint32_t q[MAXG];
-    int t[MAXG], off[MAXG], taken[MAXG], mode[MAXG];   // mode: 0 no ties, 1 all ties, 2 some ties
-    int tie_carry[MAXG];
+    uint32_t xr[kGrp][16];
+    load_run_group<VEC>(xr, ks, beg, end, tid);
+    // The chunk's records of all heads, {off, taken, ties, t} each, in one block.
+    // Per head: the selection below threshold thr (t, or t + 1 for a chunk that
+    // takes all its ties); a chunk that takes only some of its ties (mode 2)
+    // also forms the tie mask.  Heads at or past G select nothing.
+    const int32_t* rec = a.chunk_info + (((int64_t)b * a.Hkv + h) * a.chunks + c) * G * 4;
+    uint32_t q[MAXG], nthr[MAXG], nt1[MAXG];
+    int off[MAXG], taken[MAXG], mode[MAXG], tie_carry[MAXG];   // mode: 0 no ties, 1 all ties, 2 some ties
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
         const int gg = min(g, G - 1);
-        const int32_t* ci = a.chunk_info + ((row0 + gg) * a.chunks + c) * 4;
+        const int32_t* ci = rec + 4 * gg;
         q[g] = a.q_sigs[row0 + gg];
-        t[g] = a.head_info[2 * (row0 + gg)];
+        const int t = g < G ? ci[3] : -1;
         off[g] = ci[0];
         taken[g] = ci[1];
         const int ties = ci[2];
-        mode[g] = (t[g] < 0 || taken[g] == 0) ? 0 : (taken[g] == ties ? 1 : 2);
+        mode[g] = (t < 0 || taken[g] == 0) ? 0 : (taken[g] == ties ? 1 : 2);
+        nthr[g] = (uint32_t)__builtin_amdgcn_readfirstlane(-(t + (mode[g] == 1 ? 1 : 0)));
+        nt1[g] = (uint32_t)__builtin_amdgcn_readfirstlane(-(t + 1));
         tie_carry[g] = 0;
     }
     bool partial = false;   // uniform: every thread read the same chunk records
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) partial |= g < G && mode[g] == 2;
-    for (int64_t sb = beg; sb < end; sb += kSub) {
-        if (sb != beg) load_run<VEC>(x, ks, sb, end, tid);
-        const int64_t i0 = sb + 16 * tid;
-        const int nv = (int)max((int64_t)0, min((int64_t)16, end - i0));   // valid positions of this thread
-        const uint32_t valid = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
-        uint32_t win = 0;
-        if (meets_win) {
+    for (int g = 0; g < MAXG; ++g) partial |= mode[g] == 2;
+
+    int par = 0;
+    for (int64_t gb = beg; gb < end; gb += (int64_t)kGrp * kSub, par ^= 1) {
+        // Selection masks (two heads per word, 16 bits each) and their counts.
+        uint32_t sel[kGrp][kW], cnt[kGrp][kW], inc[kGrp][kW];
+        uint32_t tie[kGrp][kW], tcnt[kGrp][kW], tinc[kGrp][kW];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) win |= (uint32_t)(i0 + j < s_end || i0 + j >= r_beg) << j;
-            win &= valid;
-        }
-        uint32_t lt[MAXG], tie[MAXG];
+        for (int u = 0; u < kGrp; ++u) {
+            const int64_t sb = gb + (int64_t)u * kSub;
+            uint32_t x[16];
 #pragma unroll
-        for (int g = 0; g < MAXG; ++g) {
-            lt[g] = 0;
-            tie[g] = 0;
-            if (g < G) {
+            for (int k = 0; k < 16; ++k) x[k] = xr[u][k];
+            if (sb + (int64_t)kGrp * kSub < end) load_run<VEC>(xr[u], ks, sb + (int64_t)kGrp * kSub, end, tid);
+            const int64_t i0 = sb + 16 * tid;
+            const int nv = (int)max((int64_t)0, min((int64_t)16, end - i0));   // valid positions of this thread
+            const uint32_t valid = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
+            const uint32_t win = meets_win ? window_mask(i0, s_end, r_beg) & valid : 0u;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int d = (int)__builtin_popcount(x[j] ^ q[g]);
-                    lt[g] |= (uint32_t)(d < t[g]) << j;
-                    tie[g] |= (uint32_t)(d == t[g]) << j;
+            for (int k = 0; k < kW; ++k) {
+                uint32_t m2[2], t2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int g = 2 * k + e;
+                    const uint32_t sm = below_mask(x, q[g], nthr[g]) & valid;
+                    m2[e] = g < G ? (sm | win) : 0u;
+                    // Ties rank over every position of the chunk, window positions included.
+                    t2[e] = (partial && mode[g] == 2) ? below_mask(x, q[g], nt1[g]) & ~sm & valid : 0u;
                 }
-                lt[g] &= valid;
-                tie[g] &= valid;
+                sel[u][k] = m2[0] | (m2[1] << 16);
+                tie[u][k] = t2[0] | (t2[1] << 16);
+                tcnt[u][k] = (uint32_t)__builtin_popcount(t2[0]) | ((uint32_t)__builtin_popcount(t2[1]) << 16);
+                tinc[u][k] = partial ? wave_incl_scan(tcnt[u][k]) : 0u;
+                if (partial && lane == 63) sh[par][1][u][w][k] = tinc[u][k];
             }
         }
-        // Ties before this thread in the chunk, for heads taking only some of them.
-        int tie_before[MAXG];
-#pragma unroll
-        for (int g = 0; g < MAXG; ++g) tie_before[g] = tie_carry[g];
         if (partial) {
+            // Tie ranks: a head taking only some of the chunk's ties takes the
+            // lowest `taken - ties before` ties of each thread.
+            __syncthreads();
 #pragma unroll
-            for (int p = 0; p < kPacks; ++p) {
-                uint64_t v = 0;
+            for (int k = 0; k < kW; ++k) {
+                uint32_t run = 0;   // ties of the sub-chunks before, in this group
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (4 * p + k < MAXG) v |= (uint64_t)__builtin_popcount(tie[4 * p + k]) << (16 * k);
-                uint64_t tot;
-                const uint64_t ex = block_scan_packed(v, &tot, scan_sh);
+                for (int u = 0; u < kGrp; ++u) {
+                    uint32_t base = 0, all = 0;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if (4 * p + k < MAXG) {
-                        tie_before[4 * p + k] += (int)field16(ex, k);
-                        tie_carry[4 * p + k] += (int)field16(tot, k);
+                    for (int ww = 0; ww < 4; ++ww) {
+                        const uint32_t tw = sh[par][1][u][ww][k];
+                        base += ww < w ? tw : 0u;
+                        all += tw;
+                    }
+                    const uint32_t before2 = run + base + tinc[u][k] - tcnt[u][k];
+                    run += all;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int g = 2 * k + e;
+                        if (mode[g] == 2) {
+                            const int before = tie_carry[g] + field16(before2, e);
+                            const uint32_t tk =
+                                lowest_bits((tie[u][k] >> (16 * e)) & 0xFFFFu, min(max(taken[g] - before, 0), 16));
+                            sel[u][k] |= tk << (16 * e);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) tie_carry[2 * k + e] += field16(run, e);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGrp; ++u) {
+#pragma unroll
+            for (int k = 0; k < kW; ++k) {
+                cnt[u][k] = (uint32_t)__builtin_popcount(sel[u][k] & 0xFFFFu) |
+                            ((uint32_t)__builtin_popcount(sel[u][k] >> 16) << 16);
+                inc[u][k] = wave_incl_scan(cnt[u][k]);
+                if (lane == 63) sh[par][0][u][w][k] = inc[u][k];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kW; ++k) {
+            uint32_t run = 0;   // selected positions of the sub-chunks before, in this group
+#pragma unroll
+            for (int u = 0; u < kGrp; ++u) {
+                uint32_t base = 0, all = 0;
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) {
+                    const uint32_t sw = sh[par][0][u][ww][k];
+                    base += ww < w ? sw : 0u;
+                    all += sw;
+                }
+                const uint32_t ex2 = run + base + inc[u][k] - cnt[u][k];
+                run += all;
+                const int64_t i0 = gb + (int64_t)u * kSub + 16 * tid;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int g = 2 * k + e;
+                    if (g < G) {
+                        int32_t* out = a.idx + (row0 + g) * a.cap;
+                        int pos = off[g] + field16(ex2, e);
+                        uint32_t m = (sel[u][k] >> (16 * e)) & 0xFFFFu;
+                        while (m) {
+                            const int j = __builtin_ctz(m);
+                            if (pos < a.cap) out[pos] = (int32_t)(i0 + j);
+                            ++pos;
+                            m &= m - 1u;
+                        }
                     }
                 }
             }
-        }
-        uint32_t sel[MAXG];
 #pragma unroll
-        for (int g = 0; g < MAXG; ++g) {
-            uint32_t tk = 0;
-            if (mode[g] == 1) tk = tie[g];
-            else if (mode[g] == 2) tk = lowest_bits(tie[g], min(max(taken[g] - tie_before[g], 0), 16));
-            sel[g] = g < G ? (win | lt[g] | tk) : 0u;
-        }
-#pragma unroll
-        for (int p = 0; p < kPacks; ++p) {
-            uint64_t v = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (4 * p + k < MAXG) v |= (uint64_t)__builtin_popcount(sel[4 * p + k]) << (16 * k);
-            uint64_t tot;
-            const uint64_t ex = block_scan_packed(v, &tot, scan_sh);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int g = 4 * p + k;
-                if (g < G) {
-                    int32_t* out = a.idx + (row0 + g) * a.cap;
-                    int pos = off[g] + (int)field16(ex, k);
-                    uint32_t m = sel[g];
-                    while (m) {
-                        const int j = __builtin_ctz(m);
-                        if (pos < a.cap) out[pos] = (int32_t)(i0 + j);
-                        ++pos;
-                        m &= m - 1u;
-                    }
-                    off[g] += (int)field16(tot, k);
-                }
-            }
+            for (int e = 0; e < 2; ++e) off[2 * k + e] += field16(run, e);
         }
     }
 }
@@ -498,7 +604,7 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
 int topk_chunk_len(int64_t n) {
     const int64_t per = (int64_t)kSub * kMaxChunks;
     const int64_t subs = n > 0 ? (n + per - 1) / per : 1;
-    return (int)(subs * kSub);
+    return (int)(max(subs, tuning().topk_subs) * kSub);
 }
 
 int topk_hist_row() { return kRow; }

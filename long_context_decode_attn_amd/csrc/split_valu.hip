@@ -5,7 +5,8 @@
 // softmax renormalised over the selected set, rows read straight from the
 // cache by position, page size 1, no gathered copy).
 //
-// Partial state per row and slot as in split_mfma.hip (base-2 units).
+// Partial state per row and slot as in split_mfma.hip (base-2 units), merged
+// by the combine pass.
 //
 // Mapping: 16 lanes share one K/V row, each lane holding 8 consecutive d
 // values (16 B for bf16, 32 B for fp32), so one load instruction reads 4 whole
@@ -160,9 +161,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
     const int64_t stride = (int64_t)kWaves * kStep;
 
     // Software pipeline over steps of kStep tokens: the positions (gather mode:
-    // entries of the index list) are requested two steps ahead and the K/V rows
-    // one step ahead of the step being computed.  Requests past the end of the
-    // range are clamped to its last entry (cache-resident) and ignored.
+    // entries of the index list) are requested three steps ahead and the K/V
+    // rows two steps ahead of the step being computed.  Requests past the end
+    // of the range are clamped to its last entry (cache-resident) and ignored.
     struct Step {
         Row8<T> k[U], v[U];
     };
@@ -224,20 +225,27 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 
     int64_t t0 = t_begin + (int64_t)w * kStep;
     if (t0 < t_end) {
-        int32_t pa[U], pb[U];
-        Step sa, sb;
-        positions(t0, pa);
-        positions(t0 + stride, pb);
-        fetch(sa, pa);
+        int32_t p0[U], p1[U], p2[U];
+        Step s0, s1, s2;
+        positions(t0, p0);
+        positions(t0 + stride, p1);
+        positions(t0 + 2 * stride, p2);
+        fetch(s0, p0);
+        fetch(s1, p1);
         while (true) {
-            positions(t0 + 2 * stride, pa);
-            fetch(sb, pb);
-            compute(sa, t0);
+            positions(t0 + 3 * stride, p0);
+            fetch(s2, p2);
+            compute(s0, t0);
             t0 += stride;
             if (t0 >= t_end) break;
-            positions(t0 + 2 * stride, pb);
-            fetch(sa, pa);
-            compute(sb, t0);
+            positions(t0 + 3 * stride, p1);
+            fetch(s0, p0);
+            compute(s1, t0);
+            t0 += stride;
+            if (t0 >= t_end) break;
+            positions(t0 + 3 * stride, p2);
+            fetch(s1, p1);
+            compute(s2, t0);
             t0 += stride;
             if (t0 >= t_end) break;
         }

@@ -48,6 +48,39 @@ def test_garbage_workspace(orc, fill):
     assert_close(out, alpha, mo, ma, torch.bfloat16, "fused step, %s workspace" % fill)
 
 
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_garbage_workspace_gather_and_fp32(orc, fill):
+    """The vector-ALU split (GATHER-ATT, and the fp32 dense path) with its combine pass on a workspace of
+    garbage; each call runs twice on one workspace."""
+    B, Hq, Hkv, n, cap = 2, 16, 4, 6000, 1500
+    q, k, v, _, _ = _kv(B, Hq, Hkv, n, 73)
+    g = np.random.default_rng(74)
+    idx = np.full((B, Hq, cap), -1, np.int32)
+    cnt = g.integers(0, cap + 1, (B, Hq)).astype(np.int32)
+    cnt[0, 0] = 0
+    for b in range(B):
+        for h in range(Hq):
+            idx[b, h, :cnt[b, h]] = np.sort(g.choice(n, cnt[b, h], replace=False))
+    nb = max(ops.ws_bytes_gather_attn(B, Hq, Hkv, 128, cap), ops.ws_bytes_cached_attn_lse(B, Hq, Hkv, 128, n, Hkv * n * 128))
+    if fill == "ones":
+        ws = torch.full((nb,), 255, dtype=torch.uint8, device=DEV)
+    else:
+        ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, generator=torch.Generator().manual_seed(75)).to(DEV)
+    print("case garbage workspace (gather, fp32) fill=%s" % fill, flush=True)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    it, ct = torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+    res = [ops.gather_attn(qd, kd, vd, it, ct, ws=ws) for _ in range(2)]
+    q32, k32, v32 = q.float(), k.float(), v.float()
+    res32 = [ops.cached_attn_lse(q32.to(DEV), k32.to(DEV), v32.to(DEV), ws=ws) for _ in range(2)]
+    torch.cuda.synchronize()
+    ro, ra = orc.gather_attn(to_np(q), to_np(k), to_np(v), idx, cnt)
+    for o, a in res:
+        assert_close(o, a, ro, ra, torch.bfloat16, "gather, %s workspace" % fill)
+    ro, ra = orc.dense_attn(to_np(q32), to_np(k32), to_np(v32))
+    for o, a in res32:
+        assert_close(o, a, ro, ra, torch.float32, "fp32 dense, %s workspace" % fill)
+
+
 def test_one_workspace_many_calls(orc):
     """Calls of different shapes back to back on one workspace (counters of one call left for the next)."""
     ws = torch.empty(1 << 24, dtype=torch.uint8, device=DEV)

@@ -64,6 +64,20 @@ def test_topk_long(orc, n, m, s, r):
     _topk_case(orc, 1, 8, 2, n, m, s, r, 20 + n % 97, scores=False)
 
 
+@pytest.mark.parametrize("subs", [1, 2, 8])
+def test_topk_chunk_sizes(orc, subs):
+    """Chunks of 1, 2 and 8 sub-chunks: ragged last chunks and sub-chunks, windows cutting chunks,
+    a chunk taking only some of its ties, and heads with few distinct codes (massive ties)."""
+    old = ops.get_tuning("topk_subs")
+    ops.set_tuning("topk_subs", subs)
+    try:
+        for n, m, s, r, pool in [(50001, 1600, 128, 128, None), (70000, 3000, 5000, 9000, None),
+                                 (40000, 900, 64, 64, 3), (16384, 500, 0, 0, None)]:
+            _topk_case(orc, 2, 8, 2, n, m, s, r, 300 + subs + n % 11, pool=pool, scores=False)
+    finally:
+        ops.set_tuning("topk_subs", old)
+
+
 @pytest.mark.parametrize("pool", [1, 2, 5])
 def test_topk_massive_ties(orc, pool):
     """Few distinct signatures: almost every position ties; the lower position must win."""
