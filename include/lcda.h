@@ -147,7 +147,10 @@ int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_st
  * of Eq. (3.1): the same quantities lse_merge_local returns after
  * cached_attn_lse, up to floating-point summation order.  Because the split
  * of the softmax sum is exact, the cached and local tokens are treated as one
- * token range: one split pass and one combine pass.
+ * token range: one split pass and one combine pass.  For a document shared by
+ * B > 1 items (kv_batch_stride = 0) with more than 16 query rows per KV head,
+ * the pass that reads each document block once for all rows also takes every
+ * row's local tokens, as blocks that only that row's item sees.
  *
  *   q, k, v, kv_batch_stride, n          as in cached_attn_lse
  *   k_loc, v_loc, n_loc, n_loc_max       as in lse_merge_local
@@ -155,7 +158,8 @@ int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_st
  *   a_doc [B, Hq, d], alpha_doc [B, Hq]  fp32, or both NULL: if given, they
  *        receive cached_attn_lse's (A, alpha), and the call runs as the two
  *        separate calls (the same happens for fp32 inputs, for a document
- *        shared by B > 1 items, and for n = 0)
+ *        shared by B > 1 items with at most 16 query rows per KV head or with
+ *        n_loc_max = 0, and for n = 0)
  *   ws   at least lcda_ws_bytes_dense_decode_step(...) bytes
  */
 int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,

@@ -387,9 +387,10 @@ int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, con
 }
 
 // Fused decode step: one split pass over the unified token range (cache, then
-// the row's local tokens), then one combine.  Falls back to the two calls
-// when the fused form does not apply (fp32, shared document, doc-only outputs
-// requested).
+// the row's local tokens), then one combine.  A document shared by many rows
+// runs the 64-row split pass with the local tokens as extra per-row blocks.
+// Falls back to the two calls when no fused form applies (fp32, doc-only
+// outputs requested, a shared document read by 16 rows or fewer).
 size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride,
                                        int64_t n_loc_max) {
     if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX || n_loc_max < 0 ||
@@ -434,6 +435,41 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
     if (!ws || ws_bytes < need)
         return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, need);
     const bool shared = kv_batch_stride == 0 && B > 1;
+    if (shared && dtype == LCDA_BF16 && a_doc == nullptr && n > 0 && n_loc_max > 0) {
+        // A document shared by many rows: the 64-row split pass also takes each
+        // row's local tokens (as extra blocks seen by that row only), then one
+        // combine.
+        const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n, true);
+        if (p.kernel == kRows) {
+            const PartialLayout lay = partial_layout(B, Hq, p.splits);
+            SplitArgs a{};
+            a.q = q;
+            a.k = k;
+            a.v = v;
+            a.kv_batch_stride = 0;
+            a.n = n;
+            a.k2 = k_loc;
+            a.v2 = v_loc;
+            a.n2 = n_loc_max;
+            a.kv2_batch_stride = (int64_t)Hkv * n_loc_max * kD;
+            a.n2_b = n_loc;
+            a.B = B;
+            a.Hq = Hq;
+            a.Hkv = Hkv;
+            a.G = Hq / Hkv;
+            a.shared = 1;
+            a.rows = B * a.G;
+            a.row_groups = p.row_groups;
+            a.splits = p.splits;
+            a.blocks_per_split = p.blocks_per_split;
+            a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
+            a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
+            a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
+            a.scale_log2 = kLog2e / sqrtf((float)kD);
+            return finish(fn, p, a, dtype, B * Hq, out, alpha_out, nullptr, nullptr,
+                          static_cast<hipStream_t>(stream));
+        }
+    }
     if (dtype != LCDA_BF16 || shared || a_doc != nullptr || n == 0) {
         // Two-call form: cached_attn_lse, then lse_merge_local on its result.
         char* w = static_cast<char*>(ws);

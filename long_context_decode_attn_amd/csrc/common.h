@@ -79,6 +79,40 @@ __device__ __forceinline__ void finish_row(const Args& a, int64_t bhq, int c, fl
 // loads outstanding, and waits for stores to be acknowledged.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Reductions over lanes {l, l ^ 16} and {l, l ^ 32} without LDS: a
+// v_permlane16_swap (v_permlane32_swap) of two copies of x leaves, in every
+// lane l, the pair x[l & ~16], x[l | 16] (x[l & ~32], x[l | 32]) in the two
+// registers.  Issued as inline asm on two distinct registers: the compiler's
+// intrinsic for it folds the swap of a value with itself into a no-op.  The
+// s_nop 1 gives the two wait states the swap needs after the VALU writes of
+// its operands.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    float a = x, b = x;
+    swap16(a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    float a = x, b = x;
+    swap32(a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    float a = x, b = x;
+    swap16(a, b);
+    return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    float a = x, b = x;
+    swap32(a, b);
+    return a + b;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

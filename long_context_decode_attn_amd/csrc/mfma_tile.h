@@ -61,9 +61,11 @@ struct WaveState {
     float l[NT];
 };
 
+// valid: tokens of the block that exist (the rest are masked); col_ok: this
+// lane's query row (c16) sees the block at all (false masks every token).
 template <int NT>
 __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs& r, int valid, float scale, int j,
-                                              int c16) {
+                                              int c16, bool col_ok = true) {
     // V operand: column n = c16 of d-block nb is d = 8*c16 + nb; k element e is token tok_of(j, e).
     bf16x8 vb[8];
 #pragma unroll
@@ -99,11 +101,11 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
             for (int i = 0; i < 4; ++i) {
                 float x = s[rt][tb][i] * scale;
                 if (!full && 16 * tb + 4 * j + i >= valid) x = -INFINITY;
+                if (!col_ok) x = -INFINITY;
                 s[rt][tb][i] = x;
                 mx = fmaxf(mx, x);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_xor32(max_xor16(mx));
         bm[rt] = mx;
         need |= (mx > st.m[rt] + kLazy);
     }

@@ -206,8 +206,7 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_mfma(SplitArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
         float l = st.l[rt];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        l = sum_xor32(sum_xor16(l));
         if (j == 0) sm.ml[w][rt * 16 + c16] = make_float2(st.m[rt], l);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -76,8 +76,7 @@ __device__ __forceinline__ void load_rows_q(WaveState<1>& st, const SplitArgs& a
 __device__ __forceinline__ void write_rows(const WaveState<1>& st, const SplitArgs& a, int rows_w, int bkv, int h,
                                            int split, int j, int c16, int lane, bool direct) {
     float l = st.l[0];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l = sum_xor32(sum_xor16(l));
     const float m = st.m[0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -157,10 +156,70 @@ __device__ __forceinline__ void read_block(BlockRegs& r, uint32_t addr) {
         : "memory");
 }
 
+// Block t of a head's rows straight into registers (buffer loads; rows at or
+// past n_eff read as zero, and live = false issues an empty request).
+// Returns the rows of the block that exist.
+template <bool NTL>
+__device__ __forceinline__ int load_rows_block(BlockRegs& r, const uint16_t* kh, const uint16_t* vh, int64_t t,
+                                               int64_t n_eff, bool live, uint32_t koff, uint32_t voff) {
+    const int64_t left = n_eff - t;
+    const int valid = (int)(left < kBlock ? left : kBlock);
+    const int nrec = live ? valid * kD * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh + t * kD), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vh + t * kD), 0, nrec, kRsrcWord3);
+    constexpr int aux = NTL ? 2 : 0;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            r.k[tb][c] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 4096 * tb + 64 * c, 0, aux);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        r.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + (e < 4 ? 0 : 4096) + 256 * (e & 3), 0, aux);
+    return valid;
+}
+
+// Local tokens in the same pass (the fused decode step over a shared document):
+// each batch item's private tokens are an extra range attended to by its own G
+// rows only.  A wavefront's 16 rows belong to items i0 .. i1; the local blocks
+// of those items, numbered k = (item - i0) * nbl + block, go to the splits in
+// turn (split s takes k = s, s + splits, ...), so each wavefront runs about
+// one extra block, with the rows of other items masked.
+struct LocalWork {
+    int i0 = 0, nbl = 1;
+    int64_t count = 0;   // local blocks of this wavefront's items
+};
+
+__device__ __forceinline__ LocalWork local_work(const SplitArgs& a, int rows_w) {
+    LocalWork lw;
+    if (a.k2 == nullptr || a.n2 <= 0 || rows_w >= a.rows) return lw;
+    lw.i0 = rows_w / a.G;
+    const int i1 = (min(rows_w + 16, a.rows) - 1) / a.G;
+    lw.nbl = (int)((a.n2 + kBlock - 1) / kBlock);
+    lw.count = (int64_t)(i1 - lw.i0 + 1) * lw.nbl;
+    return lw;
+}
+
+template <bool NTL>
+__device__ __forceinline__ int load_local_block(BlockRegs& r, const SplitArgs& a, int h, const LocalWork& lw, int64_t k,
+                                                uint32_t koff, uint32_t voff) {
+    const int item = lw.i0 + (int)(k / lw.nbl);
+    const int64_t t = (int64_t)kBlock * (k % lw.nbl);
+    const int64_t n_item = a.n2_b ? min(max((int64_t)a.n2_b[item], (int64_t)0), a.n2) : a.n2;
+    const int64_t off = (int64_t)item * a.kv2_batch_stride + (int64_t)h * a.n2 * kD;
+    const uint16_t* kh = static_cast<const uint16_t*>(a.k2) + off;
+    const uint16_t* vh = static_cast<const uint16_t*>(a.v2) + off;
+    const bool live = t < n_item;
+    return load_rows_block<NTL>(r, kh, vh, live ? t : 0, n_item, live, koff, voff) * (live ? 1 : 0);
+}
+
 // SLOTS: ring slots (SLOTS - 1 blocks ahead).  WPE: waves per SIMD the
 // register allocation leaves room for.  DIRECT: one split per unit, rows
-// finished in place.
-template <int SLOTS, bool NTL, int WPE, bool DIRECT>
+// finished in place.  LOCAL: the rows' local tokens (a.k2, a.v2) are attended
+// to in the same pass.
+template <int SLOTS, bool NTL, int WPE, bool DIRECT, bool LOCAL = false>
 __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
     constexpr int kSlots = SLOTS, kAhead = SLOTS - 1;
     __shared__ __attribute__((aligned(16))) char ring[kSlots][kSlotBytes];
@@ -181,6 +240,15 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
     const int64_t t_end = min(n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
     const int nblk = t_end > t_begin ? (int)((t_end - t_begin + kBlock - 1) / kBlock) : 0;
 
+    // The first local block is requested with the query fragments; it lands
+    // while the document's blocks stream.
+    LocalWork lw;
+    BlockRegs lr;
+    int lvalid = 0;
+    if (LOCAL) {
+        lw = local_work(a, rows_w);
+        if (split < lw.count) lvalid = load_local_block<NTL>(lr, a, h, lw, split, koff, voff);
+    }
     WaveState<1> st;
     load_rows_q(st, a, rows_w, bkv, h, j, c16);
     wait_vm_all();   // only the ring's requests are outstanding from here on
@@ -209,6 +277,18 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
     }
     wait_vm_all();   // the empty requests past the end
 
+    if (LOCAL) {
+        const int r = rows_w + c16;
+        for (int64_t k = split; k < lw.count; k += a.splits) {
+            if (k != split) {
+                lvalid = load_local_block<NTL>(lr, a, h, lw, k, koff, voff);
+                wait_vm_all();
+            }
+            const int item = lw.i0 + (int)(k / lw.nbl);
+            if (lvalid > 0) compute_block<1>(st, lr, lvalid, a.scale_log2, j, c16, r < a.rows && r / a.G == item);
+        }
+    }
+
     write_rows(st, a, rows_w, bkv, h, split, j, c16, lane, DIRECT);
 
     // Several splits: the combine pass merges them (a unit here has 64 rows x
@@ -222,28 +302,6 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
 // four requests of a block go to the same addresses at about the same time and
 // are served once from the caches (cached loads), so HBM still reads each
 // block once.
-template <bool NTL>
-__device__ __forceinline__ int load_rows_block(BlockRegs& r, const uint16_t* kh, const uint16_t* vh, int64_t t,
-                                               int64_t n_eff, bool live, uint32_t koff, uint32_t voff) {
-    const int64_t left = n_eff - t;
-    const int valid = (int)(left < kBlock ? left : kBlock);
-    const int nrec = live ? valid * kD * 2 : 0;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh + t * kD), 0, nrec, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vh + t * kD), 0, nrec, kRsrcWord3);
-    constexpr int aux = NTL ? 2 : 0;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            r.k[tb][c] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 4096 * tb + 64 * c, 0, aux);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        r.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + (e < 4 ? 0 : 4096) + 256 * (e & 3), 0, aux);
-    return valid;
-}
-
 template <bool NTL, int WPE, bool DIRECT>
 __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows_regs(SplitArgs a) {
     const int lane = threadIdx.x & 63;
@@ -294,6 +352,11 @@ int split_rows_per_group() { return kRowsPerGroup; }
 hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
     dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
     const int variant = (int)tuning().rows_variant;
+    if (a.k2 != nullptr) {   // local tokens in the same pass: the default ring variant
+        if (a.direct) hipLaunchKernelGGL((k_split_rows<4, true, 1, true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_split_rows<4, true, 2, false, true>), grid, block, 0, st, a);
+        return hipGetLastError();
+    }
     if (a.direct) hipLaunchKernelGGL((k_split_rows<4, true, 1, true>), grid, block, 0, st, a);
     else if (variant == 1) hipLaunchKernelGGL((k_split_rows<3, true, 3, false>), grid, block, 0, st, a);
     else if (variant == 2) hipLaunchKernelGGL((k_split_rows<3, true, 2, false>), grid, block, 0, st, a);

@@ -254,19 +254,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
     // Merge the 4 lane groups of the wave (lanes c16, c16+16, c16+32, c16+48).
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        float M = fmaxf(m[r], __shfl_xor(m[r], 16, 64));
-        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        const float M = max_xor32(max_xor16(m[r]));
         const float wt = fast_exp2(m[r] - M);
-        float L = l[r] * wt;
-        L += __shfl_xor(L, 16, 64);
-        L += __shfl_xor(L, 32, 64);
+        const float L = sum_xor32(sum_xor16(l[r] * wt));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[r][e] * wt;
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            acc[r][e] = x;
-        }
+        for (int e = 0; e < 8; ++e) acc[r][e] = sum_xor32(sum_xor16(acc[r][e] * wt));
         if (j == 0) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.o[w][r][8 * c16 + e] = acc[r][e];

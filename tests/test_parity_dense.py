@@ -238,6 +238,19 @@ def test_decode_step_fused(orc, n, n_loc):
     _step_case(orc, len(n_loc), 32, 8, n, max(n_loc), n_loc, torch.bfloat16, 1000 + n)
 
 
+@pytest.mark.parametrize("B,Hq,n,n_loc", [
+    (16, 8, 3000, [512] * 15 + [300]),                      # 64 rows: one 64-row group, one local block per wavefront
+    (20, 8, 5003, [(37 * i) % 301 for i in range(20)]),     # 80 rows: two groups, ragged and empty local ranges
+    (11, 6, 2000, [(53 * i) % 130 + 1 for i in range(11)]),  # G = 3: a wavefront's rows span parts of items
+    (16, 8, 200, [700] * 16),                               # few splits: several local blocks per wavefront
+    (8, 8, 20, [64, 0, 33, 1, 64, 5, 31, 32]),              # one block: one split, rows finished in place
+])
+def test_decode_step_shared_rows_local(orc, B, Hq, n, n_loc):
+    """A shared document with more than 16 rows per KV head: the 64-row pass also takes each row's local
+    tokens (blocks seen only by that item's rows), then one combine."""
+    _step_case(orc, B, Hq, 2, n, max(n_loc), n_loc, torch.bfloat16, 1200 + B + n, shared=True)
+
+
 def test_decode_step_fallbacks(orc):
     """fp32, a shared document, and doc-only outputs run as the two separate calls."""
     _step_case(orc, 2, 8, 2, 700, 64, [64, 3], torch.float32, 1100)
