@@ -5,7 +5,7 @@ A step is one decode step of the named workload through the HIP library:
   dense61k    (default) Qwen3-4B-shaped layer: 8 KV heads, 32 query heads, d=128,
               n=61,440 bf16, batch 1: cached_attn_lse + lse_merge_local (256 local tokens)
   shared36    36 layers of one shared 61,440-token document, 16 queries, 512 private
-              local tokens each: 36 x (cached_attn_lse + lse_merge_local)
+              local tokens each: 36 x dense_decode_step (cached_attn_lse + lse_merge_local)
   sparse128k  HashAttention step: 8 KV heads, 32 query heads, n=131,072 bf16, batch 8,
               m = n/32 + 128 sink + 128 recent: sig_score_topk + gather_attn
   needles512k n=524,288 bf16, batch 4, 64 planted needles per head: dense vs sparse (m=n/64)
@@ -167,7 +167,9 @@ def bench_dense(args, cfg, layers=1):
                                                      layer_bytes) if fused else None,
                      "kernel": ("k_split_mfma (dense_decode_step: cache + local tokens, LSE combine in-kernel; "
                                 "one launch per layer)") if fused else
-                               "k_split_mfma + k_split_mfma (cached_attn_lse, lse_merge_local) per layer",
+                               ("k_split_rows + k_combine per layer (dense_decode_step on a shared document: "
+                                "64-row document pass that also takes each row's local tokens, then the combine; "
+                                "avg_launch_us is the per-layer time of the pair)"),
                      "bytes_per_launch": layer_bytes, "avg_launch_us": launch_us},
         "rotations": rot,
         "two_call_ms_per_step": ms_two,
@@ -376,7 +378,8 @@ def main():
                           "rotations": res["rotations"]}
         line["step"] = ("dense_decode_step: cached_attn_lse + lse_merge_local as one split-KV launch whose last "
                         "workgroup per (batch, KV head) does the LSE combine" if not cfg.shared_doc else
-                        "36 x (cached_attn_lse + lse_merge_local) over one shared document")
+                        "36 x dense_decode_step over one shared document (cached_attn_lse + lse_merge_local as "
+                        "one 64-row split-KV pass that also takes each row's local tokens, then one combine)")
         line["cached_attn_lse_us"] = res["cached_attn_lse_us"]
         line["two_call_ms_per_step"] = res["two_call_ms_per_step"]
         line["two_call_tbps"] = res["two_call_tbps"]

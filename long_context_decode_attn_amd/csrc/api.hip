@@ -126,7 +126,7 @@ int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows
 // Workspace of sig_score_topk: histograms, per-chunk and per-head selection results.
 struct TopkLayout {
     int chunks;
-    size_t hist_off, chunk_off, head_off, bytes;
+    size_t hist_off, chunk_off, head_off, ctr_off, bytes;
 };
 
 TopkLayout topk_layout(int B, int Hq, int64_t n) {
@@ -137,7 +137,8 @@ TopkLayout topk_layout(int B, int Hq, int64_t n) {
     l.hist_off = 0;
     l.chunk_off = l.hist_off + round_up(rows * l.chunks * topk_hist_row() * sizeof(uint32_t));
     l.head_off = l.chunk_off + round_up(rows * l.chunks * 4 * sizeof(int32_t));
-    l.bytes = l.head_off + round_up(rows * 2 * sizeof(int32_t));
+    l.ctr_off = l.head_off + round_up(rows * 2 * sizeof(int32_t));
+    l.bytes = l.ctr_off + round_up(rows * sizeof(unsigned long long));   // one counter per (b, KV head) <= rows
     return l;
 }
 
@@ -560,6 +561,7 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int 
     a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.hist_off);
     a.chunk_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.chunk_off);
     a.head_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.head_off);
+    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
     a.chunks = lay.chunks;
     a.chunk_len = topk_chunk_len(n);
     return hip_status(fn, launch_topk(a, static_cast<hipStream_t>(stream)));

@@ -13,6 +13,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;                       // head dimension (fixed)
+constexpr int kRsrcWord3 = 0x00020000;        // gfx9 raw buffer resource: 32-bit data format, no swizzle
 constexpr float kLog2e = 1.4426950408889634f; // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;   // ln(2)
 // Finite stand-in for "no token seen yet": exp2(kNoMax - m) is 0 for any real

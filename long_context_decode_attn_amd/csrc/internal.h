@@ -123,8 +123,9 @@ struct TopkArgs {
     int32_t* count;             // [B, Hq]
     int8_t* scores;             // [B, Hq, n] or null
     uint32_t* hist;             // ws: [B, Hq, chunks, topk_hist_row()] distance histograms
-    int32_t* chunk_info;        // ws: [B, Hq, chunks, 4] (output offset, ties taken, ties, -)
+    int32_t* chunk_info;        // ws: [B, Hkv, chunks, G, 4] (output offset, ties taken, ties, t)
     int32_t* head_info;         // ws: [B, Hq, 2] (t, quota)
+    unsigned long long* ctr;    // ws: [B, Hkv] arrival counters of the histogram pass
     int chunks;                 // ceil(n / chunk_len) <= 64
     int64_t chunk_len;
 };

@@ -51,7 +51,6 @@ struct BlockRegs {
     u32x4 v[8];     // [k element e]: 8 d values of token tok_of(j, e)
 };
 
-constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format, no swizzle
 
 template <int NT>
 struct WaveState {

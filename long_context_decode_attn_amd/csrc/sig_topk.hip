@@ -12,26 +12,29 @@
 // ties a chunk takes are its first `taken_c` ties, where taken_c follows from
 // the tie counts of the chunks before it.
 //
-// Three kernels; the two that scan codes read each KV head's codes once for
-// all G query heads of its group.  The scans are bound by instruction issue
+// Two kernels, each reading a KV head's codes once for all G query heads of
+// its group.  The scans are bound by instruction issue
 // (one xor + popcount per position and query head, plus bookkeeping), so the
 // per-position work is kept to a few vector instructions.
 //   1. k_topk_hist    - per chunk: the 33-bin distance histogram of each query
 //                       head, in 64 per-lane LDS copies laid out so that the
-//                       increments of one instruction hit distinct banks.
-//   2. k_topk_select  - per query head (one wavefront, lane = chunk): t and the
+//                       increments of one instruction hit distinct banks.  The
+//                       last workgroup of a KV head to finish (arrival counter)
+//                       then runs the selection of its G query heads:
+//      select         - per query head (one wavefront, lane = chunk): t and the
 //                       quota from the summed histograms, each chunk's ties
 //                       taken, the window positions outside the top m in the
 //                       chunks a window edge cuts (only the window part of those
-//                       chunks is scanned), per-chunk output offsets, the count
-//                       and the -1 padding.
-//   3. k_topk_compact - per chunk: the codes are staged in LDS; one wavefront
-//                       per query head writes the selected positions in order at
-//                       the chunk's offset (ballot / mbcnt ranks).  A chunk that
-//                       takes all or none of its ties and meets no window keeps
-//                       exactly the positions with d below one threshold; only
-//                       the chunk taking part of its ties and the chunks a
-//                       window meets walk the full rule.
+//                       chunks is scanned), per-chunk output offsets, the count,
+//                       the window entries of the output (its lowest and highest
+//                       entries) and the -1 padding.
+//   2. k_topk_compact - per chunk: each thread holds 16 consecutive positions
+//                       and forms per-head 16-bit selection masks (below one
+//                       threshold, plus the ties for the one chunk that takes
+//                       only some of them, plus the window positions); DPP
+//                       scans in each wavefront and one exchange of wavefront
+//                       totals place them, and each thread stores its selected
+//                       positions outside the windows.
 // A chunk is a whole number of 4096-position sub-chunks, chosen so that a head
 // has at most 64 chunks.  Positions are below n <= INT32_MAX; loop bounds that
 // can step past n are 64-bit.
@@ -160,15 +163,16 @@ __device__ void select_head(const TopkArgs& a, int b, int h, int g, int lane, ui
     load_part(pr, ks, lane);
 
     // This lane's chunk histogram.
+    // (The other workgroups of the head wrote them: device-scope loads.)
     uint32_t hv[kBins];
     {
-        const u32x4* hrow = reinterpret_cast<const u32x4*>(a.hist + (row * C + min(lane, C - 1)) * kRow);
+        const uint32_t* hrow = a.hist + (row * C + min(lane, C - 1)) * kRow;
 #pragma unroll
-        for (int k = 0; k < kRow / 4; ++k) {
-            const u32x4 v = hrow[k];
+        for (int k = 0; k < kRow / 2; ++k) {
+            const uint64_t v = load_dev_u64(hrow + 2 * k);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * k + e < kBins) hv[4 * k + e] = lane < C ? v[e] : 0u;
+            for (int e = 0; e < 2; ++e)
+                if (2 * k + e < kBins) hv[2 * k + e] = lane < C ? (uint32_t)(v >> (32 * e)) : 0u;
         }
     }
     // The head's histogram: bins transposed through LDS, lane d (< 33) sums bin d.
@@ -235,7 +239,15 @@ __device__ void select_head(const TopkArgs& a, int b, int h, int g, int lane, ui
         a.head_info[2 * row] = t;
         a.head_info[2 * row + 1] = (int32_t)quota;
     }
-    for (int64_t i = total + lane; i < a.cap; i += 64) a.idx[row * a.cap + i] = -1;
+    // The window positions are the lowest and the highest entries of I: the
+    // sink part is I[0 .. s_end) = 0 .. s_end - 1 and the recent part fills
+    // the last n - r_beg entries.  They are written here; the compaction
+    // counts them but stores only the positions of the top m.
+    int32_t* out = a.idx + row * a.cap;
+    for (int64_t i = lane; i < s_end; i += 64) out[i] = (int32_t)i;
+    const int64_t nr = n - r_beg;
+    for (int64_t i = lane; i < nr; i += 64) out[total - nr + i] = (int32_t)(r_beg + i);
+    for (int64_t i = total + lane; i < a.cap; i += 64) out[i] = -1;
 }
 
 // ---- 1. histogram ------------------------------------------------------------------
@@ -337,15 +349,17 @@ __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
         uint32_t sum = 0;
 #pragma unroll 8
         for (int l = 0; l < 64; ++l) sum += row[(l + tid) & 63];
-        a.hist[(((int64_t)b * a.Hq + h * G + g) * a.chunks + c) * kRow + bin] = sum;
+        store_dev(a.hist + (((int64_t)b * a.Hq + h * G + g) * a.chunks + c) * kRow + bin, sum);
     }
-}
 
-__global__ __launch_bounds__(256) void k_topk_select(TopkArgs a) {
-    __shared__ uint32_t tr[4][kBins * 65];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int h = blockIdx.x, b = blockIdx.y;
-    for (int g = w; g < a.G; g += 4) select_head(a, b, h, g, lane, tr[w]);
+    // The head's last workgroup to finish selects for its G query heads (one
+    // wavefront each), reusing the counters' LDS.
+    __shared__ int s_last;
+    if (arrive_count(a.ctr + (int64_t)b * a.Hkv + h, (uint32_t)a.chunks, &s_last)) {
+        uint32_t* tr = sm.cnt + (tid >> 6) * (kBins * 65);
+        static_assert(4 * kBins * 65 <= HistSmem<MAXG>::kWords, "select scratch fits the counters' LDS");
+        for (int g = tid >> 6; g < G; g += 4) select_head(a, b, h, g, lane, tr);
+    }
 }
 
 // n == 0: no positions; every row gets count 0 and is padded with -1.
@@ -483,6 +497,9 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
     bool partial = false;   // uniform: every thread read the same chunk records
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) partial |= mode[g] == 2;
+    // Rows whose byte offsets fit 32 bits are stored through a buffer
+    // resource (offset arithmetic in 32 bits, the range check in hardware).
+    const bool small_cap = a.cap < ((int64_t)1 << 29);
 
     int par = 0;
     for (int64_t gb = beg; gb < end; gb += (int64_t)kGrp * kSub, par ^= 1) {
@@ -506,10 +523,24 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int g = 2 * k + e;
-                    const uint32_t sm = below_mask(x, q[g], nthr[g]) & valid;
+                    uint32_t sm, tm = 0;
+                    if (partial && mode[g] == 2) {   // uniform
+                        // d < t and d <= t from the same popcounts; ties rank over every
+                        // position of the chunk, window positions included.
+                        uint32_t l = 0, le = 0;
+#pragma unroll
+                        for (int jj = 15; jj >= 0; --jj) {
+                            const uint32_t pc = (uint32_t)__builtin_popcount(x[jj] ^ q[g]);
+                            l = __builtin_amdgcn_alignbit(l, pc + nthr[g], 31);
+                            le = __builtin_amdgcn_alignbit(le, pc + nt1[g], 31);
+                        }
+                        sm = l & valid;
+                        tm = le & ~l & valid;
+                    } else {
+                        sm = below_mask(x, q[g], nthr[g]) & valid;
+                    }
                     m2[e] = g < G ? (sm | win) : 0u;
-                    // Ties rank over every position of the chunk, window positions included.
-                    t2[e] = (partial && mode[g] == 2) ? below_mask(x, q[g], nt1[g]) & ~sm & valid : 0u;
+                    t2[e] = tm;
                 }
                 sel[u][k] = m2[0] | (m2[1] << 16);
                 tie[u][k] = t2[0] | (t2[1] << 16);
@@ -577,18 +608,49 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
                 const uint32_t ex2 = run + base + inc[u][k] - cnt[u][k];
                 run += all;
                 const int64_t i0 = gb + (int64_t)u * kSub + 16 * tid;
+                // Window positions were stored by the select: skip them, keeping
+                // the ranks of the others.  The buffer resource bounds every
+                // store to the row (cap entries).
+                const uint32_t win = meets_win ? window_mask(i0, s_end, r_beg) : 0u;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int g = 2 * k + e;
                     if (g < G) {
-                        int32_t* out = a.idx + (row0 + g) * a.cap;
-                        int pos = off[g] + field16(ex2, e);
-                        uint32_t m = (sel[u][k] >> (16 * e)) & 0xFFFFu;
-                        while (m) {
-                            const int j = __builtin_ctz(m);
-                            if (pos < a.cap) out[pos] = (int32_t)(i0 + j);
-                            ++pos;
-                            m &= m - 1u;
+                        const uint32_t mine = (sel[u][k] >> (16 * e)) & 0xFFFFu;
+                        const uint32_t wm = mine & win;   // window positions among them
+                        uint32_t m = mine ^ wm;
+                        if (__ballot(m != 0u)) {
+                            const int base = off[g] + field16(ex2, e);
+                            int32_t* out = a.idx + (row0 + g) * a.cap;
+                            if (small_cap) {
+                                const __amdgpu_buffer_rsrc_t ro =
+                                    __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)(a.cap * 4), kRsrcWord3);
+                                uint32_t pos4 = 4u * (uint32_t)base;
+                                if (__ballot(wm != 0u)) {
+                                    // a kept position's slot also counts the window positions before it
+                                    while (m) {
+                                        const int j = __builtin_ctz(m);
+                                        const uint32_t w4 = 4u * (uint32_t)__builtin_popcount(wm & ((1u << j) - 1u));
+                                        __builtin_amdgcn_raw_buffer_store_b32((int)(i0 + j), ro, pos4 + w4, 0, 0);
+                                        pos4 += 4u;
+                                        m &= m - 1u;
+                                    }
+                                } else {
+                                    while (m) {
+                                        const int j = __builtin_ctz(m);
+                                        __builtin_amdgcn_raw_buffer_store_b32((int)(i0 + j), ro, pos4, 0, 0);
+                                        pos4 += 4u;
+                                        m &= m - 1u;
+                                    }
+                                }
+                            } else {
+                                while (m) {
+                                    const int j = __builtin_ctz(m);
+                                    const int pos = base + __builtin_popcount(mine & ((1u << j) - 1u));
+                                    if (pos < a.cap) out[pos] = (int32_t)(i0 + j);
+                                    m &= m - 1u;
+                                }
+                            }
                         }
                     }
                 }
@@ -628,10 +690,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
         else { if (sc) LCDA_HIST(8, false, true); else LCDA_HIST(8, false, false); }
     }
 #undef LCDA_HIST
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_topk_select, dim3(a.Hkv, a.B), dim3(256), 0, st, a);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.G <= 4) {
         if (vec) hipLaunchKernelGGL((k_topk_compact<4, true>), grid, block, 0, st, a);

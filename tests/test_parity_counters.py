@@ -81,6 +81,31 @@ def test_garbage_workspace_gather_and_fp32(orc, fill):
         assert_close(o, a, ro, ra, torch.float32, "fp32 dense, %s workspace" % fill)
 
 
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_garbage_workspace_topk(orc, fill):
+    """TOPK: the last histogram workgroup of each KV head runs the selection, found through the same tagged
+    counters; indices stay bit-exact whatever the workspace held, over repeated calls of two shapes."""
+    g = np.random.default_rng(76)
+    cases = [(2, 8, 2, 40000, 1300, 64, 64), (3, 4, 1, 9001, 300, 16, 16)]
+    nb = max(ops.ws_bytes_sig_score_topk(B, Hq, Hkv, n) for B, Hq, Hkv, n, _, _, _ in cases)
+    if fill == "ones":
+        ws = torch.full((nb,), 255, dtype=torch.uint8, device=DEV)
+    else:
+        ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, generator=torch.Generator().manual_seed(77)).to(DEV)
+    print("case garbage workspace (topk) fill=%s" % fill, flush=True)
+    for rep in range(2):
+        for B, Hq, Hkv, n, m, s_, r_ in cases:
+            ks = g.integers(0, 2 ** 32, (B, Hkv, n), dtype=np.uint64).astype(np.uint32)
+            qs = g.integers(0, 2 ** 32, (B, Hq), dtype=np.uint64).astype(np.uint32)
+            kt = torch.from_numpy(ks.view(np.int32).copy()).to(DEV)
+            qt = torch.from_numpy(qs.view(np.int32).copy()).to(DEV)
+            idx, cnt, _ = ops.sig_score_topk(kt, qt, m, s_, r_, ws=ws)
+            torch.cuda.synchronize()
+            ri, rc, _ = orc.sig_score_topk(ks, qs, m, s_, r_)
+            np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+            np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+
+
 def test_one_workspace_many_calls(orc):
     """Calls of different shapes back to back on one workspace (counters of one call left for the next)."""
     ws = torch.empty(1 << 24, dtype=torch.uint8, device=DEV)
