@@ -62,6 +62,8 @@ struct WaveState {
 
 // valid: tokens of the block that exist (the rest are masked); col_ok: this
 // lane's query row (c16) sees the block at all (false masks every token).
+// The logits stay unscaled up to the exponent: the row max of s*scale is
+// scale times the max of s (scale > 0), and p = exp2(fma(s, scale, -m)).
 template <int NT>
 __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs& r, int valid, float scale, int j,
                                               int c16, bool col_ok = true) {
@@ -88,7 +90,17 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[tb][c]), st.q[rt][c], acc, 0, 0, 0);
             s[rt][tb] = acc;
         }
-    const bool full = valid >= kBlock;
+    // Masking only where some token is missing or some row does not see the
+    // block (a uniform branch around it).
+    if (__builtin_amdgcn_readfirstlane(valid) < kBlock || __ballot(!col_ok) != 0) {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * tb + 4 * j + i >= valid || !col_ok) s[rt][tb][i] = -INFINITY;
+    }
     float bm[NT];
     bool need = false;
 #pragma unroll
@@ -97,14 +109,8 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = s[rt][tb][i] * scale;
-                if (!full && 16 * tb + 4 * j + i >= valid) x = -INFINITY;
-                if (!col_ok) x = -INFINITY;
-                s[rt][tb][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = max_xor32(max_xor16(mx));
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rt][tb][i]);
+        mx = max_xor32(max_xor16(mx)) * scale;
         bm[rt] = mx;
         need |= (mx > st.m[rt] + kLazy);
     }
@@ -125,11 +131,12 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
     }
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
+        const float nm = -st.m[rt];
         float p[8];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[4 * tb + i] = fast_exp2(s[rt][tb][i] - st.m[rt]);
+            for (int i = 0; i < 4; ++i) p[4 * tb + i] = fast_exp2(fmaf(s[rt][tb][i], scale, nm));
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ps += p[e];
