@@ -163,8 +163,8 @@ def bench_dense(args, cfg, layers=1):
         "step_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK,
-                     "traffic": traffic_from_profile("split_mfma_" + ("dense61k" if layers == 1 else "shared36"),
-                                                     layer_bytes) if fused else None,
+                     "traffic": traffic_from_profile("split_mfma_dense61k", layer_bytes) if fused else
+                                traffic_from_profile("split_rows_shared36", layer_bytes, "split_rows"),
                      "kernel": ("k_split_mfma (dense_decode_step: cache + local tokens, LSE combine in-kernel; "
                                 "one launch per layer)") if fused else
                                ("k_split_rows + k_combine per layer (dense_decode_step on a shared document: "
@@ -181,7 +181,7 @@ def bench_dense(args, cfg, layers=1):
 
 
 # ---------------------------------------------------------------- traffic ----
-def traffic_from_profile(name: str, algorithmic_bytes: int):
+def traffic_from_profile(name: str, algorithmic_bytes: int, kind: str = "split_mfma"):
     """HBM bytes per launch of the dominant kernel from the committed counter summary
     profiles/traffic_<name>.txt (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the
     same counter's reading for a copy of known size).  None when there is no summary or the
@@ -195,7 +195,7 @@ def traffic_from_profile(name: str, algorithmic_bytes: int):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != kernel_source_digest():
+    if kv.get("source_digest") != kernel_source_digest(kind):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -275,6 +275,7 @@ def bench_sparse(args, cfg, rot=None):
         "gather_attn_us": ms_g * 1e3,
         "topk_sig_tbps": sig_bytes / (ms_t * 1e-3) / 1e12,
         "gather_tbps": gather_bytes / (ms_g * 1e-3) / 1e12,
+        "gather_bytes": gather_bytes,
         "rotations": rot,
     }
     return res, sets[0]
@@ -399,7 +400,10 @@ def main():
         line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"]})
         ach = res["gather_tbps"] * 1e12
         line["roofline"] = {"bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                            "frac": ach / HBM_PEAK, "traffic": None, "kernel": "gather_attn (unique rows)"}
+                            "frac": ach / HBM_PEAK,
+                            "traffic": traffic_from_profile("split_valu_sparse128k", int(res["gather_bytes"]),
+                                                            "split_valu"),
+                            "kernel": "gather_attn (k_split_valu gather + k_combine; achieved on unique rows)"}
         line["config"] = {"workload": "sparse128k: " + cfg.name, "launch": launch}
         line["detail"] = res
         if args.cpu_seconds > 0:

@@ -23,14 +23,19 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNEL_SOURCES = ("long_context_decode_attn_amd/csrc/split_mfma.hip", "long_context_decode_attn_amd/csrc/common.h",
-                  "long_context_decode_attn_amd/csrc/internal.h")
+# The sources each measured kernel is built from (the digest of a traffic summary).
+_C = "long_context_decode_attn_amd/csrc/"
+KERNEL_SOURCES = {
+    "split_mfma": (_C + "split_mfma.hip", _C + "mfma_tile.h", _C + "common.h", _C + "internal.h"),
+    "split_rows": (_C + "split_rows.hip", _C + "mfma_tile.h", _C + "common.h", _C + "internal.h"),
+    "split_valu": (_C + "split_valu.hip", _C + "common.h", _C + "internal.h"),
+}
 
 
-def kernel_source_digest(paths=KERNEL_SOURCES) -> str:
-    """First 16 hex digits of the sha256 over the split kernel's sources."""
+def kernel_source_digest(kind: str = "split_mfma") -> str:
+    """First 16 hex digits of the sha256 over the sources of kernel family `kind`."""
     h = hashlib.sha256()
-    for p in paths:
+    for p in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -118,7 +123,8 @@ def traffic(a) -> str:
         "hbm_bytes_per_launch = %.0f" % hbm,
         "algorithmic_bytes_per_launch = %d" % a.bytes,
         "hbm_over_algorithmic = %.4f" % (hbm / a.bytes),
-        "source_digest = %s" % kernel_source_digest(),
+        "source_kind = %s" % a.kind,
+        "source_digest = %s" % kernel_source_digest(a.kind),
     ]
     for c in a.command or []:
         out.append("command = %s" % c)
@@ -141,6 +147,8 @@ def main(argv=None):
     t.add_argument("--copy-match", default="")
     t.add_argument("--match", required=True)
     t.add_argument("--bytes", type=int, required=True, help="algorithmic bytes per launch")
+    t.add_argument("--kind", default="split_mfma", choices=sorted(KERNEL_SOURCES),
+                   help="kernel family whose sources the digest covers")
     t.add_argument("--command", action="append", help="command that produced the inputs (repeatable)")
     t.add_argument("--out")
     a = ap.parse_args(argv)
