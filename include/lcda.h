@@ -198,7 +198,8 @@ const char* lcda_version(void);
  *   "rows_variant"   64-row workgroups: 0 = 4-slot LDS ring, 2 workgroups per CU;
  *                    1 = 3 slots, 3 per CU; 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU;
  *                    4-6 = every wavefront loads the block into registers (4: cached
- *                    loads, 2 workgroups per CU; 5: nontemporal; 6: cached, 1 per CU) (0)
+ *                    loads, 2 workgroups per CU; 5: nontemporal; 6: cached, 1 per CU);
+ *                    7 = 5-slot ring, 2 per CU (0)
  *   "direct_blocks"  units with at most this many token blocks run as one split
  *                    that writes its rows directly, without a combine pass, when
  *                    the units alone reach the workgroup target (16)

@@ -245,7 +245,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
     else if (!strcmp(key, "rows_wgs") && value > 0) t.rows_wgs = value;
     else if (!strcmp(key, "rows_kernel") && value <= 1) t.rows_kernel = value;
-    else if (!strcmp(key, "rows_variant") && value <= 6) t.rows_variant = value;
+    else if (!strcmp(key, "rows_variant") && value <= 7) t.rows_variant = value;
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
     else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;

@@ -64,7 +64,8 @@ struct Tuning {
     int64_t rows_kernel = 1;       // bf16 with more than 16 rows per KV head: 1 = 64-row workgroups, 0 = 32/64-row wavefronts
     int64_t rows_variant = 0;      // 64-row workgroups: 0 = 4-slot ring, 2 per CU; 1 = 3 slots, 3 per CU;
                                    // 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU; 4-6 = blocks in registers
-                                   // (4: cached loads, 2 per CU; 5: nontemporal; 6: cached, 1 per CU)
+                                   // (4: cached loads, 2 per CU; 5: nontemporal; 6: cached, 1 per CU);
+                                   // 7 = 5-slot ring, 2 per CU
     int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads,
                                    // 2 = two blocks ahead, 3 = nontemporal with two waves per SIMD
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads

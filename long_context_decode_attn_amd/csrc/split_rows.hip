@@ -352,8 +352,9 @@ int split_rows_per_group() { return kRowsPerGroup; }
 hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
     dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
     const int variant = (int)tuning().rows_variant;
-    if (a.k2 != nullptr) {   // local tokens in the same pass: the default ring variant
+    if (a.k2 != nullptr) {   // local tokens in the same pass: the default ring variant (or the 5-slot one)
         if (a.direct) hipLaunchKernelGGL((k_split_rows<4, true, 1, true, true>), grid, block, 0, st, a);
+        else if (variant == 7) hipLaunchKernelGGL((k_split_rows<5, true, 2, false, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_split_rows<4, true, 2, false, true>), grid, block, 0, st, a);
         return hipGetLastError();
     }
@@ -364,6 +365,7 @@ hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t
     else if (variant == 4) hipLaunchKernelGGL((k_split_rows_regs<false, 2, false>), grid, block, 0, st, a);
     else if (variant == 5) hipLaunchKernelGGL((k_split_rows_regs<true, 2, false>), grid, block, 0, st, a);
     else if (variant == 6) hipLaunchKernelGGL((k_split_rows_regs<false, 1, false>), grid, block, 0, st, a);
+    else if (variant == 7) hipLaunchKernelGGL((k_split_rows<5, true, 2, false>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_split_rows<4, true, 2, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }

@@ -61,7 +61,7 @@ def test_dense_shared_rows_kernel(orc, B, n):
     _dense_case(B, 8, 2, n, torch.bfloat16, 700 + B + n, shared=True, orc=orc)
 
 
-@pytest.mark.parametrize("variant", list(range(7)))
+@pytest.mark.parametrize("variant", list(range(8)))
 def test_dense_shared_rows_variants(orc, variant):
     """Every 64-row workgroup variant (LDS ring depths and occupancies, blocks in registers) gives the
     oracle's result, several blocks per workgroup and a ragged tail."""
