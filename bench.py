@@ -8,7 +8,9 @@ A step is one decode step of the named workload through the HIP library:
               local tokens each: 36 x dense_decode_step (cached_attn_lse + lse_merge_local)
   sparse128k  HashAttention step: 8 KV heads, 32 query heads, n=131,072 bf16, batch 8,
               m = n/32 + 128 sink + 128 recent: sig_score_topk + gather_attn
-  needles512k n=524,288 bf16, batch 4, 64 planted needles per head: dense vs sparse (m=n/64)
+  needles512k n=524,288 bf16, batch 4, 64 planted needles per head: the sparse step (m=n/64)
+              against cached_attn_lse on the same inputs, with needle recall, attention mass
+              captured and the sparse output's error against the dense one
 
 Inputs are synthetic (seeded, drawn on the GPU) and resident in HBM before the timed
 region.  Several independent input sets are cycled so that the bytes a cycle touches
@@ -281,6 +283,94 @@ def bench_sparse(args, cfg, rot=None):
     return res, sets[0]
 
 
+# ---------------------------------------------------------------- needles ----
+class NeedleSet(SparseSet):
+    """Config 5 inputs (planted needles) with the buffers of both the dense and the sparse decode."""
+
+    def __init__(self, cfg, rot, device="cuda"):
+        super().__init__(cfg, rot, device)
+        B, Hq = self.x["q"].shape[:2]
+        Hkv, n = self.x["k"].shape[1], self.x["k"].shape[2]
+        self.do = torch.empty((B, Hq, 128), device=device)
+        self.da = torch.empty((B, Hq), device=device)
+        nb = max(self.ws.numel(), ops.ws_bytes_cached_attn_lse(B, Hq, Hkv, 128, n, Hkv * n * 128))
+        if nb > self.ws.numel():
+            self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+
+    def dense(self):
+        ops.cached_attn_lse(self.x["q"], self.x["k"], self.x["v"], out=self.do, alpha=self.da, ws=self.ws)
+
+
+def needle_quality(s, cfg) -> dict:
+    """Recall of the planted needles in each query head's selected set (over all heads, and over the
+    first head of each KV group, along whose query the needles were planted), the attention mass the
+    set captures (e^{alpha_I - alpha}), and the sparse output's error against the dense one."""
+    G = cfg.Hq // cfg.Hkv
+    s.step()
+    s.dense()
+    torch.cuda.synchronize()
+    idx, cnt = s.idx.cpu().numpy(), s.cnt.cpu().numpy()
+    pos = s.x["needle_pos"].cpu().numpy()
+    B, Hq = cnt.shape
+    rec = np.empty((B, Hq))
+    for b in range(B):
+        for hq in range(Hq):
+            rec[b, hq] = np.isin(pos[b, hq // G], idx[b, hq, :cnt[b, hq]]).mean()
+    mass = torch.exp(s.oa - s.da).cpu().numpy()
+    err = (torch.linalg.vector_norm(s.o - s.do, dim=-1) / torch.linalg.vector_norm(s.do, dim=-1)).cpu().numpy()
+    other = np.ones((B, Hq), bool)
+    other[:, ::G] = False
+    res = {}
+    for name, sel in (("planted_head", ~other), ("other_heads", other)):
+        res.update({"needle_recall_%s_mean" % name: float(rec[sel].mean()),
+                    "needle_recall_%s_min" % name: float(rec[sel].min()),
+                    "mass_captured_%s_mean" % name: float(mass[sel].mean()),
+                    "mass_captured_%s_min" % name: float(mass[sel].min()),
+                    "rel_err_vs_dense_%s_mean" % name: float(err[sel].mean()),
+                    "rel_err_vs_dense_%s_max" % name: float(err[sel].max())})
+    return res
+
+
+def bench_needles(args, cfg):
+    rot = args.rot or 2
+    sets = [NeedleSet(cfg, r) for r in range(rot)]
+    torch.cuda.synchronize()
+    steps = args.steps
+    ms_s = run_steps([s.step for s in sets], steps, args.warmup, args.graph) / steps
+    ms_g = run_steps([s.gather for s in sets], steps, args.warmup, args.graph) / steps
+    ms_t = run_steps([s.topk for s in sets], steps, args.warmup, args.graph) / steps
+    ms_d = run_steps([s.dense for s in sets], steps, args.warmup, args.graph) / steps
+    G = cfg.Hq // cfg.Hkv
+    uniq = [traffic.unique_rows(s.idx.cpu().numpy(), s.cnt.cpu().numpy(), G) for s in sets]
+    sparse_bytes = float(np.mean([traffic.sparse_step_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2, s.cap, u)
+                                  for s, u in zip(sets, uniq)]))
+    gather_bytes = float(np.mean([u * 2 * cfg.d * 2 for u in uniq]))
+    sig_bytes = cfg.B * cfg.Hkv * cfg.n * 4
+    dense_bytes = traffic.dense_step_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.n, 2)
+    res = {
+        "value": cfg.B / (ms_s * 1e-3),
+        "ms_per_step": ms_s,
+        "steps": steps,
+        "sparse_step_bytes": sparse_bytes,
+        "sparse_step_tbps": sparse_bytes / (ms_s * 1e-3) / 1e12,
+        "sig_score_topk_us": ms_t * 1e3,
+        "topk_sig_tbps": sig_bytes / (ms_t * 1e-3) / 1e12,
+        "gather_attn_us": ms_g * 1e3,
+        "gather_bytes": gather_bytes,
+        "gather_tbps": gather_bytes / (ms_g * 1e-3) / 1e12,
+        "dense_queries_per_s": cfg.B / (ms_d * 1e-3),
+        "dense_ms_per_step": ms_d,
+        "dense_bytes": dense_bytes,
+        "dense_tbps": dense_bytes / (ms_d * 1e-3) / 1e12,
+        "dense_frac_of_peak": dense_bytes / (ms_d * 1e-3) / HBM_PEAK,
+        "speedup_sparse_over_dense": ms_d / ms_s,
+        "unique_rows": float(np.mean(uniq)),
+        "rotations": rot,
+    }
+    res.update(needle_quality(sets[0], cfg))
+    return res
+
+
 # -------------------------------------------------------------- CPU oracle ----
 def cpu_baseline_dense(cfg, seconds: float):
     """The oracle (plain C, fp64) on the host's cores over whole decode steps of the same workload."""
@@ -409,7 +499,16 @@ def main():
         if args.cpu_seconds > 0:
             line["cpu_baseline"] = cpu_baseline_sparse(cfg, args.cpu_seconds)
     else:
-        raise SystemExit("needles512k: use tests/test_needles.py or DESIGN.md for its report")
+        cfg = synth.CONFIGS[5]
+        res = bench_needles(args, cfg)
+        line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"]})
+        ach = res["gather_tbps"] * 1e12
+        line["roofline"] = {"bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": ach / HBM_PEAK, "traffic": None,
+                            "kernel": "gather_attn (k_split_valu gather + k_combine; achieved on unique rows)"}
+        line["config"] = {"workload": "needles512k: " + cfg.name, "launch": launch}
+        line["step"] = "sig_score_topk + gather_attn (value); cached_attn_lse on the same inputs (dense_*)"
+        line["detail"] = res
     line["device"] = dev_name
     line["host"] = platform.node()
     print(json.dumps(line))
