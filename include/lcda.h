@@ -208,9 +208,10 @@ const char* lcda_version(void);
  *                    2 = nontemporal two blocks ahead, 3 = as 0 with registers
  *                    capped so two workgroups share a CU (0)
  *   "gather_variant" GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads (0)
- *   "topk_subs"      TOPK scans: at least this many 4096-position sub-chunks per
- *                    workgroup (1..64; more where a head would otherwise exceed 64
- *                    chunks) (4)
+ *   "topk_subs"      TOPK scans: 4096-position sub-chunks per workgroup (1..64;
+ *                    more where a head would otherwise exceed 64 chunks); 0 picks
+ *                    the count that gives about topk_wgs workgroups (0)
+ *   "topk_wgs"       TOPK scans: workgroups a call aims at when topk_subs is 0 (512)
  * Returns LCDA_EINVAL for an unknown key or a negative (or, except
  * direct_blocks, zero) value.  lcda_get_tuning returns -1 for an unknown key. */
 int lcda_set_tuning(const char* key, int64_t value);

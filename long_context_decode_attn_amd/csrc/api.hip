@@ -123,22 +123,20 @@ int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows
     return hip_status(fn, launch_combine(c, st));
 }
 
-// Workspace of sig_score_topk: histograms, per-chunk and per-head selection results.
+// Workspace of sig_score_topk: the distance histograms of every chunk and of
+// the two window parts.
 struct TopkLayout {
     int chunks;
-    size_t hist_off, chunk_off, head_off, ctr_off, bytes;
+    size_t hist_off, bytes;
 };
 
-TopkLayout topk_layout(int B, int Hq, int64_t n) {
+TopkLayout topk_layout(int B, int Hq, int Hkv, int64_t n) {
     TopkLayout l;
-    const int64_t cl = topk_chunk_len(n);
+    const int64_t cl = topk_chunk_len(n, B * Hkv);
     l.chunks = (int)ceil_div(n, cl);
     const size_t rows = (size_t)B * Hq;
     l.hist_off = 0;
-    l.chunk_off = l.hist_off + round_up(rows * l.chunks * topk_hist_row() * sizeof(uint32_t));
-    l.head_off = l.chunk_off + round_up(rows * l.chunks * 4 * sizeof(int32_t));
-    l.ctr_off = l.head_off + round_up(rows * 2 * sizeof(int32_t));
-    l.bytes = l.ctr_off + round_up(rows * sizeof(unsigned long long));   // one counter per (b, KV head) <= rows
+    l.bytes = l.hist_off + round_up(rows * (l.chunks + 2) * topk_hist_row() * sizeof(uint32_t));
     return l;
 }
 
@@ -250,6 +248,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
     else if (!strcmp(key, "topk_subs") && value <= 64) t.topk_subs = value;
+    else if (!strcmp(key, "topk_wgs") && value > 0) t.topk_wgs = value;
     else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
     return LCDA_OK;
 }
@@ -268,6 +267,7 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "dense_variant")) return t.dense_variant;
     if (!strcmp(key, "gather_variant")) return t.gather_variant;
     if (!strcmp(key, "topk_subs")) return t.topk_subs;
+    if (!strcmp(key, "topk_wgs")) return t.topk_wgs;
     return -1;
 }
 
@@ -285,7 +285,7 @@ size_t lcda_ws_bytes_lse_merge_local(int B, int Hq, int Hkv, int d, int64_t n_lo
 
 size_t lcda_ws_bytes_sig_score_topk(int B, int Hq, int Hkv, int64_t n) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX) return 0;
-    return topk_layout(B, Hq, n).bytes;
+    return topk_layout(B, Hq, Hkv, n).bytes;
 }
 
 size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap) {
@@ -539,7 +539,7 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int 
     RETURN_IF(check_ptr(fn, "count", count, work));
     RETURN_IF(check_ptr(fn, "scores", scores, false));
     RETURN_IF(check_ptr(fn, "ws", ws, false));
-    const TopkLayout lay = topk_layout(B, Hq, n);
+    const TopkLayout lay = topk_layout(B, Hq, Hkv, n);
     if (!work) return LCDA_OK;
     if (!ws || ws_bytes < lay.bytes)
         return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
@@ -559,11 +559,8 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int 
     a.count = count;
     a.scores = scores;
     a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.hist_off);
-    a.chunk_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.chunk_off);
-    a.head_info = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lay.head_off);
-    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
     a.chunks = lay.chunks;
-    a.chunk_len = topk_chunk_len(n);
+    a.chunk_len = topk_chunk_len(n, B * Hkv);
     return hip_status(fn, launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -69,7 +69,8 @@ struct Tuning {
     int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads,
                                    // 2 = two blocks ahead, 3 = nontemporal with two waves per SIMD
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads
-    int64_t topk_subs = 4;         // TOPK: at least this many 4096-position sub-chunks per chunk
+    int64_t topk_subs = 0;         // TOPK: 4096-position sub-chunks per chunk (0: from topk_wgs)
+    int64_t topk_wgs = 512;        // TOPK: workgroups a call aims at when topk_subs is 0
 };
 Tuning& tuning();
 
@@ -123,14 +124,13 @@ struct TopkArgs {
     int32_t* idx;               // [B, Hq, cap]
     int32_t* count;             // [B, Hq]
     int8_t* scores;             // [B, Hq, n] or null
-    uint32_t* hist;             // ws: [B, Hq, chunks, topk_hist_row()] distance histograms
-    int32_t* chunk_info;        // ws: [B, Hkv, chunks, G, 4] (output offset, ties taken, ties, t)
-    int32_t* head_info;         // ws: [B, Hq, 2] (t, quota)
-    unsigned long long* ctr;    // ws: [B, Hkv] arrival counters of the histogram pass
+    uint32_t* hist;             // ws: [B, Hq, chunks + 2, topk_hist_row()] distance histograms of each
+                                // chunk, then of the sink part and the recent part of the chunks a
+                                // window edge cuts
     int chunks;                 // ceil(n / chunk_len) <= 64
     int64_t chunk_len;
 };
-int topk_chunk_len(int64_t n);
+int topk_chunk_len(int64_t n, int units);   // units: B * Hkv
 int topk_hist_row();
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 

@@ -18,23 +18,24 @@
 // per-position work is kept to a few vector instructions.
 //   1. k_topk_hist    - per chunk: the 33-bin distance histogram of each query
 //                       head, in 64 per-lane LDS copies laid out so that the
-//                       increments of one instruction hit distinct banks.  The
-//                       last workgroup of a KV head to finish (arrival counter)
-//                       then runs the selection of its G query heads:
-//      select         - per query head (one wavefront, lane = chunk): t and the
-//                       quota from the summed histograms, each chunk's ties
-//                       taken, the window positions outside the top m in the
-//                       chunks a window edge cuts (only the window part of those
-//                       chunks is scanned), per-chunk output offsets, the count,
+//                       increments of one instruction hit distinct banks.  A
+//                       chunk that a window edge cuts also histograms its
+//                       window part.
+//   2. k_topk_compact - per chunk, first the selection: per query head (one
+//                       wavefront, lane = chunk), t and the quota from the
+//                       summed histograms, each chunk's ties taken, the window
+//                       positions outside the top m (from the window parts'
+//                       histograms) and the chunks' output offsets; every
+//                       workgroup of a head computes them while its codes are
+//                       on their way, and the one of chunk 0 writes the count,
 //                       the window entries of the output (its lowest and highest
-//                       entries) and the -1 padding.
-//   2. k_topk_compact - per chunk: each thread holds 16 consecutive positions
-//                       and forms per-head 16-bit selection masks (below one
-//                       threshold, plus the ties for the one chunk that takes
-//                       only some of them, plus the window positions); DPP
-//                       scans in each wavefront and one exchange of wavefront
-//                       totals place them, and each thread stores its selected
-//                       positions outside the windows.
+//                       entries) and the -1 padding.  Then each thread holds 16
+//                       consecutive positions and forms per-head 16-bit
+//                       selection masks (below one threshold, plus the ties for
+//                       the one chunk that takes only some of them, plus the
+//                       window positions); DPP scans in each wavefront and one
+//                       exchange of wavefront totals place them, and each thread
+//                       stores its selected positions outside the windows.
 // A chunk is a whole number of 4096-position sub-chunks, chosen so that a head
 // has at most 64 chunks.  Positions are below n <= INT32_MAX; loop bounds that
 // can step past n are 64-bit.
@@ -49,11 +50,7 @@ constexpr int kSub = 4096;            // positions per sub-chunk (256 threads x 
 constexpr int kMaxChunks = 64;        // chunks per head: one lane each in the select wavefront
 constexpr int kBins = 33;
 constexpr int kRow = 36;              // words per histogram row: 33 bins, padded to 9 x 16 bytes
-constexpr int kPre = 8;               // window-part steps of 64 positions prefetched in the select
-
-__device__ __forceinline__ int mbcnt64(uint64_t m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
+constexpr int kTr = 68;               // words per bin in the selection's transposition: 64 chunks + 4
 
 // ---- loads ------------------------------------------------------------------
 // Thread tid's 16 codes of the sub-chunk at sb: positions sb + 4*(tid + 256*u) + e.
@@ -74,191 +71,17 @@ __device__ __forceinline__ void load_sub(uint32_t (&x)[16], const uint32_t* ks, 
     }
 }
 
-// ---- selection (one wavefront per query head, lane = chunk) -------------------
-// A window part [p0, p1) of a cut chunk, walked in steps of 64 positions (lane l
-// of step s holds p0 + 64*s + l); the first kPre steps are requested up front.
-struct Part {
-    int64_t p0, p1;
-    uint32_t x[kPre];
-};
-
-__device__ __forceinline__ void load_part(Part& pt, const uint32_t* ks, int lane) {
-    const int64_t last = pt.p1 > pt.p0 ? pt.p1 - 1 : 0;
-#pragma unroll
-    for (int s = 0; s < kPre; ++s) pt.x[s] = ks[min(pt.p0 + 64 * s + lane, last)];
-}
-
-// f(i, code) for every lane's position of every step, in step order (all lanes
-// call it; positions at or past p1 get some in-range code).
-template <class F>
-__device__ __forceinline__ void part_walk(const Part& pt, const uint32_t* ks, int lane, F&& f) {
-#pragma unroll
-    for (int s = 0; s < kPre; ++s)
-        if (pt.p0 + 64 * s < pt.p1) f(pt.p0 + 64 * s + lane, pt.x[s]);
-    for (int64_t p = pt.p0 + 64 * kPre; p < pt.p1; p += 64) f(p + lane, ks[min(p + lane, pt.p1 - 1)]);
-}
-
-// Ties (d == t) in a part.
-__device__ __forceinline__ int part_ties(const Part& pt, const uint32_t* ks, uint32_t q, int t, int lane) {
-    int ties = 0;
-    part_walk(pt, ks, lane, [&](int64_t i, uint32_t x) {
-        ties += __popcll(__ballot(i < pt.p1 && (int)__builtin_popcount(x ^ q) == t));
-    });
-    return ties;
-}
-
-// Positions of a part in the top m, given that tie_base ties of the chunk come
-// before the part and the chunk takes its first `taken` ties.
-__device__ __forceinline__ int part_top(const Part& pt, const uint32_t* ks, uint32_t q, int t, int tie_base, int taken,
-                                        int lane) {
-    int top = 0, carry = tie_base;
-    part_walk(pt, ks, lane, [&](int64_t i, uint32_t x) {
-        const int d = (int)__builtin_popcount(x ^ q);
-        const bool ok = i < pt.p1;
-        const uint64_t tm = __ballot(ok && d == t);
-        const int rank = carry + mbcnt64(tm);
-        top += __popcll(__ballot(ok && (d < t || (d == t && rank < taken))));
-        carry += __popcll(tm);
-    });
-    return top;
-}
-
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
-__device__ __forceinline__ int wave_excl_scan_i(int x, int lane) {
-    int inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += y;
-    }
-    return inc - x;
-}
-
-__device__ void select_head(const TopkArgs& a, int b, int h, int g, int lane, uint32_t* tr /*[kBins][65]*/) {
-    const int64_t row = (int64_t)b * a.Hq + h * a.G + g;
-    const int64_t n = a.n;
-    const int C = a.chunks;
-    const int64_t len = a.chunk_len;
-    const uint32_t q = a.q_sigs[row];
-    const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * n;
-    const int64_t s_end = min(a.n_sink, n);
-    const int64_t r_beg = max(max((int64_t)0, n - a.n_recent), s_end);
-
-    // Chunks cut by a window edge and the window part of each: the prefix
-    // [cs*len, s_end) of the sink-cut chunk and the suffix [r_beg, end of cr) of
-    // the recent-cut chunk.  Their codes do not depend on t: request them first.
-    const int cs = (s_end > 0 && s_end < n && s_end % len != 0) ? (int)(s_end / len) : -1;
-    const int cr = (r_beg < n && r_beg % len != 0) ? (int)(r_beg / len) : -1;
-    Part ps, pr;
-    ps.p0 = cs >= 0 ? cs * len : 0;
-    ps.p1 = cs >= 0 ? s_end : 0;
-    pr.p0 = cr >= 0 ? r_beg : 0;
-    pr.p1 = cr >= 0 ? min(n, (cr + 1) * len) : 0;
-    load_part(ps, ks, lane);
-    load_part(pr, ks, lane);
-
-    // This lane's chunk histogram.
-    // (The other workgroups of the head wrote them: device-scope loads.)
-    uint32_t hv[kBins];
-    {
-        const uint32_t* hrow = a.hist + (row * C + min(lane, C - 1)) * kRow;
-#pragma unroll
-        for (int k = 0; k < kRow / 2; ++k) {
-            const uint64_t v = load_dev_u64(hrow + 2 * k);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                if (2 * k + e < kBins) hv[2 * k + e] = lane < C ? (uint32_t)(v >> (32 * e)) : 0u;
-        }
-    }
-    // The head's histogram: bins transposed through LDS, lane d (< 33) sums bin d.
-#pragma unroll
-    for (int d = 0; d < kBins; ++d) tr[d * 65 + lane] = hv[d];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    int64_t hsum = 0;
-    if (lane < kBins) {
-#pragma unroll 8
-        for (int l = 0; l < 64; ++l) hsum += tr[lane * 65 + l];
-    }
-    // t = the first bin whose inclusive prefix reaches m; quota = what it must give (t = -1: m = 0).
-    const int64_t meff = min(a.m, n);
-    int64_t incl = hsum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
-    const uint64_t reach = __ballot(lane < kBins && meff > 0 && incl >= meff);
-    const int t = reach ? (int)__builtin_ctzll(reach) : -1;
-    const int64_t quota = t >= 0 ? meff - (__shfl(incl, t, 64) - __shfl(hsum, t, 64)) : 0;
-    int below = 0, ties = 0;
-#pragma unroll
-    for (int d = 0; d < kBins; ++d) {
-        below += d < t ? (int)hv[d] : 0;
-        ties = d == t ? (int)hv[d] : ties;
-    }
-    const int ties_before = wave_excl_scan_i(ties, lane);
-    const int taken = t < 0 ? 0 : (int)min(max(quota - ties_before, (int64_t)0), (int64_t)ties);
-
-    // Window positions outside the top m in the cut chunks.
-    int extra_s = 0, extra_r = 0;
-    if (cs >= 0) {
-        const int tk = __shfl(taken, cs, 64);
-        extra_s = (int)(ps.p1 - ps.p0) - part_top(ps, ks, q, t, 0, tk, lane);
-    }
-    if (cr >= 0) {
-        const int tk = __shfl(taken, cr, 64);
-        const int tie_c = __shfl(ties, cr, 64);
-        const int tsuf = part_ties(pr, ks, q, t, lane);
-        extra_r = (int)(pr.p1 - pr.p0) - part_top(pr, ks, q, t, tie_c - tsuf, tk, lane);
-    }
-
-    const int64_t cb = lane * len, ce = min(n, cb + len);
-    int cnt = 0;
-    if (lane < C) {
-        if (ce <= s_end || cb >= r_beg) cnt = (int)(ce - cb);   // entirely inside a window
-        else cnt = below + taken + (lane == cs ? extra_s : 0) + (lane == cr ? extra_r : 0);
-    }
-    const int off = wave_excl_scan_i(cnt, lane);
-    const int total = wave_sum_i(cnt);
-    if (lane < C) {
-        // Records of one chunk for all G heads of the group sit together.
-        int32_t* ci = a.chunk_info + ((((int64_t)b * a.Hkv + h) * C + lane) * a.G + g) * 4;
-        ci[0] = off;
-        ci[1] = taken;
-        ci[2] = ties;
-        ci[3] = t;
-    }
-    if (lane == 0) {
-        a.count[row] = total;
-        a.head_info[2 * row] = t;
-        a.head_info[2 * row + 1] = (int32_t)quota;
-    }
-    // The window positions are the lowest and the highest entries of I: the
-    // sink part is I[0 .. s_end) = 0 .. s_end - 1 and the recent part fills
-    // the last n - r_beg entries.  They are written here; the compaction
-    // counts them but stores only the positions of the top m.
-    int32_t* out = a.idx + row * a.cap;
-    for (int64_t i = lane; i < s_end; i += 64) out[i] = (int32_t)i;
-    const int64_t nr = n - r_beg;
-    for (int64_t i = lane; i < nr; i += 64) out[total - nr + i] = (int32_t)(r_beg + i);
-    for (int64_t i = total + lane; i < a.cap; i += 64) out[i] = -1;
-}
-
 // ---- 1. histogram ------------------------------------------------------------------
 // LDS cnt[g][bin][lane]: one copy per lane of the wavefront (the four
 // wavefronts share them through atomic adds), with a spare bin 33 for
 // positions past the end.  An increment's address is bin * 64 + lane, so the
 // 64 lanes of one instruction fall into distinct banks whatever their bins.
 template <int MAXG>
-struct HistSmem {
+struct __align__(16) HistSmem {
     static constexpr int kWords = MAXG * (kBins + 1) * 64;
+    static constexpr int kPartWords = 2 * MAXG * kBins;
     uint32_t cnt[kWords];
+    uint32_t part[kPartWords];   // [sink part, recent part][head][bin], shared by all lanes
 };
 
 // The increments of one chunk.  All MAXG heads are counted; heads at or past
@@ -278,10 +101,14 @@ __device__ __forceinline__ void load_group(uint32_t (&xr)[kGrp][16], const uint3
         if (gb + (int64_t)u * kSub < end) load_sub<VEC>(xr[u], ks, gb + (int64_t)u * kSub, end, tid);
 }
 
+// The window parts of a chunk that a window edge cuts are counted as well,
+// into counters that all lanes share: positions below s_cut (the sink part;
+// s_cut = beg when the chunk is not cut there) and from r_cut (the recent part;
+// r_cut = end when not cut).  Only the sub-chunks that meet a part do this.
 template <int MAXG, bool VEC, bool FULL, bool SCORES>
-__device__ __forceinline__ void hist_chunk(const TopkArgs& a, uint32_t* my, const uint32_t* ks,
+__device__ __forceinline__ void hist_chunk(const TopkArgs& a, uint32_t* my, uint32_t* part, const uint32_t* ks,
                                            const uint32_t (&qs)[MAXG], uint32_t (&xr)[kGrp][16], int64_t beg,
-                                           int64_t end, int tid, int64_t row0) {
+                                           int64_t end, int64_t s_cut, int64_t r_cut, int tid, int64_t row0) {
     for (int64_t gb = beg; gb < end; gb += (int64_t)kGrp * kSub) {
 #pragma unroll
         for (int u = 0; u < kGrp; ++u) {
@@ -293,6 +120,26 @@ __device__ __forceinline__ void hist_chunk(const TopkArgs& a, uint32_t* my, cons
                 const int64_t nb = sb + (int64_t)kGrp * kSub;
                 if (nb < end) load_sub<VEC>(xr[u], ks, nb, end, tid);
                 const int rem = FULL ? kSub : (int)min(end - sb, (int64_t)kSub);
+                if (sb < s_cut || min(sb + (int64_t)kSub, end) > r_cut) {   // uniform
+                    // Offsets from sb: the sink part is below s_rel, the recent part in [r_rel, rem).
+                    const int s_rel = (int)max(min(s_cut - sb, (int64_t)kSub), (int64_t)0);
+                    const int r_rel = (int)max(min(r_cut - sb, (int64_t)kSub), (int64_t)0);
+#pragma unroll
+                    for (int uu = 0; uu < 4; ++uu) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int k = 4 * (tid + 256 * uu) + e;
+                            const int pt = k < s_rel ? 0 : (k >= r_rel && k < rem ? 1 : -1);
+                            if (pt >= 0) {
+#pragma unroll
+                                for (int g = 0; g < MAXG; ++g)
+                                    __hip_atomic_fetch_add(part + (pt * MAXG + g) * kBins +
+                                                               __builtin_popcount(x[4 * uu + e] ^ qs[g]),
+                                                           1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                            }
+                        }
+                    }
+                }
 #pragma unroll
                 for (int uu = 0; uu < 4; ++uu) {
 #pragma unroll
@@ -316,6 +163,30 @@ __device__ __forceinline__ void hist_chunk(const TopkArgs& a, uint32_t* my, cons
     }
 }
 
+template <int MAXG>
+__device__ __forceinline__ void zero_counters(HistSmem<MAXG>& sm, int tid) {
+    static_assert(HistSmem<MAXG>::kWords % 4 == 0, "zeroed in 16-byte stores");
+    for (int k = 4 * tid; k < HistSmem<MAXG>::kWords; k += 4 * 256)
+        *reinterpret_cast<u32x4*>(sm.cnt + k) = u32x4{0u, 0u, 0u, 0u};
+    for (int k = tid; k < HistSmem<MAXG>::kPartWords; k += 256) sm.part[k] = 0u;
+}
+
+// Sum the 64 copies of each (head, bin) into histogram row `slot` of each of
+// the G heads; each thread starts at its own lane copy so that the reads of
+// one instruction fall into distinct banks.
+template <int MAXG>
+__device__ __forceinline__ void store_rows(const HistSmem<MAXG>& sm, const TopkArgs& a, int64_t row0, int slot,
+                                           int tid) {
+    for (int k = tid; k < a.G * kBins; k += 256) {
+        const int g = k / kBins, bin = k % kBins;
+        const uint32_t* r = sm.cnt + (g * (kBins + 1) + bin) * 64;
+        uint32_t sum = 0;
+#pragma unroll 8
+        for (int l = 0; l < 64; ++l) sum += r[(l + tid) & 63];
+        a.hist[((row0 + g) * (a.chunks + 2) + slot) * kRow + bin] = sum;
+    }
+}
+
 template <int MAXG, bool VEC, bool SCORES>
 __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
     __shared__ HistSmem<MAXG> sm;
@@ -329,36 +200,30 @@ __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
 
     uint32_t xr[kGrp][16];
     load_group<VEC>(xr, ks, beg, end, tid);
-    static_assert(HistSmem<MAXG>::kWords % 4 == 0, "zeroed in 16-byte stores");
-    for (int k = 4 * tid; k < HistSmem<MAXG>::kWords; k += 4 * 256)
-        *reinterpret_cast<u32x4*>(sm.cnt + k) = u32x4{0u, 0u, 0u, 0u};
+    zero_counters(sm, tid);
     uint32_t qs[MAXG];
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) qs[g] = a.q_sigs[row0 + min(g, G - 1)];
     __syncthreads();
 
+    // A chunk that a window edge cuts also counts its window part (the prefix
+    // below s_end, the suffix from r_beg) into rows chunks and chunks + 1.
+    const int64_t s_end = min(a.n_sink, a.n);
+    const int64_t r_beg = max(max((int64_t)0, a.n - a.n_recent), s_end);
+    const int64_t s_cut = (beg < s_end && s_end < end) ? s_end : beg;
+    const int64_t r_cut = (beg < r_beg && r_beg < end) ? r_beg : end;
     uint32_t* my = sm.cnt + lane;
-    if (end - beg == a.chunk_len) hist_chunk<MAXG, VEC, true, SCORES>(a, my, ks, qs, xr, beg, end, tid, row0);
-    else hist_chunk<MAXG, VEC, false, SCORES>(a, my, ks, qs, xr, beg, end, tid, row0);
+    if (end - beg == a.chunk_len)
+        hist_chunk<MAXG, VEC, true, SCORES>(a, my, sm.part, ks, qs, xr, beg, end, s_cut, r_cut, tid, row0);
+    else
+        hist_chunk<MAXG, VEC, false, SCORES>(a, my, sm.part, ks, qs, xr, beg, end, s_cut, r_cut, tid, row0);
     __syncthreads();
-    // Sum the 64 copies of each (head, bin); each thread starts at its own
-    // lane copy so that the reads of one instruction fall into distinct banks.
-    for (int k = tid; k < G * kBins; k += 256) {
-        const int g = k / kBins, bin = k % kBins;
-        const uint32_t* row = sm.cnt + (g * (kBins + 1) + bin) * 64;
-        uint32_t sum = 0;
-#pragma unroll 8
-        for (int l = 0; l < 64; ++l) sum += row[(l + tid) & 63];
-        store_dev(a.hist + (((int64_t)b * a.Hq + h * G + g) * a.chunks + c) * kRow + bin, sum);
-    }
+    store_rows(sm, a, row0, c, tid);
 
-    // The head's last workgroup to finish selects for its G query heads (one
-    // wavefront each), reusing the counters' LDS.
-    __shared__ int s_last;
-    if (arrive_count(a.ctr + (int64_t)b * a.Hkv + h, (uint32_t)a.chunks, &s_last)) {
-        uint32_t* tr = sm.cnt + (tid >> 6) * (kBins * 65);
-        static_assert(4 * kBins * 65 <= HistSmem<MAXG>::kWords, "select scratch fits the counters' LDS");
-        for (int g = tid >> 6; g < G; g += 4) select_head(a, b, h, g, lane, tr);
+    for (int k = tid; k < 2 * a.G * kBins; k += 256) {
+        const int pt = k / (a.G * kBins), g = (k / kBins) % a.G, bin = k % kBins;
+        if (pt == 0 ? s_cut > beg : r_cut < end)
+            a.hist[((row0 + g) * (a.chunks + 2) + a.chunks + pt) * kRow + bin] = sm.part[(pt * MAXG + g) * kBins + bin];
     }
 }
 
@@ -456,10 +321,147 @@ __device__ __forceinline__ void load_run_group(uint32_t (&xr)[kGrp][16], const u
         if (gb + (int64_t)u * kSub < end) load_run<VEC>(xr[u], ks, gb + (int64_t)u * kSub, end, tid);
 }
 
+// ---- 2. selection (in every compaction workgroup) -----------------------------------
+// One wavefront per query head, lane = chunk, from the histograms of all the
+// head's chunks: t and the quota, the ties each chunk takes (the ties of the
+// chunks before it come first), the window positions outside the top m in the
+// chunks a window edge cuts (from the histograms of their window parts), and
+// each chunk's output offset.  Every compaction workgroup of a head computes
+// the same values and keeps its own chunk's; the workgroup of chunk 0 also
+// writes the count, the window entries of the output (its lowest and highest
+// entries) and the -1 padding.
+struct ChunkRec {
+    int off, taken, ties, t;
+};
+
+__device__ __forceinline__ uint32_t lane_of(uint32_t x, int l) {   // l uniform
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+
+// The histograms one selection reads: this lane's chunk histogram, and bin
+// `lane` of the two window parts (zero where no chunk is cut).
+struct SelIn {
+    uint32_t hv[kRow];
+    uint32_t ps, pr;
+};
+
+__device__ __forceinline__ void window_cuts(const TopkArgs& a, int64_t& s_end, int64_t& r_beg, int& cs, int& cr) {
+    s_end = min(a.n_sink, a.n);
+    r_beg = max(max((int64_t)0, a.n - a.n_recent), s_end);
+    cs = (s_end > 0 && s_end < a.n && s_end % a.chunk_len != 0) ? (int)(s_end / a.chunk_len) : -1;   // sink-cut chunk
+    cr = (r_beg < a.n && r_beg % a.chunk_len != 0) ? (int)(r_beg / a.chunk_len) : -1;               // recent-cut chunk
+}
+
+__device__ __forceinline__ void select_load(const TopkArgs& a, int64_t row, int lane, SelIn& in) {
+    int64_t s_end, r_beg;
+    int cs, cr;
+    window_cuts(a, s_end, r_beg, cs, cr);
+    const int C = a.chunks;
+    const uint32_t* hrow = a.hist + row * (C + 2) * kRow;
+#pragma unroll
+    for (int k = 0; k < kRow / 4; ++k) {
+        const u32x4 v = lane < C ? *reinterpret_cast<const u32x4*>(hrow + lane * kRow + 4 * k) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) in.hv[4 * k + e] = v[e];
+    }
+    in.ps = (cs >= 0 && lane < kBins) ? hrow[C * kRow + lane] : 0u;
+    in.pr = (cr >= 0 && lane < kBins) ? hrow[(C + 1) * kRow + lane] : 0u;
+}
+
+__device__ ChunkRec select_chunk(const TopkArgs& a, int64_t row, int c, int lane, const SelIn& in,
+                                 uint32_t* tr /*[kBins][kTr]*/) {
+    const int64_t n = a.n;
+    const int C = a.chunks;
+    const int64_t len = a.chunk_len;
+    int64_t s_end, r_beg;
+    int cs, cr;
+    window_cuts(a, s_end, r_beg, cs, cr);
+    const uint32_t* hv = in.hv;
+    const uint32_t ps = in.ps, pr = in.pr;
+
+    // The head's histogram: bins transposed through LDS, lane d (< 33) sums bin d.
+#pragma unroll
+    for (int d = 0; d < kBins; ++d) tr[d * kTr + lane] = hv[d];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint32_t hsum = 0;
+    if (lane < kBins) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(tr + lane * kTr + 4 * k);
+            hsum += (v[0] + v[1]) + (v[2] + v[3]);
+        }
+    }
+    // t = the first bin whose inclusive prefix reaches m; quota = what it must
+    // give (t = -1: m = 0).  Counts stay below n <= INT32_MAX.
+    const uint32_t meff = (uint32_t)min(a.m, n);
+    const uint32_t incl = wave_incl_scan(hsum);
+    const uint64_t reach = __ballot(lane < kBins && meff > 0 && incl >= meff);
+    const int t = reach ? (int)__builtin_ctzll(reach) : -1;
+    const int tl = t >= 0 ? t : 0;
+    const int quota = t >= 0 ? (int)(meff - (lane_of(incl, tl) - lane_of(hsum, tl))) : 0;
+    uint32_t below = 0, ties = 0;
+#pragma unroll
+    for (int d = 0; d < kBins; ++d) {
+        below += d < t ? hv[d] : 0u;
+        ties = d == t ? hv[d] : ties;
+    }
+    const int ties_before = (int)(wave_incl_scan(ties) - ties);
+    const int taken = t < 0 ? 0 : min(max(quota - ties_before, 0), (int)ties);
+
+    // Window positions outside the top m in the cut chunks.  The ties a chunk
+    // takes are its first ones: the sink part (a prefix) takes the first of
+    // them, the recent part (a suffix) what is left after the ties before it.
+    int extra_s = 0, extra_r = 0;
+    if (cs >= 0) {
+        int top = 0;
+        if (t >= 0)
+            top = (int)(lane_of(wave_incl_scan(lane < t ? ps : 0u), 63)) +
+                  min((int)lane_of(ps, tl), (int)lane_of((uint32_t)taken, cs));
+        extra_s = (int)(s_end - (int64_t)cs * len) - top;
+    }
+    if (cr >= 0) {
+        int top = 0;
+        if (t >= 0) {
+            const int tp = (int)lane_of(pr, tl);
+            const int before = (int)lane_of(ties, cr) - tp;
+            top = (int)(lane_of(wave_incl_scan(lane < t ? pr : 0u), 63)) +
+                  min(max((int)lane_of((uint32_t)taken, cr) - before, 0), tp);
+        }
+        extra_r = (int)(min(n, (int64_t)(cr + 1) * len) - r_beg) - top;
+    }
+
+    const int64_t cb = (int64_t)lane * len, ce = min(n, cb + len);
+    uint32_t cnt = 0;
+    if (lane < C) {
+        if (ce <= s_end || cb >= r_beg) cnt = (uint32_t)(ce - cb);   // entirely inside a window
+        else cnt = below + (uint32_t)taken + (uint32_t)(lane == cs ? extra_s : 0) + (uint32_t)(lane == cr ? extra_r : 0);
+    }
+    const uint32_t cincl = wave_incl_scan(cnt);
+    const int total = (int)lane_of(cincl, 63);
+
+    if (c == 0) {   // uniform
+        if (lane == 0) a.count[row] = total;
+        // The window positions are the lowest and the highest entries of I:
+        // the sink part is I[0 .. s_end) = 0 .. s_end - 1 and the recent part
+        // fills the last n - r_beg entries.  The compaction stores only the
+        // positions of the top m.
+        int32_t* out = a.idx + row * a.cap;
+        for (int64_t i = lane; i < s_end; i += 64) out[i] = (int32_t)i;
+        const int64_t nr = n - r_beg;
+        for (int64_t i = lane; i < nr; i += 64) out[total - nr + i] = (int32_t)(r_beg + i);
+        for (int64_t i = total + lane; i < a.cap; i += 64) out[i] = -1;
+    }
+    return ChunkRec{(int)(lane_of(cincl, c) - lane_of(cnt, c)), (int)lane_of((uint32_t)taken, c),
+                    (int)lane_of(ties, c), t};
+}
+
 template <int MAXG, bool VEC>
 __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
     constexpr int kW = MAXG / 2;                 // words of packed 16-bit counts
     __shared__ uint32_t sh[2][2][kGrp][4][kW];   // [parity][selection, ties][sub][wavefront][word]
+    __shared__ __align__(16) uint32_t s_tr[4][kBins * kTr];   // the selection's transposition, one per wavefront
+    __shared__ int s_rec[MAXG][4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int G = a.G;
@@ -471,19 +473,32 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
     const bool meets_win = beg < s_end || end > r_beg;   // uniform
     const int64_t row0 = (int64_t)b * a.Hq + h * G;
 
+    // The chunk's records of all heads, {off, taken, ties, t} each, while the
+    // codes are on their way.  Per head: the selection below threshold thr (t,
+    // or t + 1 for a chunk that takes all its ties); a chunk that takes only
+    // some of its ties (mode 2) also forms the tie mask.  Heads at or past G
+    // select nothing.
+    SelIn sin;
+    if (w < G) select_load(a, row0 + w, lane, sin);   // the histograms are requested before the codes
     uint32_t xr[kGrp][16];
     load_run_group<VEC>(xr, ks, beg, end, tid);
-    // The chunk's records of all heads, {off, taken, ties, t} each, in one block.
-    // Per head: the selection below threshold thr (t, or t + 1 for a chunk that
-    // takes all its ties); a chunk that takes only some of its ties (mode 2)
-    // also forms the tie mask.  Heads at or past G select nothing.
-    const int32_t* rec = a.chunk_info + (((int64_t)b * a.Hkv + h) * a.chunks + c) * G * 4;
+    for (int g = w; g < G; g += 4) {
+        if (g != w) select_load(a, row0 + g, lane, sin);
+        const ChunkRec r = select_chunk(a, row0 + g, c, lane, sin, s_tr[w]);
+        if (lane == 0) {
+            s_rec[g][0] = r.off;
+            s_rec[g][1] = r.taken;
+            s_rec[g][2] = r.ties;
+            s_rec[g][3] = r.t;
+        }
+    }
+    __syncthreads();
     uint32_t q[MAXG], nthr[MAXG], nt1[MAXG];
     int off[MAXG], taken[MAXG], mode[MAXG], tie_carry[MAXG];   // mode: 0 no ties, 1 all ties, 2 some ties
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
         const int gg = min(g, G - 1);
-        const int32_t* ci = rec + 4 * gg;
+        const int* ci = s_rec[gg];
         q[g] = a.q_sigs[row0 + gg];
         const int t = g < G ? ci[3] : -1;
         off[g] = ci[0];
@@ -663,10 +678,18 @@ __global__ __launch_bounds__(256) void k_topk_compact(TopkArgs a) {
 
 }  // namespace
 
-int topk_chunk_len(int64_t n) {
+// Chunks of whole sub-chunks, at most kMaxChunks per head.  By default about
+// topk_wgs workgroups per call: two per CU, so that both scans run in one
+// round (their register use allows two workgroups of 256 threads per CU).
+int topk_chunk_len(int64_t n, int units) {
     const int64_t per = (int64_t)kSub * kMaxChunks;
-    const int64_t subs = n > 0 ? (n + per - 1) / per : 1;
-    return (int)(max(subs, tuning().topk_subs) * kSub);
+    const int64_t min_subs = n > 0 ? (n + per - 1) / per : 1;
+    int64_t subs = tuning().topk_subs;
+    if (subs <= 0) {
+        const int64_t chunks = max((int64_t)1, tuning().topk_wgs / max(units, 1));
+        subs = max((int64_t)1, (n + (int64_t)kSub * chunks - 1) / ((int64_t)kSub * chunks));
+    }
+    return (int)(max(min_subs, subs) * kSub);
 }
 
 int topk_hist_row() { return kRow; }

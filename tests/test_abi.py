@@ -89,10 +89,11 @@ def test_merge_and_topk_and_gather_reject(lib):
 def test_workspace_sizes(lib):
     assert lib.lcda_ws_bytes_cached_attn_lse(1, 32, 8, 128, 61440, 8 * 61440 * 128) > 0
     assert lib.lcda_ws_bytes_cached_attn_lse(1, 32, 8, 64, 61440, 0) == 0
-    # One 33-bin histogram per query head and chunk; a chunk holds at least
-    # topk_subs sub-chunks of 4096 positions.
-    subs = lib.lcda_get_tuning(b"topk_subs")
-    chunks = -(-131072 // (4096 * subs))
+    # One 33-bin histogram per query head and chunk (and two for the window
+    # parts); by default about topk_wgs workgroups of whole 4096-position
+    # sub-chunks: 512 / (8 x 8) = 8 chunks here.
+    assert lib.lcda_get_tuning(b"topk_subs") == 0 and lib.lcda_get_tuning(b"topk_wgs") == 512
+    chunks = 8
     assert lib.lcda_ws_bytes_sig_score_topk(8, 32, 8, 131072) >= 8 * 32 * chunks * 33 * 4
     assert lib.lcda_ws_bytes_gather_attn(8, 32, 8, 128, 4352) > 0
     assert lib.lcda_ws_bytes_lse_merge_local(1, 32, 8, 128, 256) > 0

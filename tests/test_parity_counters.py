@@ -83,8 +83,8 @@ def test_garbage_workspace_gather_and_fp32(orc, fill):
 
 @pytest.mark.parametrize("fill", ["ones", "random"])
 def test_garbage_workspace_topk(orc, fill):
-    """TOPK: the last histogram workgroup of each KV head runs the selection, found through the same tagged
-    counters; indices stay bit-exact whatever the workspace held, over repeated calls of two shapes."""
+    """TOPK: histogram rows of earlier calls (and of window parts no chunk has) left in the workspace are
+    never read; indices stay bit-exact whatever the workspace held, over repeated calls of two shapes."""
     g = np.random.default_rng(76)
     cases = [(2, 8, 2, 40000, 1300, 64, 64), (3, 4, 1, 9001, 300, 16, 16)]
     nb = max(ops.ws_bytes_sig_score_topk(B, Hq, Hkv, n) for B, Hq, Hkv, n, _, _, _ in cases)
