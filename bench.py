@@ -8,6 +8,8 @@ A step is one decode step of the named workload through the HIP library:
               local tokens each: 36 x dense_decode_step (cached_attn_lse + lse_merge_local)
   sparse128k  HashAttention step: 8 KV heads, 32 query heads, n=131,072 bf16, batch 8,
               m = n/32 + 128 sink + 128 recent: sig_score_topk + gather_attn
+  quadrature  Nectar's quadrature module as cached_attn_lse: 256 queries against p = 6,144 shared
+              (W, Z) pairs per KV head (the 10 % module of a 61,440-token document); MFMA-bound
   needles512k n=524,288 bf16, batch 4, 64 planted needles per head: the sparse step (m=n/64)
               against cached_attn_lse on the same inputs, with needle recall, attention mass
               captured and the sparse output's error against the dense one
@@ -35,6 +37,7 @@ from long_context_decode_attn_amd import ops, synth, traffic  # noqa: E402
 from long_context_decode_attn_amd.profsum import kernel_source_digest  # noqa: E402
 
 HBM_PEAK = 8.0e12   # B/s, MI355X published peak
+MFMA_BF16_PEAK = 2.5e15   # FLOP/s, MI355X published dense bf16 matrix peak
 METRIC = "decode-attention queries/sec + achieved HBM TB/s (KV+sig bytes) vs ~8 TB/s peak"
 
 
@@ -371,6 +374,34 @@ def bench_needles(args, cfg):
     return res
 
 
+# ------------------------------------------------------------- quadrature ----
+class QuadSet:
+    """One input set of the quadrature workload: q [B, Hq, d] against one shared (W, Z) per KV head."""
+
+    def __init__(self, cfg, rot, device="cuda"):
+        self.x = synth.make_inputs(cfg, device=device, rot=rot)
+        B, Hq = self.x["q"].shape[:2]
+        Hkv, n = self.x["k"].shape[1], self.x["k"].shape[2]
+        self.o = torch.empty((B, Hq, 128), device=device)
+        self.al = torch.empty((B, Hq), device=device)
+        self.ws = torch.empty(ops.ws_bytes_cached_attn_lse(B, Hq, Hkv, 128, n, 0), dtype=torch.uint8, device=device)
+
+    def step(self):
+        ops.cached_attn_lse(self.x["q"], self.x["k"], self.x["v"], out=self.o, alpha=self.al, ws=self.ws)
+
+
+def bench_quadrature(args, cfg):
+    rot = args.rot or 2
+    sets = [QuadSet(cfg, r) for r in range(rot)]
+    torch.cuda.synchronize()
+    ms = run_steps([s.step for s in sets], args.steps, args.warmup, args.graph) / args.steps
+    flops = 4.0 * cfg.B * cfg.Hq * cfg.n * cfg.d          # q.w and p.z: two multiply-adds per (row, pair, dim)
+    bytes_ = 2 * cfg.Hkv * cfg.n * cfg.d * 2 + cfg.B * cfg.Hq * cfg.d * 2 + cfg.B * cfg.Hq * (cfg.d + 1) * 4
+    return {"value": cfg.B / (ms * 1e-3), "ms_per_step": ms, "steps": args.steps, "flops": flops,
+            "tflops": flops / (ms * 1e-3) / 1e12, "bytes": bytes_, "tbps": bytes_ / (ms * 1e-3) / 1e12,
+            "rotations": rot}
+
+
 # -------------------------------------------------------------- CPU oracle ----
 def cpu_baseline_dense(cfg, seconds: float):
     """The oracle (plain C, fp64) on the host's cores over whole decode steps of the same workload."""
@@ -396,6 +427,28 @@ def cpu_baseline_dense(cfg, seconds: float):
     return {"value": cfg.B * steps / el, "unit": "queries/s", "cores": orc.get_threads(), "kind": "oracle",
             "sample": "%d full decode step(s) of the same workload (cached_attn_lse + lse_merge_local "
                       "definitions, fp64), %.1f s wall" % (steps, el)}
+
+
+def cpu_baseline_quadrature(cfg, seconds: float, B: int = 4):
+    """The oracle's dense attention for B of the queries against the whole shared module."""
+    from oracle import oracle as orc_mod
+    orc = orc_mod.default()
+    orc.set_threads(os.cpu_count() or 1)
+    x = synth.make_inputs(cfg, device="cpu")
+    q = x["q"][:B].contiguous().view(torch.int16).numpy().view(np.uint16)
+    k = x["k"].contiguous().view(torch.int16).numpy().view(np.uint16)
+    v = x["v"].contiguous().view(torch.int16).numpy().view(np.uint16)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.dense_attn(q, k, v)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": B * steps / el, "unit": "queries/s", "cores": orc.get_threads(), "kind": "oracle",
+            "sample": "%d x %d queries against the shared module (cached_attn_lse definition, fp64), %.1f s wall"
+                      % (steps, B, el)}
 
 
 def cpu_baseline_sparse(cfg, seconds: float, B: int = 1):
@@ -430,7 +483,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dense61k", choices=["dense61k", "shared36", "sparse128k", "needles512k"])
+    ap.add_argument("--workload", default="dense61k",
+                    choices=["dense61k", "shared36", "sparse128k", "needles512k", "quadrature"])
     ap.add_argument("--rot", type=int, default=0, help="input sets cycled (0: workload default)")
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
@@ -498,6 +552,18 @@ def main():
         line["detail"] = res
         if args.cpu_seconds > 0:
             line["cpu_baseline"] = cpu_baseline_sparse(cfg, args.cpu_seconds)
+    elif args.workload == "quadrature":
+        cfg = synth.QUADRATURE
+        res = bench_quadrature(args, cfg)
+        line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"]})
+        line["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_BF16_PEAK / 1e12,
+                            "unit": "TFLOP/s", "frac": res["tflops"] * 1e12 / MFMA_BF16_PEAK, "traffic": None,
+                            "kernel": "k_split_rows (64-row MFMA pass over the shared module) + k_combine"}
+        line["config"] = {"workload": "quadrature: " + cfg.name, "launch": launch}
+        line["step"] = "cached_attn_lse of 256 queries against p = 6,144 shared (W, Z) pairs per KV head"
+        line["detail"] = res
+        if args.cpu_seconds > 0:
+            line["cpu_baseline"] = cpu_baseline_quadrature(cfg, args.cpu_seconds)
     else:
         cfg = synth.CONFIGS[5]
         res = bench_needles(args, cfg)

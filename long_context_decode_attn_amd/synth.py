@@ -150,6 +150,19 @@ CONFIGS = {
               m=524288 // 64, n_sink=128, n_recent=128, needles=64),
 }
 
+# A workload the same kernels serve beyond the five above: the Nectar quadrature
+# module's evaluation, softmax(W q / sqrt d)^T Z with alpha = log sum exp(W q /
+# sqrt d) ("Nectar: Neural Estimation of Cached-Token Attention via Regression",
+# slide "The representation and the loss are separate choices", quadrature
+# block), which is cached_attn_lse with K = W and V = Z.  p = 6,144 pairs per (layer, KV head) is the 10 % module of
+# the 61,440-token document (Table 9's 914 MB over 36 layers x 8 KV heads x 512
+# B per pair); 256 decode queries share it, so each KV head has 1,024 query rows
+# and the contraction is dense.  W and Z are random (their quality needs trained
+# values).
+QUADRATURE = Config(6, "Nectar quadrature module: Hkv=8 Hq=32 d=128 p=6144 pairs (10% of 61,440) bf16, "
+                       "256 queries sharing it",
+                    B=256, Hq=32, Hkv=8, d=128, n=6144, dtype=torch.bfloat16, shared_doc=True)
+
 
 def make_inputs(cfg: Config, device="cpu", rot: int = 0, n: int | None = None, B: int | None = None,
                 layer: int = 0, with_sigs: bool | None = None, n_loc=None):
