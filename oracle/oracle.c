@@ -13,7 +13,9 @@
  *        (exact o and sparse o-hat, the SCORE/TOPK/GATHER-ATT stages);
  *        slide "A 32-bit signature makes scoring cheap", Eq. (2);
  *        slide "Token-level sparsity still needs a careful kernel" (sink and
- *        recent windows, budget accounting).
+ *        recent windows, budget accounting);
+ *        slide "Learning the codes matters more than merely hashing" (the
+ *        random-projection LSH selector, whose codes sig_encode computes).
  *
  * Readings taken where the slides leave a step open are stated at each use.
  * Every sum is accumulated in double.
@@ -331,4 +333,23 @@ int orc_gather_attn(const void* q, const void* k, const void* v, int dtype,
         free(s);
     }
     return bad ? 1 : 0;
+}
+
+/* ---- T_map: random-projection signatures ---------------------------------- */
+
+/* phi(x) = ReLU(sign(F(x))) with F(x) = R^T x, [HA] Eq. (1); component b is
+ * bit b of the code.  sign(0) = 0, so a zero projection gives bit 0. */
+int orc_sig_encode(const void* x, int dtype, int64_t rows, int d, const float* R, int bits, uint32_t* codes) {
+    if (rows < 0 || d <= 0 || bits <= 0 || bits > 32 || (rows > 0 && (!x || !R || !codes))) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        uint32_t c = 0;
+        for (int b = 0; b < bits; ++b) {
+            double z = 0.0;
+            for (int e = 0; e < d; ++e) z = fma(elem(x, dtype, i * d + e), (double)R[(int64_t)e * bits + b], z);
+            if (z > 0.0) c |= 1u << b;
+        }
+        codes[i] = c;
+    }
+    return 0;
 }

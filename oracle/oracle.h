@@ -55,6 +55,17 @@ int orc_gather_attn(const void* q, const void* k, const void* v, int dtype,
                     int64_t cap, int B, int Hq, int Hkv, int d, int64_t n,
                     double* out, double* alpha);
 
+/* T_map with a random projection (the LSH selector HashAttention compares
+ * against): code bit b of row i is phi(x_i)_b = ReLU(sign(z_b)), i.e. 1 when
+ * z_b = sum_e x[i][e] * R[e][b] > 0 and 0 otherwise ("A 32-bit signature makes
+ * scoring cheap", Eq. (1)).  x: [rows, d] in dtype, R: [d, bits] float32 with
+ * bits <= 32, codes: [rows].  z_b is accumulated as a chain of fused
+ * multiply-adds in double, e = 0 .. d-1 in order, from 0: every product of a
+ * bf16 or float32 value with a float32 value is exact in double, and the chain
+ * fixes the rounding of the sum, so the sign of a near-zero z_b is
+ * reproducible. */
+int orc_sig_encode(const void* x, int dtype, int64_t rows, int d, const float* R, int bits, uint32_t* codes);
+
 /* OpenMP thread count used by the calls above (<= 0: leave the default). */
 void orc_set_threads(int nthreads);
 int orc_get_threads(void);

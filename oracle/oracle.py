@@ -74,7 +74,8 @@ class Oracle:
         lib.orc_merge_local.argtypes = [P, i32, P, P, P, P, P, i64, i32, i32, i32, i32, P, P]
         lib.orc_sig_topk.argtypes = [P, P, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P]
         lib.orc_gather_attn.argtypes = [P, P, P, i32, i64, P, P, i64, i32, i32, i32, i32, i64, P, P]
-        for f in (lib.orc_dense_attn, lib.orc_merge_local, lib.orc_sig_topk, lib.orc_gather_attn):
+        lib.orc_sig_encode.argtypes = [P, i32, i64, i32, P, i32, P]
+        for f in (lib.orc_dense_attn, lib.orc_merge_local, lib.orc_sig_topk, lib.orc_gather_attn, lib.orc_sig_encode):
             f.restype = ctypes.c_int
         lib.orc_set_threads.argtypes = [i32]
         lib.orc_set_threads.restype = None
@@ -171,6 +172,22 @@ class Oracle:
             raise ValueError("orc_gather_attn: invalid arguments")
         return out, alpha
 
+    def sig_encode(self, x, R):
+        """Random-projection codes of the rows of x [..., d] (bf16 bit patterns or float32):
+        bit b = (x . R[:, b] > 0), as an fma chain in double.  R: [d, bits] float32, bits <= 32.
+        Returns uint32 [...]."""
+        x = _c(x)
+        R = _c(np.asarray(R, np.float32), np.float32)
+        d, bits = R.shape
+        assert x.shape[-1] == d
+        lead = x.shape[:-1]
+        rows = int(np.prod(lead)) if lead else 1
+        codes = np.empty(rows, np.uint32)
+        st = self.lib.orc_sig_encode(_ptr(x), _dtype_code(x), rows, d, _ptr(R), bits, _ptr(codes))
+        if st:
+            raise ValueError("orc_sig_encode: invalid arguments")
+        return codes.reshape(lead)
+
 
 _default = None
 
@@ -194,6 +211,10 @@ def merge_local(*a, **kw):
 
 def sig_score_topk(*a, **kw):
     return default().sig_score_topk(*a, **kw)
+
+
+def sig_encode(*a, **kw):
+    return default().sig_encode(*a, **kw)
 
 
 def gather_attn(*a, **kw):

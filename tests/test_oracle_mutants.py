@@ -30,6 +30,9 @@ MUTANTS = {
     "batch stride ignored": ("(int64_t)b * kv_batch_stride", "(int64_t)0 * kv_batch_stride"),
     "local value rows not used": ("o[c] += w * elem(v_loc, dtype, kv_off + i * d + c);",
                                   "o[c] += w * elem(v_loc, dtype, kv_off + c);"),
+    "signature of a zero projection set": ("if (z > 0.0) c |= 1u << b;", "if (z >= 0.0) c |= 1u << b;"),
+    "signature bits reversed": ("if (z > 0.0) c |= 1u << b;", "if (z > 0.0) c |= 1u << (bits - 1 - b);"),
+    "projection read transposed": ("(double)R[(int64_t)e * bits + b]", "(double)R[(int64_t)b * d + e]"),
 }
 
 

@@ -467,3 +467,69 @@ def test_kv_storage_bytes():
     b = traffic.doc_kv_state_bytes(g["n"], g["layers"], g["kv_heads"], g["d"], g["bytes_per_entry"])
     assert b == 9_142_272_000
     assert round(b / 1e9, 2) == g["gigabytes_about"]
+
+
+# ------------------------------------------------------- T_map (N2) --------
+# phi(x) = ReLU(sign(R^T x)) ("HashAttention: Semantic Sparsity for Faster
+# Inference", slide "A 32-bit signature makes scoring cheap", Eq. (1)) with a
+# random projection R, the LSH selector of slide "Learning the codes matters
+# more than merely hashing".  Component b is bit b of the code.
+
+def test_sig_encode_axis_projection(orc):
+    """R = the first 32 coordinate axes: bit b is x_b > 0 (zero gives 0)."""
+    g = rng(501)
+    x = g.standard_normal((40, 128)).astype(np.float32)
+    x[3, :32] = 0.0
+    x[4, 5] = -0.0
+    R = np.zeros((128, 32), np.float32)
+    R[np.arange(32), np.arange(32)] = 1.0
+    want = ((x[:, :32] > 0).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(1).astype(np.uint32)
+    np.testing.assert_array_equal(orc.sig_encode(x, R), want)
+    assert orc.sig_encode(x[3:4], R)[0] == 0
+
+
+def test_sig_encode_signed_permuted_axes_bf16(orc):
+    """R[pi(b), b] = s_b (one entry per column): bit b is s_b * x_pi(b) > 0; bf16 inputs read exactly."""
+    g = rng(502)
+    xb = bf16_bits(g.standard_normal((33, 128)).astype(np.float32))
+    xf = bits_to_f32(xb)
+    pi = g.permutation(128)[:32]
+    s = g.choice(np.array([-2.0, -0.5, 0.25, 3.0], np.float32), 32)
+    R = np.zeros((128, 32), np.float32)
+    R[pi, np.arange(32)] = s
+    want = ((s[None, :] * xf[:, pi] > 0).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(1).astype(np.uint32)
+    np.testing.assert_array_equal(orc.sig_encode(xb, R), want)
+
+
+def test_sig_encode_matches_matmul_signs_away_from_zero(orc):
+    """Against a library matmul in float64: every bit whose projection is not within 1e-9 of zero."""
+    g = rng(503)
+    x = g.standard_normal((300, 128)).astype(np.float32)
+    R = g.standard_normal((128, 32)).astype(np.float32)
+    z = x.astype(np.float64) @ R.astype(np.float64)
+    got = orc.sig_encode(x, R)
+    bits = ((got[:, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(bool)
+    far = np.abs(z) > 1e-9
+    assert far.mean() > 0.999
+    np.testing.assert_array_equal(bits[far], (z > 0)[far])
+
+
+def test_sig_encode_negation_and_scaling(orc):
+    """Negating x complements every bit whose projection is nonzero; scaling by 4 changes nothing."""
+    g = rng(504)
+    x = g.standard_normal((64, 128)).astype(np.float32)
+    R = g.standard_normal((128, 32)).astype(np.float32)
+    c = orc.sig_encode(x, R)
+    np.testing.assert_array_equal(orc.sig_encode(-x, R), ~c)
+    np.testing.assert_array_equal(orc.sig_encode(4.0 * x, R), c)
+
+
+def test_sig_encode_fewer_bits_and_empty(orc):
+    """A projection of b < 32 columns gives b-bit codes; zero rows give an empty result."""
+    g = rng(505)
+    x = g.standard_normal((10, 128)).astype(np.float32)
+    R = g.standard_normal((128, 32)).astype(np.float32)
+    c32 = orc.sig_encode(x, R)
+    c8 = orc.sig_encode(x, np.ascontiguousarray(R[:, :8]))
+    np.testing.assert_array_equal(c8, c32 & 0xFF)
+    assert orc.sig_encode(np.zeros((0, 128), np.float32), R).shape == (0,)
