@@ -251,6 +251,46 @@ class SparseSet:
         self.topk()
         self.gather()
 
+    # T_map (random projection): the query codes, and the codes of one new key per (b, KV head)
+    def tmap_setup(self):
+        c = self.cfg
+        self.R = synth.projection(128, 32, c.cid, device=self.x["q"].device).float()
+        self.qs_enc = torch.empty_like(self.x["q_sigs"])
+        B, Hkv, n = self.x["key_sigs"].shape
+        self.codes_tail = torch.empty((B, Hkv, n), dtype=torch.int32, device=self.x["q"].device)
+
+    def encode_q(self):
+        ops.sig_encode(self.x["q"], self.R, codes=self.qs_enc)
+
+    def append_key(self):
+        n = self.x["k"].shape[2]
+        ops.sig_encode(self.x["k"][:, :, n - 1:n], self.R, codes=self.codes_tail[:, :, n - 1:n])
+
+    def encode_cache(self):
+        ops.sig_encode(self.x["k"], self.R, codes=self.codes_tail)
+
+    def topk_q(self):
+        c = self.cfg
+        ops.sig_score_topk_q(self.x["key_sigs"], self.x["q"], self.R, c.m, c.n_sink, c.n_recent, cap=self.cap,
+                             idx=self.idx, count=self.cnt, q_sigs=self.qs_enc, ws=self.ws)
+
+
+def bench_tmap(args, sets, cfg):
+    """Timings of the T_map stage (N2) on the sparse workload's inputs."""
+    for s in sets:
+        s.tmap_setup()
+    torch.cuda.synchronize()
+    steps = max(10, args.steps // 2)
+    us = lambda fns, k=steps: run_steps(fns, k, max(2, args.warmup // 4), args.graph) / k * 1e3
+    rows = cfg.B * cfg.Hkv * cfg.n
+    t_cache = us([s.encode_cache for s in sets], 5)
+    return {"encode_queries_us": us([s.encode_q for s in sets]),
+            "append_one_key_per_head_us": us([s.append_key for s in sets]),
+            "sig_score_topk_q_us": us([s.topk_q for s in sets]),
+            "encode_whole_cache_us": t_cache,
+            "encode_whole_cache_rows_per_s": rows / (t_cache * 1e-6),
+            "encode_whole_cache_fp64_tflops": rows * 32 * 128 * 2 / (t_cache * 1e-6) / 1e12}
+
 
 def bench_sparse(args, cfg, rot=None):
     rot = rot or args.rot or 2
@@ -283,6 +323,7 @@ def bench_sparse(args, cfg, rot=None):
         "gather_bytes": gather_bytes,
         "rotations": rot,
     }
+    res["t_map"] = bench_tmap(args, sets, cfg)
     return res, sets[0]
 
 

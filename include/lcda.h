@@ -4,7 +4,9 @@
  * Two paths:
  *   dense:  cached_attn_lse   - A(q) and alpha(q) against all cached tokens
  *           lse_merge_local   - exact merge of (A, alpha) with local tokens
- *   sparse: sig_score_topk    - HashAttention SCORE + TOPK over 32-bit codes
+ *   sparse: sig_encode        - T_map: random-projection codes of queries or new keys
+ *           sig_score_topk    - HashAttention SCORE + TOPK over 32-bit codes
+ *           sig_score_topk_q  - the same with the query codes encoded at its head
  *           gather_attn       - attention renormalised over the selected rows
  *
  * Conventions shared by every call
@@ -119,6 +121,39 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs,
                    int B, int Hq, int Hkv, int64_t n, int64_t m, int64_t n_sink,
                    int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
                    int8_t* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* sig_score_topk with the query codes encoded at its head (the T_map stage of
+ * the query fused into the scan): q [B, Hq, 128] in q_dtype and R [128, bits]
+ * fp32 as in sig_encode; q_sigs [B, Hq] uint32 receives the codes, and the
+ * selection is the one sig_score_topk makes from them.  Everything else, the
+ * workspace included, as in sig_score_topk. */
+int sig_score_topk_q(const uint32_t* key_sigs, const void* q, int q_dtype, const float* R, int bits,
+                     int B, int Hq, int Hkv, int64_t n, int64_t m, int64_t n_sink, int64_t n_recent,
+                     int32_t* idx, int64_t cap, int32_t* count, int8_t* scores, uint32_t* q_sigs,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* T_map with a random projection: 32-bit codes of 128-value rows.
+ *
+ * Bit b of the code of row x is phi(x)_b = ReLU(sign(x . R[:, b])): 1 when
+ * the projection is > 0, else 0 ("HashAttention ...", slide "A 32-bit
+ * signature makes scoring cheap", Eq. (1), with F(x) = R^T x: the
+ * random-projection selector of slide "Learning the codes matters more than
+ * merely hashing"; the learned map needs trained weights).  Each projection is
+ * a chain of fp64 fused multiply-adds over the 128 values in order, from 0:
+ * codes are exact and reproducible, including the sign of a projection near
+ * zero.  One call encodes queries (groups = 1, rows_per_group = B*Hq) or
+ * appends new keys' codes (groups = B*Hkv, one group per cached head).
+ *
+ *   x      row (g, i), g < groups, i < rows_per_group, at
+ *          x + g*x_group_stride + i*128 elements, dtype (fp32 or bf16);
+ *          16-byte aligned, x_group_stride a multiple of 8
+ *   R      [128, bits] fp32, 1 <= bits <= 32 (code bits at or past bits are 0)
+ *   codes  row (g, i)'s code at codes[g*codes_group_stride + i] (uint32,
+ *          4-byte aligned: e.g. key_sigs + n_old with codes_group_stride = n)
+ * With groups > 1 the strides must not make rows overlap.  No workspace.
+ */
+int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group, int64_t x_group_stride,
+               const float* R, int bits, uint32_t* codes, int64_t codes_group_stride, void* stream);
 
 /* GATHER-ATT: attention over the selected rows only, renormalised over I:
  *   out = sum_{i in I} e^{s_i} v_i / sum_{j in I} e^{s_j},  alpha = log sum_{j in I} e^{s_j}

@@ -516,10 +516,11 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
     return finish(fn, p, a, dtype, B * Hq, out, alpha_out, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
-int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int Hq, int Hkv, int64_t n,
-                   int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
-                   int8_t* scores, void* ws, size_t ws_bytes, void* stream) {
-    static const char* fn = "sig_score_topk";
+// sig_score_topk and sig_score_topk_q.  enc: q, R and bits are given, and the
+// query codes are encoded into q_sigs by the histogram pass.
+static int topk_impl(const char* fn, const uint32_t* key_sigs, uint32_t* q_sigs, const void* q, int q_dtype, const float* R,
+              int bits, bool enc, int B, int Hq, int Hkv, int64_t n, int64_t m, int64_t n_sink, int64_t n_recent,
+              int32_t* idx, int64_t cap, int32_t* count, int8_t* scores, void* ws, size_t ws_bytes, void* stream) {
     if (B < 0) return fail(LCDA_EINVAL, "%s: B = %d < 0", fn, B);
     if (Hq <= 0 || Hkv <= 0) return fail(LCDA_EINVAL, "%s: Hq = %d, Hkv = %d must be positive", fn, Hq, Hkv);
     if (Hq % Hkv != 0) return fail(LCDA_EINVAL, "%s: Hq = %d is not a multiple of Hkv = %d", fn, Hq, Hkv);
@@ -535,6 +536,12 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int 
     const bool work = B > 0;
     RETURN_IF(check_ptr(fn, "key_sigs", key_sigs, work && n > 0));
     RETURN_IF(check_ptr(fn, "q_sigs", q_sigs, work));
+    if (enc) {
+        RETURN_IF(check_dtype(fn, q_dtype));
+        RETURN_IF(check_ptr(fn, "q", q, work));
+        RETURN_IF(check_ptr(fn, "R", R, work));
+        if (bits < 1 || bits > 32) return fail(LCDA_EINVAL, "%s: bits = %d outside 1 .. 32", fn, bits);
+    }
     RETURN_IF(check_ptr(fn, "idx", idx, work && cap > 0));
     RETURN_IF(check_ptr(fn, "count", count, work));
     RETURN_IF(check_ptr(fn, "scores", scores, false));
@@ -561,7 +568,76 @@ int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int 
     a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.hist_off);
     a.chunks = lay.chunks;
     a.chunk_len = topk_chunk_len(n, B * Hkv);
-    return hip_status(fn, launch_topk(a, static_cast<hipStream_t>(stream)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (enc && lay.chunks == 0) {   // no positions: the codes still come back, from the encoder
+        EncodeArgs e{};
+        e.x = q;
+        e.bf16 = q_dtype == LCDA_BF16;
+        e.groups = 1;
+        e.rows_per_group = (int64_t)B * Hq;
+        e.x_group_stride = 0;
+        e.R = R;
+        e.bits = bits;
+        e.codes = q_sigs;
+        e.codes_group_stride = 0;
+        RETURN_IF(hip_status(fn, launch_sig_encode(e, st)));
+    } else if (enc) {
+        a.q = q;
+        a.q_bf16 = q_dtype == LCDA_BF16;
+        a.R = R;
+        a.bits = bits;
+        a.q_codes = q_sigs;
+    }
+    return hip_status(fn, launch_topk(a, st));
+}
+
+int sig_score_topk(const uint32_t* key_sigs, const uint32_t* q_sigs, int B, int Hq, int Hkv, int64_t n,
+                   int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                   int8_t* scores, void* ws, size_t ws_bytes, void* stream) {
+    return topk_impl("sig_score_topk", key_sigs, const_cast<uint32_t*>(q_sigs), nullptr, 0, nullptr, 0, false, B, Hq,
+                     Hkv, n, m, n_sink, n_recent, idx, cap, count, scores, ws, ws_bytes, stream);
+}
+
+int sig_score_topk_q(const uint32_t* key_sigs, const void* q, int q_dtype, const float* R, int bits, int B, int Hq,
+                     int Hkv, int64_t n, int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap,
+                     int32_t* count, int8_t* scores, uint32_t* q_sigs, void* ws, size_t ws_bytes, void* stream) {
+    return topk_impl("sig_score_topk_q", key_sigs, q_sigs, q, q_dtype, R, bits, true, B, Hq, Hkv, n, m, n_sink,
+                     n_recent, idx, cap, count, scores, ws, ws_bytes, stream);
+}
+
+int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group, int64_t x_group_stride,
+               const float* R, int bits, uint32_t* codes, int64_t codes_group_stride, void* stream) {
+    static const char* fn = "sig_encode";
+    RETURN_IF(check_dtype(fn, dtype));
+    if (groups < 0 || rows_per_group < 0)
+        return fail(LCDA_EINVAL, "%s: groups = %lld, rows_per_group = %lld must be >= 0", fn, (long long)groups,
+                    (long long)rows_per_group);
+    if (bits < 1 || bits > 32) return fail(LCDA_EINVAL, "%s: bits = %d outside 1 .. 32", fn, bits);
+    const bool work = groups > 0 && rows_per_group > 0;
+    if (work && groups > 1 && (x_group_stride < rows_per_group * kD || codes_group_stride < rows_per_group))
+        return fail(LCDA_EINVAL, "%s: group strides overlap the rows (x %lld < %lld or codes %lld < %lld)", fn,
+                    (long long)x_group_stride, (long long)(rows_per_group * kD), (long long)codes_group_stride,
+                    (long long)rows_per_group);
+    if (x_group_stride < 0 || x_group_stride % 8 != 0 || codes_group_stride < 0)
+        return fail(LCDA_EINVAL, "%s: x_group_stride must be a non-negative multiple of 8, codes_group_stride >= 0",
+                    fn);
+    RETURN_IF(check_ptr(fn, "x", x, work));
+    RETURN_IF(check_ptr(fn, "R", R, work));
+    if (work && !codes) return fail(LCDA_EINVAL, "%s: codes is NULL", fn);
+    if (codes && reinterpret_cast<uintptr_t>(codes) % 4 != 0)
+        return fail(LCDA_EINVAL, "%s: codes is not 4-byte aligned", fn);
+    if (!work) return LCDA_OK;
+    EncodeArgs e{};
+    e.x = x;
+    e.bf16 = dtype == LCDA_BF16;
+    e.groups = groups;
+    e.rows_per_group = rows_per_group;
+    e.x_group_stride = x_group_stride;
+    e.R = R;
+    e.bits = bits;
+    e.codes = codes;
+    e.codes_group_stride = codes_group_stride;
+    return hip_status(fn, launch_sig_encode(e, static_cast<hipStream_t>(stream)));
 }
 
 int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_stride, const int32_t* idx,

@@ -115,6 +115,18 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
+// Random-projection codes (T_map).
+struct EncodeArgs {
+    const void* x;             // row (g, i) at x + g * x_group_stride + i * 128 elements
+    bool bf16;                 // x is bf16 (else fp32)
+    int64_t groups, rows_per_group, x_group_stride;
+    const float* R;            // [128, bits]
+    int bits;                  // 1 .. 32
+    uint32_t* codes;           // row (g, i) at codes[g * codes_group_stride + i]
+    int64_t codes_group_stride;
+};
+hipError_t launch_sig_encode(const EncodeArgs& a, hipStream_t st);
+
 // Signature top-k.
 struct TopkArgs {
     const uint32_t* key_sigs;   // [B, Hkv, n]
@@ -127,6 +139,11 @@ struct TopkArgs {
     uint32_t* hist;             // ws: [B, Hq, chunks + 2, topk_hist_row()] distance histograms of each
                                 // chunk, then of the sink part and the recent part of the chunks a
                                 // window edge cuts
+    const void* q;              // [B, Hq, 128] or null: the histogram pass encodes the query codes itself
+    bool q_bf16;                // (with R [128, bits]) and writes them to q_codes, which the
+    const float* R;             // compaction then reads
+    int bits;
+    uint32_t* q_codes;          // [B, Hq]: where the encoded query codes go
     int chunks;                 // ceil(n / chunk_len) <= 64
     int64_t chunk_len;
 };

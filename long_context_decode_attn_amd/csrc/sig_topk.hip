@@ -42,6 +42,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "sig_proj.h"
 
 namespace lcda {
 namespace {
@@ -69,6 +70,32 @@ __device__ __forceinline__ void load_sub(uint32_t (&x)[16], const uint32_t* ks, 
             for (int e = 0; e < 4; ++e) x[4 * u + e] = ks[min(i + e, end - 1)];
         }
     }
+}
+
+// ---- 0. query codes at the head of the histogram pass ----------------------------
+// R ([128][32], columns at or past `bits` zero, so those bits come out 0) and
+// the G query rows (as floats) are staged in LDS with one round of loads, so
+// that the chains wait on memory once.  Thread t < 32 * G computes bit t % 32
+// of head t / 32's code, and each wavefront's ballot packs two heads' codes.
+__device__ void encode_q_heads(const TopkArgs& a, int64_t row0, int tid, float* sR /* [128 * 32 + 8 * 128] */,
+                               uint32_t* s_codes /* [8] */) {
+    float* sQ = sR + kD * 32;
+    for (int k = tid; k < kD * 32; k += 256) {
+        const int e = k >> 5, b = k & 31;
+        sR[k] = b < a.bits ? a.R[e * a.bits + b] : 0.f;
+    }
+    for (int k = tid; k < a.G * kD; k += 256) {
+        const int64_t i = row0 * kD + k;
+        sQ[k] = a.q_bf16 ? bf16_lo(static_cast<const uint16_t*>(a.q)[i]) : static_cast<const float*>(a.q)[i];
+    }
+    __syncthreads();
+    const int g = min(tid >> 5, a.G - 1), b = tid & 31;
+    const float* xr = sQ + g * kD;
+    const double z = proj_chain([&](int e) { return xr[e]; }, sR + b, 32);
+    const uint64_t bits = __ballot(z > 0.0);
+    const int h0 = 2 * (tid >> 6);
+    if ((tid & 63) == 0 && h0 < a.G) s_codes[h0] = (uint32_t)bits;
+    if ((tid & 63) == 32 && h0 + 1 < a.G) s_codes[h0 + 1] = (uint32_t)(bits >> 32);
 }
 
 // ---- 1. histogram ------------------------------------------------------------------
@@ -200,10 +227,20 @@ __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
 
     uint32_t xr[kGrp][16];
     load_group<VEC>(xr, ks, beg, end, tid);
-    zero_counters(sm, tid);
     uint32_t qs[MAXG];
+    __shared__ uint32_t s_qc[8];
+    if (a.q != nullptr) {   // uniform: the query codes are encoded here (T_map), while the codes load
+        static_assert(HistSmem<MAXG>::kWords >= kD * 32 + 8 * kD, "R and the query rows fit the counters' LDS");
+        encode_q_heads(a, row0, tid, reinterpret_cast<float*>(sm.cnt), s_qc);   // before the counters are zeroed
+        __syncthreads();
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) qs[g] = a.q_sigs[row0 + min(g, G - 1)];
+        for (int g = 0; g < MAXG; ++g) qs[g] = s_qc[min(g, G - 1)];
+        if (c == 0 && tid < G) a.q_codes[row0 + tid] = s_qc[tid];   // for the compaction
+    } else {
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g) qs[g] = a.q_sigs[row0 + min(g, G - 1)];
+    }
+    zero_counters(sm, tid);
     __syncthreads();
 
     // A chunk that a window edge cuts also counts its window part (the prefix
@@ -715,12 +752,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 #undef LCDA_HIST
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    TopkArgs ac = a;
+    if (a.q != nullptr) ac.q_sigs = a.q_codes;   // written by the histogram pass
     if (a.G <= 4) {
-        if (vec) hipLaunchKernelGGL((k_topk_compact<4, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_topk_compact<4, false>), grid, block, 0, st, a);
+        if (vec) hipLaunchKernelGGL((k_topk_compact<4, true>), grid, block, 0, st, ac);
+        else hipLaunchKernelGGL((k_topk_compact<4, false>), grid, block, 0, st, ac);
     } else {
-        if (vec) hipLaunchKernelGGL((k_topk_compact<8, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_topk_compact<8, false>), grid, block, 0, st, a);
+        if (vec) hipLaunchKernelGGL((k_topk_compact<8, true>), grid, block, 0, st, ac);
+        else hipLaunchKernelGGL((k_topk_compact<8, false>), grid, block, 0, st, ac);
     }
     return hipGetLastError();
 }

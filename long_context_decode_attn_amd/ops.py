@@ -24,7 +24,7 @@ EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn"
            "lcda_ws_bytes_cached_attn_lse", "lcda_ws_bytes_lse_merge_local",
            "lcda_ws_bytes_sig_score_topk", "lcda_ws_bytes_gather_attn",
            "lcda_last_error", "lcda_version", "lcda_set_tuning", "lcda_get_tuning",
-           "dense_decode_step", "lcda_ws_bytes_dense_decode_step")
+           "dense_decode_step", "lcda_ws_bytes_dense_decode_step", "sig_encode", "sig_score_topk_q")
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load(path: str = LIB_PATH):
     lib.cached_attn_lse.argtypes = [P, P, P, i32, i32, i32, i32, i64, i64, i32, P, P, P, sz, P]
     lib.lse_merge_local.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, sz, P]
     lib.sig_score_topk.argtypes = [P, P, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P, P, sz, P]
+    lib.sig_score_topk_q.argtypes = [P, P, i32, P, i32, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P, P, P, sz, P]
+    lib.sig_encode.argtypes = [P, i32, i64, i64, i64, P, i32, P, i64, P]
     lib.gather_attn.argtypes = [P, P, P, i64, P, P, i64, i32, i32, i32, i32, i64, i32, P, P, P, sz, P]
     for f in (lib.cached_attn_lse, lib.lse_merge_local, lib.sig_score_topk, lib.gather_attn):
         f.restype = ctypes.c_int
@@ -243,6 +245,57 @@ def sig_score_topk(key_sigs, q_sigs, m, n_sink, n_recent, cap=None, want_scores=
                             cap, _p(count), _p(scores), _p(w), w.numel() * w.element_size(), _stream(dev))
     _check("sig_score_topk", st)
     return idx, count, scores
+
+
+def sig_score_topk_q(key_sigs, q, R, m, n_sink, n_recent, cap=None, want_scores=False, idx=None, count=None,
+                     q_sigs=None, ws=None):
+    """SCORE + TOPK with the query codes encoded at the head of the scan from q [B, Hq, 128] and R [128, bits]
+    (fp32).  Returns (idx, count, scores or None, q_sigs [B, Hq] int32 storage of uint32 codes)."""
+    lib = load()
+    _need(key_sigs.dtype in (torch.int32, torch.uint32) and key_sigs.is_contiguous(), "key codes: contiguous 32-bit")
+    _need(q.is_contiguous() and q.shape[-1] == 128, "q must be contiguous [B, Hq, 128]")
+    _need(R.dtype == torch.float32 and R.is_contiguous() and R.shape[0] == 128 and R.dim() == 2, "R: [128, bits] fp32")
+    B, Hkv, n = key_sigs.shape
+    Hq = q.shape[1]
+    cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
+    dev = key_sigs.device
+    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
+    q_sigs = torch.empty((B, Hq), dtype=torch.int32, device=dev) if q_sigs is None else q_sigs
+    scores = torch.empty((B, Hq, n), dtype=torch.int8, device=dev) if want_scores else None
+    nb = lib.lcda_ws_bytes_sig_score_topk(B, Hq, Hkv, n)
+    w = _ws(nb, dev, ws)
+    st = lib.sig_score_topk_q(_p(key_sigs), _p(q), _dtype_code(q), _p(R), R.shape[1], B, Hq, Hkv, n, int(m),
+                              int(n_sink), int(n_recent), _p(idx), cap, _p(count), _p(scores), _p(q_sigs), _p(w),
+                              w.numel() * w.element_size(), _stream(dev))
+    _check("sig_score_topk_q", st)
+    return idx, count, scores, q_sigs
+
+
+def sig_encode(x, R, codes=None):
+    """Random-projection codes (T_map) of rows of 128 values, R [128, bits] fp32.
+
+    x contiguous [..., 128] gives codes [...] (int32 storage of uint32), new unless given.  x may also be a
+    [B, H, r, 128] view into a cache (rows contiguous, heads evenly strided, e.g. K[:, :, n_old:n_old + r]); codes
+    must then be the matching [B, H, r] view into the key codes (e.g. key_sigs[:, :, n_old:n_old + r])."""
+    lib = load()
+    _need(R.dtype == torch.float32 and R.is_contiguous() and R.dim() == 2 and R.shape[0] == 128, "R: [128, bits] fp32")
+    _need(x.shape[-1] == 128 and x.stride(-1) == 1, "rows of x must hold 128 contiguous values")
+    if x.is_contiguous():
+        lead = x.shape[:-1]
+        rows = x.numel() // 128
+        codes = torch.empty(lead, dtype=torch.int32, device=x.device) if codes is None else codes
+        _need(codes.is_contiguous() and codes.numel() == rows, "codes must be contiguous, one per row")
+        g, rpg, xs, cs = 1, rows, 0, 0
+    else:
+        _need(x.dim() == 4 and x.stride(2) == 128 and x.stride(0) == x.shape[1] * x.stride(1),
+              "a strided x must be [B, H, r, 128] with contiguous rows and evenly strided heads")
+        _need(codes is not None and tuple(codes.shape) == tuple(x.shape[:3]) and codes.stride(2) == 1
+              and codes.stride(0) == codes.shape[1] * codes.stride(1), "codes must be the matching [B, H, r] view")
+        g, rpg, xs, cs = x.shape[0] * x.shape[1], x.shape[2], x.stride(1), codes.stride(1)
+    st = lib.sig_encode(_p(x), _dtype_code(x), g, rpg, xs, _p(R), R.shape[1], _p(codes), cs, _stream(x.device))
+    _check("sig_encode", st)
+    return codes
 
 
 def gather_attn(q, k, v, idx, count, out=None, alpha=None, ws=None, want_alpha=True):

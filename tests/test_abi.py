@@ -101,3 +101,31 @@ def test_workspace_sizes(lib):
 
 def test_empty_batch_is_a_no_op(lib):
     assert call_dense(lib, B=0, q=None, out=None, alpha=None, ws=None, ws_bytes=0) == 0
+
+
+def test_sig_encode_rejects(lib):
+    """T_map: bad bit counts, dtypes, strides and alignments are refused before any HIP call."""
+    R = fake()
+    def call(**kw):
+        a = dict(x=fake(), dtype=1, groups=2, rpg=4, xs=4 * 128, R=R, bits=32, codes=fake(), cs=4)
+        a.update(kw)
+        return lib.sig_encode(a["x"], a["dtype"], a["groups"], a["rpg"], a["xs"], a["R"], a["bits"], a["codes"],
+                              a["cs"], None)
+    assert call(bits=0) == 1 and b"bits" in lib.lcda_last_error()
+    assert call(bits=33) == 1
+    assert call(dtype=5) == 2
+    assert call(xs=3 * 128) == 1 and b"overlap" in lib.lcda_last_error()
+    assert call(cs=3) == 1
+    assert call(xs=4 * 128 + 4) == 1 and b"multiple of 8" in lib.lcda_last_error()
+    assert call(codes=ctypes.c_void_p(0x10002)) == 1 and b"4-byte" in lib.lcda_last_error()
+    assert call(x=None) == 1
+    assert call(groups=0, x=None, R=None, codes=None) == 0   # nothing to do
+
+
+def test_sig_score_topk_q_rejects(lib):
+    st = lib.sig_score_topk_q(fake(), fake(), 1, fake(), 40, 1, 4, 1, 1000, 10, 2, 2, fake(), 14, fake(), None,
+                              fake(), fake(), 1 << 30, None)
+    assert st == 1 and b"bits" in lib.lcda_last_error()
+    st = lib.sig_score_topk_q(fake(), None, 1, fake(), 32, 1, 4, 1, 1000, 10, 2, 2, fake(), 14, fake(), None,
+                              fake(), fake(), 1 << 30, None)
+    assert st == 1 and b"q is NULL" in lib.lcda_last_error()
