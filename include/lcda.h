@@ -225,7 +225,8 @@ const char* lcda_version(void);
  *   "dense_wgs"      target workgroups of the MFMA split with 16/32-row tiles (256)
  *   "dense_wgs_nt4"  target workgroups of the MFMA split with 64-row tiles (256)
  *   "valu_wgs"       target workgroups of the fp32 dense split (512)
- *   "gather_wgs"     target workgroups of the GATHER-ATT split (2048)
+ *   "gather_wgs"     target workgroups of the GATHER-ATT split (256)
+ *   "gather_waves"   GATHER-ATT wavefronts per workgroup: 4, 8 or 16 (8)
  *   "rows_wgs"       target workgroups of the MFMA split with 64 rows per workgroup,
  *                    used when more than 16 query rows read one KV head (512)
  *   "rows_kernel"    more than 16 rows per KV head: 1 = 64-row workgroups sharing

@@ -165,6 +165,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = 1;
         p.block = valu_step_tokens();
         units = B * Hq;
+        p.waves = (int)tuning().gather_waves;
         target = (int)tuning().gather_wgs;
         p.grid_y = Hq;
         p.grid_z = B;
@@ -241,6 +242,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "dense_wgs_nt4") && value > 0) t.dense_wgs_nt4 = value;
     else if (!strcmp(key, "valu_wgs") && value > 0) t.valu_wgs = value;
     else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
+    else if (!strcmp(key, "gather_waves") && (value == 4 || value == 8 || value == 16)) t.gather_waves = value;
     else if (!strcmp(key, "rows_wgs") && value > 0) t.rows_wgs = value;
     else if (!strcmp(key, "rows_kernel") && value <= 1) t.rows_kernel = value;
     else if (!strcmp(key, "rows_variant") && value <= 7) t.rows_variant = value;
@@ -260,6 +262,7 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "dense_wgs_nt4")) return t.dense_wgs_nt4;
     if (!strcmp(key, "valu_wgs")) return t.valu_wgs;
     if (!strcmp(key, "gather_wgs")) return t.gather_wgs;
+    if (!strcmp(key, "gather_waves")) return t.gather_waves;
     if (!strcmp(key, "rows_wgs")) return t.rows_wgs;
     if (!strcmp(key, "rows_kernel")) return t.rows_kernel;
     if (!strcmp(key, "rows_variant")) return t.rows_variant;

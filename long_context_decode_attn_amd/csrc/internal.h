@@ -58,7 +58,8 @@ struct Tuning {
     int64_t dense_wgs = 256;       // target workgroups, MFMA split with 16/32-row tiles
     int64_t dense_wgs_nt4 = 256;   // target workgroups, MFMA split with 64-row tiles
     int64_t valu_wgs = 512;        // target workgroups, VALU dense split
-    int64_t gather_wgs = 2048;     // target workgroups, GATHER-ATT split
+    int64_t gather_wgs = 256;      // target workgroups, GATHER-ATT split (one per row in config 4: no combine)
+    int64_t gather_waves = 8;      // GATHER-ATT wavefronts per workgroup (4, 8 or 16)
     int64_t direct_blocks = 16;    // at most this many blocks per unit: one split, no combine pass
     int64_t rows_wgs = 512;        // target workgroups, MFMA split with 64 rows per workgroup (shared document)
     int64_t rows_kernel = 1;       // bf16 with more than 16 rows per KV head: 1 = 64-row workgroups, 0 = 32/64-row wavefronts

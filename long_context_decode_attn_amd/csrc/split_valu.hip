@@ -57,17 +57,18 @@ struct Row8<uint16_t> {
     }
 };
 
-template <typename T, int R>
+template <typename T, int R, int W>
 struct ValuSmem {
-    float o[kWaves][R][kD];
-    float2 ml[kWaves][R];
+    float o[W][R][kD];
+    float2 ml[W][R];
 };
 
 // R: query rows per unit (dense) - 1 in gather mode.  U: rows per lane group per step.
-// NTL: K/V rows are loaded nontemporal.
-template <typename T, int R, int U, bool GATHER, bool NTL>
-__global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
-    __shared__ ValuSmem<T, R> sm;
+// NTL: K/V rows are loaded nontemporal.  W: wavefronts per workgroup, which
+// share the split's token range step by step.
+template <typename T, int R, int U, bool GATHER, bool NTL, int W = kWaves>
+__global__ __launch_bounds__(64 * W) void k_split_valu(SplitArgs a) {
+    __shared__ ValuSmem<T, R, W> sm;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int j = lane >> 4, c16 = lane & 15;
@@ -130,13 +131,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 
     // Direct mode with a (alpha_in, a_in) pair: read the values this thread
     // will finish now, so their latency hides behind the main loop.
-    constexpr int kFin = (R * kD + 64 * kWaves - 1) / (64 * kWaves);
+    constexpr int kFin = (R * kD + 64 * W - 1) / (64 * W);
     float pre_al[kFin], pre_a[kFin];
 #pragma unroll
     for (int f = 0; f < kFin; ++f) {
         pre_al[f] = -INFINITY;
         pre_a[f] = 0.f;
-        const int e = threadIdx.x + f * 64 * kWaves;
+        const int e = threadIdx.x + f * 64 * W;
         const int r = e / kD;
         if (a.direct && a.alpha_in && e < R * kD && r < n_rows) {
             int b, hq;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 
     const int64_t t_begin = (int64_t)split * a.blocks_per_split * kStep;
     const int64_t t_end = min(n_tok, t_begin + (int64_t)a.blocks_per_split * kStep);
-    const int64_t stride = (int64_t)kWaves * kStep;
+    const int64_t stride = (int64_t)W * kStep;
 
     // Software pipeline over steps of kStep tokens: the positions (gather mode:
     // entries of the index list) are requested three steps ahead and the K/V
@@ -269,15 +270,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_split_valu(SplitArgs a) {
 
 #pragma unroll
     for (int f = 0; f < kFin; ++f) {
-        const int e = threadIdx.x + f * 64 * kWaves;
+        const int e = threadIdx.x + f * 64 * W;
         const int r = e / kD, c = e % kD;
         if (e >= R * kD || r >= n_rows) continue;
         float M = sm.ml[0][r].x;
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.ml[ww][r].x);
+        for (int ww = 1; ww < W; ++ww) M = fmaxf(M, sm.ml[ww][r].x);
         float L = 0.f, x = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
+        for (int ww = 0; ww < W; ++ww) {
             const float wt = fast_exp2(sm.ml[ww][r].x - M);
             L += wt * sm.ml[ww][r].y;
             x += wt * sm.o[ww][r][c];
@@ -300,7 +301,10 @@ hipError_t launch_t(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
     dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
     constexpr int U = 4;
     if (GATHER) {
-        if (tuning().gather_variant == 1) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, false>), grid, block, 0, st, a);
+        const dim3 gblock(64 * p.waves);
+        if (p.waves == 16) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true, 16>), grid, gblock, 0, st, a);
+        else if (p.waves == 8) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true, 8>), grid, gblock, 0, st, a);
+        else if (tuning().gather_variant == 1) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, false>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true>), grid, block, 0, st, a);
     } else {
         switch (p.rows_per_group) {

@@ -202,3 +202,33 @@ def test_gather_clamps_out_of_range_entries(orc):
     assert_close(out.cpu().numpy()[keep], alpha.cpu().numpy()[keep], ro[keep], ra[keep], torch.bfloat16,
                  "gather rows next to clamped rows")
     assert torch.all(out[1, 5] == 0) and torch.isneginf(alpha[1, 5])     # a negative count is an empty set
+
+
+@pytest.mark.parametrize("waves,wgs", [(4, 2048), (4, 16), (8, 16), (8, 512), (16, 16), (16, 300)])
+def test_gather_workgroup_shapes(orc, waves, wgs):
+    """GATHER-ATT with 4, 8 or 16 wavefronts per workgroup, as one split per row finished in place (few
+    workgroups) and as several splits merged by the combine pass; an empty and a one-row set included."""
+    old = (ops.get_tuning("gather_waves"), ops.get_tuning("gather_wgs"))
+    ops.set_tuning("gather_waves", waves)
+    ops.set_tuning("gather_wgs", wgs)
+    try:
+        B, Hq, Hkv, n = 2, 8, 2, 9000
+        q, k, v = _kv(B, Hq, Hkv, n, torch.bfloat16, 81)
+        ks = _sigs((B, Hkv, n), 82)
+        qs = _sigs((B, Hq), 83)
+        ri, rc, _ = orc.sig_score_topk(sig_np(ks), sig_np(qs), 700, 64, 64)
+        rc[0, 1] = 0
+        rc[1, 2] = 1
+        print("case gather waves=%d wgs=%d" % (waves, wgs), flush=True)
+        out, alpha = ops.gather_attn(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(ri).to(DEV),
+                                     torch.from_numpy(rc).to(DEV))
+        torch.cuda.synchronize()
+        ro, ra = orc.gather_attn(to_np(q), to_np(k), to_np(v), ri, rc)
+        keep = np.ones((B, Hq), bool)
+        keep[0, 1] = False
+        assert_close(out.cpu().numpy()[keep], alpha.cpu().numpy()[keep], ro[keep], ra[keep], torch.bfloat16,
+                     "gather waves=%d wgs=%d" % (waves, wgs))
+        assert torch.all(out[0, 1] == 0) and torch.isneginf(alpha[0, 1])
+    finally:
+        ops.set_tuning("gather_waves", old[0])
+        ops.set_tuning("gather_wgs", old[1])
