@@ -335,6 +335,72 @@ int orc_gather_attn(const void* q, const void* k, const void* v, int dtype,
     return bad ? 1 : 0;
 }
 
+/* ---- wider codes ---------------------------------------------------------- */
+
+/* [HA] Eq. (2) with b = 32 W bits: the Hamming distance sums the bit
+ * differences of all W words.  The selection is the one orc_sig_topk makes:
+ * sort by (distance, position), take the first min(m, n), unite with the
+ * windows, list ascending, pad with -1. */
+int orc_sig_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W,
+                   int B, int Hq, int Hkv, int64_t n, int64_t m, int64_t n_sink,
+                   int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                   int16_t* scores) {
+    if (!q_sigs || !idx || !count || (n > 0 && !key_sigs)) return 1;
+    if (W < 1 || W > 16 || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 1;
+    if (n < 0 || m < 0 || n_sink < 0 || n_recent < 0 || cap < 0 || n > 2147483647LL) return 1;
+    if (cap < (m + n_sink + n_recent < n ? m + n_sink + n_recent : n)) return 1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        dist_pos* list = (dist_pos*)malloc(sizeof(dist_pos) * (size_t)(n > 0 ? n : 1));
+        unsigned char* chosen = (unsigned char*)malloc((size_t)(n > 0 ? n : 1));
+        if (!list || !chosen) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic)
+        for (int b = 0; b < B; ++b)
+            for (int hq = 0; hq < Hq; ++hq) {
+                if (!list || !chosen) continue;
+                int h = hq / G;
+                int64_t row = (int64_t)b * Hq + hq;
+                const uint32_t* ks = key_sigs + ((int64_t)b * Hkv + h) * n * W;
+                const uint32_t* qw = q_sigs + row * W;
+                for (int64_t i = 0; i < n; ++i) {
+                    int dist = 0;
+                    for (int w = 0; w < W; ++w) dist += hamming32(ks[i * W + w], qw[w]);
+                    list[i].dist = dist;
+                    list[i].pos = i;
+                    if (scores) scores[row * n + i] = (int16_t)(-dist);
+                    chosen[i] = 0;
+                }
+                qsort(list, (size_t)n, sizeof(dist_pos), cmp_dist_pos);
+                int64_t take = m < n ? m : n;
+                for (int64_t t = 0; t < take; ++t) chosen[list[t].pos] = 1;
+                for (int64_t i = 0; i < n && i < n_sink; ++i) chosen[i] = 1;
+                for (int64_t i = (n - n_recent > 0 ? n - n_recent : 0); i < n; ++i) chosen[i] = 1;
+                int64_t c = 0;
+                int overflow = 0;
+                for (int64_t i = 0; i < n; ++i)
+                    if (chosen[i]) {
+                        if (c < cap) idx[row * cap + c] = (int32_t)i;
+                        else overflow = 1;
+                        ++c;
+                    }
+                for (int64_t t = c; t < cap; ++t) idx[row * cap + t] = -1;
+                count[row] = (int32_t)(c < cap ? c : cap);
+                if (overflow) {
+#pragma omp atomic write
+                    bad = 1;
+                }
+            }
+        free(list);
+        free(chosen);
+    }
+    return bad ? 1 : 0;
+}
+
 /* ---- T_map: random-projection signatures ---------------------------------- */
 
 /* phi(x) = ReLU(sign(F(x))) with F(x) = R^T x, [HA] Eq. (1); component b is

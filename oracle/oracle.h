@@ -55,6 +55,17 @@ int orc_gather_attn(const void* q, const void* k, const void* v, int dtype,
                     int64_t cap, int B, int Hq, int Hkv, int d, int64_t n,
                     double* out, double* alpha);
 
+/* SCORE + TOPK over codes of W 32-bit words (b = 32 W bits, 1 <= W <= 16):
+ * the distance is the popcount of the XOR over all W words, so it runs from 0
+ * to b; selection, windows, order and padding as in orc_sig_topk.  The wider
+ * codes are the ones HashAttention's code-width sweep scores (slide "Table 6:
+ * scoring cost", 64 to 512 bits).  key_sigs [B, Hkv, n, W], q_sigs [B, Hq, W];
+ * scores [B, Hq, n] int16 (= -distance) or NULL. */
+int orc_sig_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W,
+                   int B, int Hq, int Hkv, int64_t n, int64_t m, int64_t n_sink,
+                   int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                   int16_t* scores);
+
 /* T_map with a random projection (the LSH selector HashAttention compares
  * against): code bit b of row i is phi(x_i)_b = ReLU(sign(z_b)), i.e. 1 when
  * z_b = sum_e x[i][e] * R[e][b] > 0 and 0 otherwise ("A 32-bit signature makes

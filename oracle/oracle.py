@@ -75,7 +75,9 @@ class Oracle:
         lib.orc_sig_topk.argtypes = [P, P, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P]
         lib.orc_gather_attn.argtypes = [P, P, P, i32, i64, P, P, i64, i32, i32, i32, i32, i64, P, P]
         lib.orc_sig_encode.argtypes = [P, i32, i64, i32, P, i32, P]
-        for f in (lib.orc_dense_attn, lib.orc_merge_local, lib.orc_sig_topk, lib.orc_gather_attn, lib.orc_sig_encode):
+        lib.orc_sig_topk_w.argtypes = [P, P, i32, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P]
+        for f in (lib.orc_dense_attn, lib.orc_merge_local, lib.orc_sig_topk, lib.orc_gather_attn, lib.orc_sig_encode,
+                  lib.orc_sig_topk_w):
             f.restype = ctypes.c_int
         lib.orc_set_threads.argtypes = [i32]
         lib.orc_set_threads.restype = None
@@ -171,6 +173,26 @@ class Oracle:
         if st:
             raise ValueError("orc_gather_attn: invalid arguments")
         return out, alpha
+
+    def sig_score_topk_w(self, key_sigs, q_sigs, m, n_sink, n_recent, cap=None, want_scores=False):
+        """SCORE + TOPK over codes of W words.  key_sigs [B, Hkv, n, W] uint32, q_sigs [B, Hq, W] uint32.
+
+        Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, scores [B, Hq, n] int16 or None)."""
+        ks = _c(np.asarray(key_sigs).view(np.uint32), np.uint32)
+        qs = _c(np.asarray(q_sigs).view(np.uint32), np.uint32)
+        B, Hkv, n, W = ks.shape
+        Hq = qs.shape[1]
+        assert qs.shape == (B, Hq, W)
+        if cap is None:
+            cap = capacity(n, m, n_sink, n_recent)
+        idx = np.empty((B, Hq, cap), np.int32)
+        count = np.empty((B, Hq), np.int32)
+        scores = np.empty((B, Hq, n), np.int16) if want_scores else None
+        st = self.lib.orc_sig_topk_w(_ptr(ks), _ptr(qs), W, B, Hq, Hkv, n, int(m), int(n_sink), int(n_recent),
+                                     _ptr(idx), int(cap), _ptr(count), _ptr(scores))
+        if st:
+            raise ValueError("orc_sig_topk_w: invalid arguments or cap too small")
+        return idx, count, scores
 
     def sig_encode(self, x, R):
         """Random-projection codes of the rows of x [..., d] (bf16 bit patterns or float32):

@@ -33,6 +33,8 @@ MUTANTS = {
     "signature of a zero projection set": ("if (z > 0.0) c |= 1u << b;", "if (z >= 0.0) c |= 1u << b;"),
     "signature bits reversed": ("if (z > 0.0) c |= 1u << b;", "if (z > 0.0) c |= 1u << (bits - 1 - b);"),
     "projection read transposed": ("(double)R[(int64_t)e * bits + b]", "(double)R[(int64_t)b * d + e]"),
+    "wide codes skip the last word": ("for (int w = 0; w < W; ++w) dist +=", "for (int w = 0; w < W - 1; ++w) dist +="),
+    "wide codes read one word per key": ("hamming32(ks[i * W + w], qw[w])", "hamming32(ks[i + w], qw[w])"),
 }
 
 
@@ -48,6 +50,8 @@ def _run(fn, orc):
     kw = {"orc": orc}
     if "n" in inspect.signature(fn).parameters:
         kw["n"] = 7
+    if "W" in inspect.signature(fn).parameters:
+        kw["W"] = 4
     fn(**kw)
 
 

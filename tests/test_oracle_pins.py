@@ -533,3 +533,70 @@ def test_sig_encode_fewer_bits_and_empty(orc):
     c8 = orc.sig_encode(x, np.ascontiguousarray(R[:, :8]))
     np.testing.assert_array_equal(c8, c32 & 0xFF)
     assert orc.sig_encode(np.zeros((0, 128), np.float32), R).shape == (0,)
+
+
+# ------------------------------------------------------ wider codes (N3) ----
+def _brute_topk_w(ks, qs, m, s, r):
+    """Brute force: distances from a bit-by-bit count, a stable sort on (distance, position), the first m,
+    the windows, ascending."""
+    B, Hkv, n, W = ks.shape
+    Hq = qs.shape[1]
+    G = Hq // Hkv
+    out = []
+    for b in range(B):
+        for hq in range(Hq):
+            x = ks[b, hq // G] ^ qs[b, hq][None, :]
+            d = np.zeros(n, np.int64)
+            for w in range(W):
+                for bit in range(32):
+                    d += ((x[:, w] >> np.uint32(bit)) & np.uint32(1)).astype(np.int64)
+            order = sorted(range(n), key=lambda i: (d[i], i))
+            chosen = set(order[:min(m, n)]) | set(range(min(s, n))) | set(range(max(n - r, 0), n))
+            out.append((sorted(chosen), -d))
+    return out
+
+
+@pytest.mark.parametrize("W", [2, 4, 16])
+def test_wide_topk_brute_force(orc, W):
+    """Tiny inputs with few distinct codes (ties everywhere) against a brute-force selection."""
+    g = rng(700 + W)
+    B, Hq, Hkv, n = 2, 4, 2, 57
+    pool = g.integers(0, 2 ** 32, (5, W), dtype=np.uint64).astype(np.uint32)
+    ks = pool[g.integers(0, 5, (B, Hkv, n))]
+    qs = g.integers(0, 2 ** 32, (B, Hq, W), dtype=np.uint64).astype(np.uint32)
+    for m, s, r in [(10, 3, 4), (0, 2, 2), (57, 0, 0), (20, 30, 30)]:
+        idx, cnt, sc = orc.sig_score_topk_w(ks, qs, m, s, r, want_scores=True)
+        for row, (want, negd) in enumerate(_brute_topk_w(ks, qs, m, s, r)):
+            b, hq = divmod(row, Hq)
+            assert cnt[b, hq] == len(want)
+            np.testing.assert_array_equal(idx[b, hq, :len(want)], want)
+            assert np.all(idx[b, hq, len(want):] == -1)
+            np.testing.assert_array_equal(sc[b, hq], negd)
+
+
+def test_wide_topk_one_word_and_constant_words(orc):
+    """W = 1 is the 32-bit selection; extra words that every key shares with the query change nothing."""
+    g = rng(710)
+    B, Hq, Hkv, n = 1, 4, 1, 3000
+    ks = g.integers(0, 2 ** 32, (B, Hkv, n), dtype=np.uint64).astype(np.uint32)
+    qs = g.integers(0, 2 ** 32, (B, Hq), dtype=np.uint64).astype(np.uint32)
+    ri, rc, _ = orc.sig_score_topk(ks, qs, 100, 8, 8)
+    i1, c1, _ = orc.sig_score_topk_w(ks[..., None], qs[..., None], 100, 8, 8)
+    np.testing.assert_array_equal(i1, ri)
+    np.testing.assert_array_equal(c1, rc)
+    extra = g.integers(0, 2 ** 32, (B, Hq, 3), dtype=np.uint64).astype(np.uint32)
+    extra[:] = extra[:, :1]       # one shared pattern per batch item
+    ks4 = np.concatenate([ks[..., None], np.broadcast_to(extra[:, :1, None, :], (B, Hkv, n, 3))], axis=-1)
+    qs4 = np.concatenate([qs[..., None], np.broadcast_to(extra[:, :1, :], (B, Hq, 3))], axis=-1)
+    i4, c4, _ = orc.sig_score_topk_w(ks4, qs4, 100, 8, 8)
+    np.testing.assert_array_equal(i4, ri)
+
+
+def test_wide_topk_4bit_example_in_wide_codes(orc):
+    """The slide's 4-bit example (distances 0, 1, 3) placed in the third word of 4-word codes."""
+    ks = np.zeros((1, 1, 3, 4), np.uint32)
+    qs = np.zeros((1, 1, 4), np.uint32)
+    ks[0, 0, :, 2] = [0b1011, 0b1001, 0b0110]
+    qs[0, 0, 2] = 0b1011
+    idx, cnt, sc = orc.sig_score_topk_w(ks, qs, 2, 0, 0, want_scores=True)
+    assert sc.tolist() == [[[0, -1, -3]]] and cnt[0, 0] == 2 and idx[0, 0].tolist() == [0, 1]
