@@ -7,6 +7,7 @@
  *   sparse: sig_encode        - T_map: random-projection codes of queries or new keys
  *           sig_score_topk    - HashAttention SCORE + TOPK over 32-bit codes
  *           sig_score_topk_q  - the same with the query codes encoded at its head
+ *           sig_score_topk_w  - the same over codes of 2 to 16 words (64 to 512 bits)
  *           gather_attn       - attention renormalised over the selected rows
  *
  * Conventions shared by every call
@@ -132,6 +133,23 @@ int sig_score_topk_q(const uint32_t* key_sigs, const void* q, int q_dtype, const
                      int32_t* idx, int64_t cap, int32_t* count, int8_t* scores, uint32_t* q_sigs,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* SCORE + TOPK over codes of W 32-bit words (b = 32 W bits; W = 1, 2, 4, 8 or
+ * 16): the distance popcount(h_i XOR h_q) of sig_score_topk summed over the
+ * words, from 0 to b; the same selection, windows, order and padding.  These
+ * are the code widths of HashAttention's scoring-cost sweep (64 to 512 bits;
+ * slide with Table 6).  One workgroup per query head: the plain form, in which
+ * each of a group's G query heads reads its KV head's codes.
+ *
+ *   key_sigs  [B, Hkv, n, W] uint32 (word w of position i's code at i*W + w)
+ *   q_sigs    [B, Hq, W]     uint32
+ *   idx, cap, count          as in sig_score_topk
+ *   scores    [B, Hq, n] int16 = -distance, or NULL
+ *   ws        at least lcda_ws_bytes_sig_score_topk_w(B, Hq, n) bytes
+ */
+int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, int B, int Hq, int Hkv, int64_t n,
+                     int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                     int16_t* scores, void* ws, size_t ws_bytes, void* stream);
+
 /* T_map with a random projection: 32-bit codes of 128-value rows.
  *
  * Bit b of the code of row x is phi(x)_b = ReLU(sign(x . R[:, b])): 1 when
@@ -209,6 +227,7 @@ size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n,
 size_t lcda_ws_bytes_lse_merge_local(int B, int Hq, int Hkv, int d, int64_t n_loc_max);
 size_t lcda_ws_bytes_sig_score_topk(int B, int Hq, int Hkv, int64_t n);
 size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap);
+size_t lcda_ws_bytes_sig_score_topk_w(int B, int Hq, int64_t n);
 size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n,
                                        int64_t kv_batch_stride, int64_t n_loc_max);
 

@@ -608,6 +608,59 @@ int sig_score_topk_q(const uint32_t* key_sigs, const void* q, int q_dtype, const
                      n_recent, idx, cap, count, scores, ws, ws_bytes, stream);
 }
 
+size_t lcda_ws_bytes_sig_score_topk_w(int B, int Hq, int64_t n) {
+    if (B < 0 || Hq <= 0 || n < 0 || n > INT32_MAX) return 0;
+    return round_up((size_t)B * Hq * (size_t)n * sizeof(uint16_t)) + 256;
+}
+
+int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, int B, int Hq, int Hkv, int64_t n,
+                     int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count,
+                     int16_t* scores, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "sig_score_topk_w";
+    if (W != 1 && W != 2 && W != 4 && W != 8 && W != 16)
+        return fail(LCDA_EUNSUPPORTED, "%s: W = %d words (1, 2, 4, 8 or 16 supported)", fn, W);
+    if (B < 0) return fail(LCDA_EINVAL, "%s: B = %d < 0", fn, B);
+    if (Hq <= 0 || Hkv <= 0) return fail(LCDA_EINVAL, "%s: Hq = %d, Hkv = %d must be positive", fn, Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(LCDA_EINVAL, "%s: Hq = %d is not a multiple of Hkv = %d", fn, Hq, Hkv);
+    RETURN_IF(check_n(fn, "n", n));
+    if (m < 0 || n_sink < 0 || n_recent < 0)
+        return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be >= 0", fn);
+    if (cap < 0 || cap > INT32_MAX) return fail(LCDA_EINVAL, "%s: cap = %lld out of range", fn, (long long)cap);
+    const int64_t need = (m + n_sink + n_recent < n) ? m + n_sink + n_recent : n;
+    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX || cap < need)
+        return fail(LCDA_EINVAL, "%s: cap = %lld < min(n, m + n_sink + n_recent) = %lld", fn, (long long)cap,
+                    (long long)need);
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "key_sigs", key_sigs, work && n > 0));
+    RETURN_IF(check_ptr(fn, "q_sigs", q_sigs, work));
+    RETURN_IF(check_ptr(fn, "idx", idx, work && cap > 0));
+    RETURN_IF(check_ptr(fn, "count", count, work));
+    RETURN_IF(check_ptr(fn, "scores", scores, false));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    if (!work) return LCDA_OK;
+    const size_t need_ws = lcda_ws_bytes_sig_score_topk_w(B, Hq, n);
+    if (!ws || ws_bytes < need_ws)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, need_ws);
+    WideArgs a{};
+    a.key_sigs = key_sigs;
+    a.q_sigs = q_sigs;
+    a.W = W;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.n = n;
+    a.m = m;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.cap = cap;
+    a.idx = idx;
+    a.count = count;
+    a.scores = scores;
+    a.dist = static_cast<uint16_t*>(ws);
+    return hip_status(fn, launch_topk_wide(a, static_cast<hipStream_t>(stream)));
+}
+
 int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group, int64_t x_group_stride,
                const float* R, int bits, uint32_t* codes, int64_t codes_group_stride, void* stream) {
     static const char* fn = "sig_encode";

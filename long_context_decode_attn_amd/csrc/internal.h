@@ -116,6 +116,19 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
+// Signature top-k over codes of W words (one workgroup per query head).
+struct WideArgs {
+    const uint32_t* key_sigs;   // [B, Hkv, n, W]
+    const uint32_t* q_sigs;     // [B, Hq, W]
+    int W, B, Hq, Hkv, G;
+    int64_t n, m, n_sink, n_recent, cap;
+    int32_t* idx;               // [B, Hq, cap]
+    int32_t* count;             // [B, Hq]
+    int16_t* scores;            // [B, Hq, n] or null
+    uint16_t* dist;             // ws: [B, Hq, n] distances
+};
+hipError_t launch_topk_wide(const WideArgs& a, hipStream_t st);
+
 // Random-projection codes (T_map).
 struct EncodeArgs {
     const void* x;             // row (g, i) at x + g * x_group_stride + i * 128 elements

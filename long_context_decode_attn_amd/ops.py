@@ -24,7 +24,8 @@ EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn"
            "lcda_ws_bytes_cached_attn_lse", "lcda_ws_bytes_lse_merge_local",
            "lcda_ws_bytes_sig_score_topk", "lcda_ws_bytes_gather_attn",
            "lcda_last_error", "lcda_version", "lcda_set_tuning", "lcda_get_tuning",
-           "dense_decode_step", "lcda_ws_bytes_dense_decode_step", "sig_encode", "sig_score_topk_q")
+           "dense_decode_step", "lcda_ws_bytes_dense_decode_step", "sig_encode", "sig_score_topk_q",
+           "sig_score_topk_w", "lcda_ws_bytes_sig_score_topk_w")
 
 _lib = None
 
@@ -50,6 +51,9 @@ def load(path: str = LIB_PATH):
     lib.sig_score_topk.argtypes = [P, P, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P, P, sz, P]
     lib.sig_score_topk_q.argtypes = [P, P, i32, P, i32, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P, P, P, sz, P]
     lib.sig_encode.argtypes = [P, i32, i64, i64, i64, P, i32, P, i64, P]
+    lib.sig_score_topk_w.argtypes = [P, P, i32, i32, i32, i32, i64, i64, i64, i64, P, i64, P, P, P, sz, P]
+    lib.lcda_ws_bytes_sig_score_topk_w.argtypes = [i32, i32, i64]
+    lib.lcda_ws_bytes_sig_score_topk_w.restype = sz
     lib.gather_attn.argtypes = [P, P, P, i64, P, P, i64, i32, i32, i32, i32, i64, i32, P, P, P, sz, P]
     for f in (lib.cached_attn_lse, lib.lse_merge_local, lib.sig_score_topk, lib.gather_attn):
         f.restype = ctypes.c_int
@@ -270,6 +274,30 @@ def sig_score_topk_q(key_sigs, q, R, m, n_sink, n_recent, cap=None, want_scores=
                               w.numel() * w.element_size(), _stream(dev))
     _check("sig_score_topk_q", st)
     return idx, count, scores, q_sigs
+
+
+def sig_score_topk_w(key_sigs, q_sigs, m, n_sink, n_recent, cap=None, want_scores=False, idx=None, count=None,
+                     ws=None):
+    """SCORE + TOPK over codes of W words.  key_sigs [B, Hkv, n, W], q_sigs [B, Hq, W] (int32 storage).
+
+    Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, scores [B, Hq, n] int16 or None)."""
+    lib = load()
+    _need(key_sigs.dtype in (torch.int32, torch.uint32) and q_sigs.dtype == key_sigs.dtype, "codes must be 32-bit")
+    _need(key_sigs.is_contiguous() and q_sigs.is_contiguous(), "codes must be contiguous")
+    B, Hkv, n, W = key_sigs.shape
+    Hq = q_sigs.shape[1]
+    _need(tuple(q_sigs.shape) == (B, Hq, W), "q_sigs must be [B, Hq, W]")
+    cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
+    dev = key_sigs.device
+    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
+    scores = torch.empty((B, Hq, n), dtype=torch.int16, device=dev) if want_scores else None
+    nb = lib.lcda_ws_bytes_sig_score_topk_w(B, Hq, n)
+    w = _ws(nb, dev, ws)
+    st = lib.sig_score_topk_w(_p(key_sigs), _p(q_sigs), W, B, Hq, Hkv, n, int(m), int(n_sink), int(n_recent), _p(idx),
+                              cap, _p(count), _p(scores), _p(w), w.numel() * w.element_size(), _stream(dev))
+    _check("sig_score_topk_w", st)
+    return idx, count, scores
 
 
 def sig_encode(x, R, codes=None):
