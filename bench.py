@@ -10,6 +10,7 @@ A step is one decode step of the named workload through the HIP library:
               m = n/32 + 128 sink + 128 recent: sig_score_topk + gather_attn
   quadrature  Nectar's quadrature module as cached_attn_lse: 256 queries against p = 6,144 shared
               (W, Z) pairs per KV head (the 10 % module of a 61,440-token document); MFMA-bound
+  sigwidth    sig_score_topk_w on the sparse128k shape with random codes of 32 to 512 bits (value: 256)
   needles512k n=524,288 bf16, batch 4, 64 planted needles per head: the sparse step (m=n/64)
               against cached_attn_lse on the same inputs, with needle recall, attention mass
               captured and the sparse output's error against the dense one
@@ -443,6 +444,36 @@ def bench_quadrature(args, cfg):
             "rotations": rot}
 
 
+# --------------------------------------------------------------- sigwidth ----
+def bench_sigwidth(args, cfg):
+    """sig_score_topk_w at 32 to 512 bits on config 4's shape (random codes): the code-width sweep."""
+    B, Hq, Hkv, n = cfg.B, cfg.Hq, cfg.Hkv, cfg.n
+    out = {}
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    for W in (1, 2, 4, 8, 16):
+        sets = []
+        for r in range(2):
+            ks = torch.randint(-(1 << 31), 1 << 31, (B, Hkv, n, W), generator=gen, device="cuda", dtype=torch.int64)
+            qs = torch.randint(-(1 << 31), 1 << 31, (B, Hq, W), generator=gen, device="cuda", dtype=torch.int64)
+            ks, qs = ks.to(torch.int32), qs.to(torch.int32)
+            cap = ops.capacity(n, cfg.m, cfg.n_sink, cfg.n_recent)
+            idx = torch.empty((B, Hq, cap), dtype=torch.int32, device="cuda")
+            cnt = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
+            ws = torch.empty(ops.load().lcda_ws_bytes_sig_score_topk_w(B, Hq, n), dtype=torch.uint8, device="cuda")
+            sets.append((ks, qs, idx, cnt, ws))
+        fns = [lambda s_=s_: ops.sig_score_topk_w(s_[0], s_[1], cfg.m, cfg.n_sink, cfg.n_recent, idx=s_[2],
+                                                   count=s_[3], ws=s_[4]) for s_ in sets]
+        torch.cuda.synchronize()
+        steps = max(10, args.steps // 4)
+        ms = run_steps(fns, steps, max(2, args.warmup // 4), args.graph) / steps
+        code_bytes = B * Hkv * n * 4 * W
+        out["%d_bits" % (32 * W)] = {"us": ms * 1e3, "queries_per_s": B / (ms * 1e-3), "code_bytes": code_bytes,
+                                    "code_tbps": code_bytes / (ms * 1e-3) / 1e12}
+        del sets, fns
+        torch.cuda.empty_cache()
+    return out
+
+
 # -------------------------------------------------------------- CPU oracle ----
 def cpu_baseline_dense(cfg, seconds: float):
     """The oracle (plain C, fp64) on the host's cores over whole decode steps of the same workload."""
@@ -525,7 +556,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dense61k",
-                    choices=["dense61k", "shared36", "sparse128k", "needles512k", "quadrature"])
+                    choices=["dense61k", "shared36", "sparse128k", "needles512k", "quadrature", "sigwidth"])
     ap.add_argument("--rot", type=int, default=0, help="input sets cycled (0: workload default)")
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
@@ -593,6 +624,18 @@ def main():
         line["detail"] = res
         if args.cpu_seconds > 0:
             line["cpu_baseline"] = cpu_baseline_sparse(cfg, args.cpu_seconds)
+    elif args.workload == "sigwidth":
+        cfg = synth.CONFIGS[4]
+        res = bench_sigwidth(args, cfg)
+        w8 = res["256_bits"]
+        line.update({"value": w8["queries_per_s"], "steps": max(10, args.steps // 4), "ms_per_step": w8["us"] / 1e3})
+        line["roofline"] = {"bound": "hbm", "achieved": w8["code_tbps"] * 1e3, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                            "frac": w8["code_tbps"] * 1e12 / HBM_PEAK, "traffic": None,
+                            "kernel": "k_topk_wide<8> (256-bit codes; achieved on the key-code bytes)"}
+        line["config"] = {"workload": "sigwidth: sig_score_topk_w on " + cfg.name + ", random codes of 32-512 bits",
+                          "launch": launch}
+        line["step"] = "sig_score_topk_w at 256 bits (value); every width in detail"
+        line["detail"] = res
     elif args.workload == "quadrature":
         cfg = synth.QUADRATURE
         res = bench_quadrature(args, cfg)

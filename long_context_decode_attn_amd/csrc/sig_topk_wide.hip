@@ -9,12 +9,12 @@
 // ascending, padded with -1.  Wider codes are the ones the pages' code-width
 // sweep scores (slide with Table 6, 64 to 512 bits).
 //
-// One workgroup per query head (row), in three phases:
+// One workgroup of 16 wavefronts per query head (row), in three phases:
 //   1. every position's distance, kept in the workspace (u16), and a b+1-bin
 //      histogram, one copy per wavefront in LDS;
 //   2. the threshold t (the first bin whose prefix reaches m) and the quota of
 //      ties at t the top m takes;
-//   3. ordered compaction in tiles of 4096 positions (16 consecutive per
+//   3. ordered compaction in tiles of 16,384 positions (16 consecutive per
 //      thread): one wavefront-plus-LDS scan per tile of the selected and the
 //      tie counts, packed in the two halves of a word, places every position.
 // This is the plain form: a head's G query heads each read the key codes.
@@ -25,7 +25,8 @@
 namespace lcda {
 namespace {
 
-constexpr int kWThreads = 256;
+constexpr int kWThreads = 1024;
+constexpr int kWWaves = kWThreads / 64;
 constexpr int kWMaxBins = 16 * 32 + 1;
 constexpr int kWPer = 16;                       // positions per thread and tile
 constexpr int kWTile = kWThreads * kWPer;
@@ -43,9 +44,9 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
 template <int W>
 __global__ __launch_bounds__(kWThreads) void k_topk_wide(WideArgs a) {
     constexpr int kBinsW = 32 * W + 1;
-    __shared__ uint32_t hist[4][kBinsW];
+    __shared__ uint32_t hist[kWWaves][kBinsW];
     __shared__ uint32_t s_tot[kBinsW];
-    __shared__ uint32_t s_wave[4];
+    __shared__ uint32_t s_wave[kWWaves];
     __shared__ int s_t;
     __shared__ uint32_t s_quota;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(kWThreads) void k_topk_wide(WideArgs a) {
     uint32_t q[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) q[k] = a.q_sigs[row * W + k];
-    for (int k = tid; k < 4 * kBinsW; k += kWThreads) (&hist[0][0])[k] = 0u;
+    for (int k = tid; k < kWWaves * kBinsW; k += kWThreads) (&hist[0][0])[k] = 0u;
     __syncthreads();
 
     // 1. distances and per-wavefront histograms
@@ -80,7 +81,12 @@ __global__ __launch_bounds__(kWThreads) void k_topk_wide(WideArgs a) {
         __hip_atomic_fetch_add(&hist[w][d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
-    for (int k = tid; k < kBinsW; k += kWThreads) s_tot[k] = hist[0][k] + hist[1][k] + hist[2][k] + hist[3][k];
+    for (int k = tid; k < kBinsW; k += kWThreads) {
+        uint32_t sum = 0;
+#pragma unroll
+        for (int ww = 0; ww < kWWaves; ++ww) sum += hist[ww][k];
+        s_tot[k] = sum;
+    }
     __syncthreads();
 
     // 2. threshold and quota (wavefront 0; lane l owns bins l*per .. l*per + per - 1)
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kWThreads) void k_topk_wide(WideArgs a) {
         __syncthreads();
         uint32_t tb = ties_run + ti - nt, tall = 0;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < kWWaves; ++ww) {
             tb += ww < w ? s_wave[ww] : 0u;
             tall += s_wave[ww];
         }
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(kWThreads) void k_topk_wide(WideArgs a) {
         __syncthreads();
         uint32_t sb = sel_run + si - ns, sall = 0;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < kWWaves; ++ww) {
             sb += ww < w ? s_wave[ww] : 0u;
             sall += s_wave[ww];
         }
