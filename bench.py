@@ -619,7 +619,8 @@ def main():
                             "frac": ach / HBM_PEAK,
                             "traffic": traffic_from_profile("split_valu_sparse128k", int(res["gather_bytes"]),
                                                             "split_valu"),
-                            "kernel": "gather_attn (k_split_valu gather + k_combine; achieved on unique rows)"}
+                            "kernel": "gather_attn (k_split_valu in gather mode, one workgroup per query head "
+                                      "here, so no combine pass; achieved on unique rows)"}
         line["config"] = {"workload": "sparse128k: " + cfg.name, "launch": launch}
         line["detail"] = res
         if args.cpu_seconds > 0:

@@ -81,7 +81,11 @@ __global__ __launch_bounds__(64 * W) void k_split_valu(SplitArgs a) {
     int64_t n_tok;
     const int32_t* list = nullptr;
     if (GATHER) {
-        const int hq = blockIdx.y, b = blockIdx.z;
+        // blockIdx.y walks the KV heads fastest, so that the G query heads of
+        // one KV head sit Hkv workgroups apart in dispatch order: on the same
+        // XCD (workgroups go round the 8 XCDs in turn) when Hkv * splits is a
+        // multiple of 8, where the rows the heads share hit that XCD's L2.
+        const int hq = (int)(blockIdx.y % a.Hkv) * a.G + (int)(blockIdx.y / a.Hkv), b = blockIdx.z;
         h = hq / a.G;
         bkv = a.shared ? 0 : b;
         rows_base = 0;
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(64 * W) void k_split_valu(SplitArgs a) {
     auto row_bhq = [&](int r, int& b, int& hq) {
         if (GATHER) {
             b = blockIdx.z;
-            hq = blockIdx.y;
+            hq = (int)(blockIdx.y % a.Hkv) * a.G + (int)(blockIdx.y / a.Hkv);
         } else {
             const int rr = rows_base + r;
             b = a.shared ? rr / a.G : bkv;
