@@ -247,14 +247,17 @@ const char* lcda_version(void);
  *   "gather_wgs"     target workgroups of the GATHER-ATT split (256)
  *   "gather_waves"   GATHER-ATT wavefronts per workgroup: 4, 8 or 16 (8)
  *   "rows_wgs"       target workgroups of the MFMA split with 64 rows per workgroup,
- *                    used when more than 16 query rows read one KV head (512)
+ *                    used when more than 64 query rows read one KV head (512)
+ *   "rows_wgs_single" the same when 17 to 64 query rows read one KV head (256)
  *   "rows_kernel"    more than 16 rows per KV head: 1 = 64-row workgroups sharing
  *                    each block through LDS, 0 = one wavefront per 32 / 64 rows (1)
  *   "rows_variant"   64-row workgroups: 0 = 4-slot LDS ring, 2 workgroups per CU;
  *                    1 = 3 slots, 3 per CU; 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU;
  *                    4-6 = every wavefront loads the block into registers (4: cached
  *                    loads, 2 workgroups per CU; 5: nontemporal; 6: cached, 1 per CU);
- *                    7 = 5-slot ring, 2 per CU (0)
+ *                    7 = 5-slot ring, 2 per CU; 8 = two 16-row tiles per wavefront, the
+ *                    two wavefronts of each 32-row half on alternate blocks, 5-slot
+ *                    ring, 2 per CU (8)
  *   "direct_blocks"  units with at most this many token blocks run as one split
  *                    that writes its rows directly, without a combine pass, when
  *                    the units alone reach the workgroup target (16)

@@ -178,7 +178,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = 32;
         units = bkv * Hkv * p.row_groups;
-        target = (int)tuning().rows_wgs;
+        target = (int)(p.row_groups == 1 ? tuning().rows_wgs_single : tuning().rows_wgs);
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
     } else if (dtype == LCDA_BF16) {
@@ -244,8 +244,9 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
     else if (!strcmp(key, "gather_waves") && (value == 4 || value == 8 || value == 16)) t.gather_waves = value;
     else if (!strcmp(key, "rows_wgs") && value > 0) t.rows_wgs = value;
+    else if (!strcmp(key, "rows_wgs_single") && value > 0) t.rows_wgs_single = value;
     else if (!strcmp(key, "rows_kernel") && value <= 1) t.rows_kernel = value;
-    else if (!strcmp(key, "rows_variant") && value <= 7) t.rows_variant = value;
+    else if (!strcmp(key, "rows_variant") && value <= 8) t.rows_variant = value;
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
     else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
@@ -264,6 +265,7 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "gather_wgs")) return t.gather_wgs;
     if (!strcmp(key, "gather_waves")) return t.gather_waves;
     if (!strcmp(key, "rows_wgs")) return t.rows_wgs;
+    if (!strcmp(key, "rows_wgs_single")) return t.rows_wgs_single;
     if (!strcmp(key, "rows_kernel")) return t.rows_kernel;
     if (!strcmp(key, "rows_variant")) return t.rows_variant;
     if (!strcmp(key, "direct_blocks")) return t.direct_blocks;

@@ -61,12 +61,16 @@ struct Tuning {
     int64_t gather_wgs = 256;      // target workgroups, GATHER-ATT split (one per row in config 4: no combine)
     int64_t gather_waves = 8;      // GATHER-ATT wavefronts per workgroup (4, 8 or 16)
     int64_t direct_blocks = 16;    // at most this many blocks per unit: one split, no combine pass
-    int64_t rows_wgs = 512;        // target workgroups, MFMA split with 64 rows per workgroup (shared document)
+    int64_t rows_wgs = 512;        // target workgroups, MFMA split with 64 rows per workgroup (shared document),
+                                   // several 64-row groups per KV head (MFMA-bound: two workgroups per CU)
+    int64_t rows_wgs_single = 256; // the same with one 64-row group per KV head (HBM-bound: one workgroup per
+                                   // CU, half the partial states of two)
     int64_t rows_kernel = 1;       // bf16 with more than 16 rows per KV head: 1 = 64-row workgroups, 0 = 32/64-row wavefronts
-    int64_t rows_variant = 0;      // 64-row workgroups: 0 = 4-slot ring, 2 per CU; 1 = 3 slots, 3 per CU;
+    int64_t rows_variant = 8;      // 64-row workgroups: 0 = 4-slot ring, 2 per CU; 1 = 3 slots, 3 per CU;
                                    // 2 = 3 slots, 2 per CU; 3 = 2 slots, 3 per CU; 4-6 = blocks in registers
                                    // (4: cached loads, 2 per CU; 5: nontemporal; 6: cached, 1 per CU);
-                                   // 7 = 5-slot ring, 2 per CU
+                                   // 7 = 5-slot ring, 2 per CU; 8 = two-tile wavefronts on
+                                   // alternate blocks, 5-slot ring advanced by pairs, 2 per CU
     int64_t dense_variant = 0;     // MFMA split: 0 = nontemporal K/V loads, 1 = cached loads,
                                    // 2 = two blocks ahead, 3 = nontemporal with two waves per SIMD
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads

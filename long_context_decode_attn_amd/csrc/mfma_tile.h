@@ -60,13 +60,14 @@ struct WaveState {
     float l[NT];
 };
 
-// valid: tokens of the block that exist (the rest are masked); col_ok: this
-// lane's query row (c16) sees the block at all (false masks every token).
+// valid: tokens of the block that exist (the rest are masked); col_ok: bit rt
+// set = this lane's query row (c16) of row tile rt sees the block at all (a
+// clear bit masks every token of that row).
 // The logits stay unscaled up to the exponent: the row max of s*scale is
 // scale times the max of s (scale > 0), and p = exp2(fma(s, scale, -m)).
 template <int NT>
 __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs& r, int valid, float scale, int j,
-                                              int c16, bool col_ok = true) {
+                                              int c16, int col_ok = -1) {
     // V operand: column n = c16 of d-block nb is d = 8*c16 + nb; k element e is token tok_of(j, e).
     bf16x8 vb[8];
 #pragma unroll
@@ -92,14 +93,16 @@ __device__ __forceinline__ void compute_block(WaveState<NT>& st, const BlockRegs
         }
     // Masking only where some token is missing or some row does not see the
     // block (a uniform branch around it).
-    if (__builtin_amdgcn_readfirstlane(valid) < kBlock || __ballot(!col_ok) != 0) {
+    constexpr int kAll = (1 << NT) - 1;
+    const int ok = col_ok & kAll;
+    if (__builtin_amdgcn_readfirstlane(valid) < kBlock || __ballot(ok != kAll) != 0) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (16 * tb + 4 * j + i >= valid || !col_ok) s[rt][tb][i] = -INFINITY;
+                    if (16 * tb + 4 * j + i >= valid || !((ok >> rt) & 1)) s[rt][tb][i] = -INFINITY;
     }
     float bm[NT];
     bool need = false;

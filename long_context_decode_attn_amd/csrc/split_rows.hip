@@ -50,58 +50,69 @@ constexpr int vmcnt_ring() {
     return 0x0F70 | (kPieces * (AHEAD - 1));
 }
 
-// Query fragments of a wavefront's 16 rows (row c16 of the tile) and a fresh state.
-__device__ __forceinline__ void load_rows_q(WaveState<1>& st, const SplitArgs& a, int rows_w, int bkv, int h, int j,
+// Query fragments of a wavefront's 16*NT rows (row c16 of each tile) and a fresh state.
+template <int NT>
+__device__ __forceinline__ void load_rows_q(WaveState<NT>& st, const SplitArgs& a, int rows_w, int bkv, int h, int j,
                                             int c16) {
-    const int r = rows_w + c16;
-    if (r < a.rows) {
-        const int b = a.shared ? r / a.G : bkv;
-        const int g = a.shared ? r % a.G : r;
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.G + g) * kD + 8 * j;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(ld16(qp + 32 * c));
-    } else {
+    for (int rt = 0; rt < NT; ++rt) {
+        const int r = rows_w + 16 * rt + c16;
+        if (r < a.rows) {
+            const int b = a.shared ? r / a.G : bkv;
+            const int g = a.shared ? r % a.G : r;
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.G + g) * kD + 8 * j;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) st.q[0][c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+            for (int c = 0; c < 4; ++c) st.q[rt][c] = as_bf16x8(ld16(qp + 32 * c));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) st.q[rt][c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) st.o[rt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m[rt] = kNoMax;
+        st.l[rt] = 0.f;
     }
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) st.o[0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m[0] = kNoMax;
-    st.l[0] = 0.f;
 }
 
-// A wavefront's 16 rows out: m per row c16 (shared by the lane groups), l summed
-// over them; o[nb][i] is row 4j + i, column 8*c16 + nb.  Direct: finished rows
-// (with the optional virtual pair); else the (row, split) partial state.
-__device__ __forceinline__ void write_rows(const WaveState<1>& st, const SplitArgs& a, int rows_w, int bkv, int h,
+// A wavefront's 16*NT rows out: per tile, m per row c16 (shared by the lane
+// groups), l summed over them; o[rt][nb][i] is row 16*rt + 4j + i, column
+// 8*c16 + nb.  Direct: finished rows (with the optional virtual pair); else the
+// (row, split) partial state.
+template <int NT>
+__device__ __forceinline__ void write_rows(const WaveState<NT>& st, const SplitArgs& a, int rows_w, int bkv, int h,
                                            int split, int j, int c16, int lane, bool direct) {
-    float l = st.l[0];
-    l = sum_xor32(sum_xor16(l));
-    const float m = st.m[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * j + i;
-        const int r = rows_w + rr;
-        const float M = __shfl(m, rr, 64);   // row rr's state lives in lane rr (j = 0)
-        const float L = __shfl(l, rr, 64);
-        if (r >= a.rows) continue;
-        const int b = a.shared ? r / a.G : bkv;
-        const int g = a.shared ? r % a.G : r;
-        const int64_t bhq = (int64_t)b * a.Hq + h * a.G + g;
-        if (direct) {
-            const bool virt = a.alpha_in != nullptr && a.alpha_in[bhq] > -INFINITY;
-            const float al = virt ? a.alpha_in[bhq] : -INFINITY;
+    for (int rt = 0; rt < NT; ++rt) {
+        float l = st.l[rt];
+        l = sum_xor32(sum_xor16(l));
+        const float m = st.m[rt];
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int c = 8 * c16 + nb;
-                finish_row(a, bhq, c, M, L, st.o[0][nb][i], virt, al, virt ? a.a_in[bhq * kD + c] : 0.f);
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * j + i;
+            const int r = rows_w + 16 * rt + rr;
+            const float M = __shfl(m, rr, 64);   // row rr's state lives in lane rr (j = 0)
+            const float L = __shfl(l, rr, 64);
+            if (r >= a.rows) continue;
+            const int b = a.shared ? r / a.G : bkv;
+            const int g = a.shared ? r % a.G : r;
+            const int64_t bhq = (int64_t)b * a.Hq + h * a.G + g;
+            if (direct) {
+                const bool virt = a.alpha_in != nullptr && a.alpha_in[bhq] > -INFINITY;
+                const float al = virt ? a.alpha_in[bhq] : -INFINITY;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) {
+                    const int c = 8 * c16 + nb;
+                    finish_row(a, bhq, c, M, L, st.o[rt][nb][i], virt, al, virt ? a.a_in[bhq * kD + c] : 0.f);
+                }
+            } else {
+                const int64_t slot = bhq * a.splits + split;
+                float* dst = a.acc + slot * kD + 8 * c16;
+                *reinterpret_cast<f32x4*>(dst) =
+                    f32x4{st.o[rt][0][i], st.o[rt][1][i], st.o[rt][2][i], st.o[rt][3][i]};
+                *reinterpret_cast<f32x4*>(dst + 4) =
+                    f32x4{st.o[rt][4][i], st.o[rt][5][i], st.o[rt][6][i], st.o[rt][7][i]};
+                if (c16 == 0) a.ml[slot] = make_float2(M, L);
             }
-        } else {
-            const int64_t slot = bhq * a.splits + split;
-            float* dst = a.acc + slot * kD + 8 * c16;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{st.o[0][0][i], st.o[0][1][i], st.o[0][2][i], st.o[0][3][i]};
-            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.o[0][4][i], st.o[0][5][i], st.o[0][6][i], st.o[0][7][i]};
-            if (c16 == 0) a.ml[slot] = make_float2(M, L);
         }
     }
 }
@@ -296,6 +307,181 @@ __global__ __launch_bounds__(64 * kWaves, WPE) void k_split_rows(SplitArgs a) {
     // last to gather quickly).
 }
 
+// ---- pair variant -------------------------------------------------------------
+// The 64 rows as two halves of 32 (two 16-row tiles per wavefront); the two
+// wavefronts of a half take alternate blocks (wavefront w: half w & 1, block
+// parity w >> 1), so every block is read back from LDS by two wavefronts
+// instead of four, and each wavefront's block chain carries two independent
+// tiles.  The ring advances by a pair of blocks per barrier: pair k (blocks 2k,
+// 2k + 1) is computed while blocks 2k + 2 .. 2k + 4 are in flight, in a ring
+// of five slots (block b in slot b % 5).  At the end the two wavefronts of a
+// half merge their states through LDS (exactly, by their maxima) and one of
+// them writes the half's rows.
+constexpr int kPairSlots = 5;
+constexpr int kPairRows = 32;
+
+// s_waitcnt vmcnt(kPieces): the pair's blocks have landed; the one younger
+// block may still be in flight.
+constexpr int vmcnt_pair() { return 0x0F70 | kPieces; }
+
+// Local blocks of a wavefront's 32 rows: as local_work, for the items of rows
+// rows_w .. rows_w + 31.
+__device__ __forceinline__ LocalWork local_work_rows(const SplitArgs& a, int rows_w, int nrows) {
+    LocalWork lw;
+    if (a.k2 == nullptr || a.n2 <= 0 || rows_w >= a.rows) return lw;
+    lw.i0 = rows_w / a.G;
+    const int i1 = (min(rows_w + nrows, a.rows) - 1) / a.G;
+    lw.nbl = (int)((a.n2 + kBlock - 1) / kBlock);
+    lw.count = (int64_t)(i1 - lw.i0 + 1) * lw.nbl;
+    return lw;
+}
+
+// One 16-row tile of a two-tile state through the one-tile block computation
+// (a local block that only one item's rows see, so at most the tiles holding
+// them run).
+template <int RT>
+__device__ __forceinline__ void compute_tile(WaveState<2>& st, const BlockRegs& r, int valid, float scale, int j,
+                                             int c16, bool ok) {
+    WaveState<1> t;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t.q[0][c] = st.q[RT][c];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) t.o[0][nb] = st.o[RT][nb];
+    t.m[0] = st.m[RT];
+    t.l[0] = st.l[RT];
+    compute_block<1>(t, r, valid, scale, j, c16, ok ? 1 : 0);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st.o[RT][nb] = t.o[0][nb];
+    st.m[RT] = t.m[0];
+    st.l[RT] = t.l[0];
+}
+
+template <bool NTL, bool DIRECT, bool LOCAL>
+__global__ __launch_bounds__(64 * kWaves, 2) void k_split_rows_pair(SplitArgs a) {
+    static_assert(kWaves == 4 && 2 * kPairRows == kRowsPerGroup, "two halves of two wavefronts");
+    __shared__ __attribute__((aligned(16))) char ring[kPairSlots][kSlotBytes];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = w & 1, par = w >> 1;
+    const int j = lane >> 4, c16 = lane & 15;
+    const uint32_t koff = 256u * c16 + 16u * j;
+    const uint32_t voff = 1024u * j + 16u * c16;
+    const int split = blockIdx.x, h = blockIdx.y;
+    const int bkv = blockIdx.z / a.row_groups, rg = blockIdx.z % a.row_groups;
+    const int rows_w = rg * kRowsPerGroup + kPairRows * half;   // this wavefront's first row
+
+    const int64_t n_eff = a.n_b ? min((int64_t)a.n_b[bkv], a.n) : a.n;
+    const int64_t head_off = (int64_t)bkv * a.kv_batch_stride + (int64_t)h * a.n * kD;
+    const uint16_t* kh = static_cast<const uint16_t*>(a.k) + head_off;
+    const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_off;
+    const int64_t t_begin = (int64_t)split * a.blocks_per_split * kBlock;
+    const int64_t t_end = min(n_eff, t_begin + (int64_t)a.blocks_per_split * kBlock);
+    const int nblk = t_end > t_begin ? (int)((t_end - t_begin + kBlock - 1) / kBlock) : 0;
+
+    // Local blocks of the half's items go to the 2 * splits wavefronts of the
+    // half in turn: wavefront (split, par) takes k = 2*split + par, then every
+    // 2 * splits-th.  The first one is requested with the query fragments and
+    // computed while the ring's first blocks are in flight, so no local block
+    // is held in registers across the document loop.
+    LocalWork lw;
+    BlockRegs lr;
+    int lvalid = 0;
+    const int64_t lfirst = 2 * (int64_t)split + par, lstep = 2 * (int64_t)a.splits;
+    if (LOCAL) {
+        lw = local_work_rows(a, rows_w, kPairRows);
+        if (lfirst < lw.count) lvalid = load_local_block<NTL>(lr, a, h, lw, lfirst, koff, voff);
+    }
+    WaveState<2> st;
+    load_rows_q(st, a, rows_w, bkv, h, j, c16);
+    wait_vm_all();   // only the ring's requests are outstanding from here on
+
+    // A local block k: only the tiles holding the item's rows run (the item's
+    // rows are consecutive, so this is uniform), with the other rows masked.
+    auto local_block = [&](int64_t k) {
+        if (lvalid <= 0) return;
+        const int item = lw.i0 + (int)(k / lw.nbl);
+        const int r0 = rows_w + c16, r1 = rows_w + 16 + c16;
+        const int first = item * a.G - rows_w, last = first + a.G - 1;
+        if (first < 16) compute_tile<0>(st, lr, lvalid, a.scale_log2, j, c16, r0 < a.rows && r0 / a.G == item);
+        if (last >= 16) compute_tile<1>(st, lr, lvalid, a.scale_log2, j, c16, r1 < a.rows && r1 / a.G == item);
+    };
+
+    const uint32_t lane_off = lds_addr(ring[0]) + 16 * lane;
+    if (nblk > 0) {
+#pragma unroll
+        for (int k = 0; k < kPairSlots - 2; ++k) {
+            const int kk = min(k, nblk - 1);
+            request_block<NTL>(ring[k], kh, vh, t_begin + (int64_t)kBlock * kk, n_eff, k < nblk, w, koff, voff);
+        }
+    }
+    if (LOCAL && lfirst < lw.count) local_block(lfirst);
+    if (nblk > 0) {
+        const int npairs = (nblk + 1) / 2;
+        for (int k = 0; k < npairs; ++k) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_pair());   // this wavefront's pieces of blocks 2k, 2k + 1
+            // Everyone's pieces of the pair have landed, and every wavefront has read pair k - 1.
+            __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {   // into the slots of pair k - 1
+                const int kn = 2 * k + kPairSlots - 2 + u;
+                request_block<NTL>(ring[kn % kPairSlots], kh, vh, t_begin + (int64_t)kBlock * min(kn, nblk - 1),
+                                   n_eff, kn < nblk, w, koff, voff);
+            }
+            const int kb = 2 * k + par;
+            if (kb < nblk) {
+                BlockRegs r;
+                read_block(r, lane_off + (kb % kPairSlots) * kSlotBytes);
+                const int64_t left = n_eff - (t_begin + (int64_t)kBlock * kb);
+                compute_block<2>(st, r, (int)(left < kBlock ? left : kBlock), a.scale_log2, j, c16);
+            }
+        }
+    }
+    wait_vm_all();   // the empty requests past the end
+
+    if (LOCAL) {
+        for (int64_t k = lfirst + lstep; k < lw.count; k += lstep) {
+            lvalid = load_local_block<NTL>(lr, a, h, lw, k, koff, voff);
+            wait_vm_all();
+            local_block(k);
+        }
+    }
+
+    // Merge the two block parities of each half: parity 1 leaves its state in
+    // the ring (no longer in use), parity 0 folds it into its own.
+    __builtin_amdgcn_s_barrier();   // every wavefront is done reading the ring
+    float* xo = reinterpret_cast<float*>(&ring[0][0]) + half * (2 * 8 * 4 * 64);   // [rt][nb][i][lane]
+    float2* xml = reinterpret_cast<float2*>(&ring[2][0]) + half * (2 * 64);          // [rt][lane]
+    if (par == 1) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xo[((rt * 8 + nb) * 4 + i) * 64 + lane] = st.o[rt][nb][i];
+            xml[rt * 64 + lane] = make_float2(st.m[rt], st.l[rt]);
+        }
+    }
+    __syncthreads();
+    if (par == 0) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const float2 o1 = xml[rt * 64 + lane];   // row c16's max and this lane's sum, parity 1
+            const float M = fmaxf(st.m[rt], o1.x);
+            const float w0 = fast_exp2(st.m[rt] - M), w1 = fast_exp2(o1.x - M);
+            st.m[rt] = M;
+            st.l[rt] = st.l[rt] * w0 + o1.y * w1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a0 = __shfl(w0, 4 * j + i, 64), a1 = __shfl(w1, 4 * j + i, 64);   // row 4j + i
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+                    st.o[rt][nb][i] = st.o[rt][nb][i] * a0 + xo[((rt * 8 + nb) * 4 + i) * 64 + lane] * a1;
+            }
+        }
+        write_rows(st, a, rows_w, bkv, h, split, j, c16, lane, DIRECT);
+    }
+}
+
 // ---- register variant ---------------------------------------------------------
 // The same split of rows over wavefronts, without LDS: every wavefront requests
 // the whole block into its own registers (buffer loads, one block ahead); the
@@ -352,6 +538,13 @@ int split_rows_per_group() { return kRowsPerGroup; }
 hipError_t launch_split_rows(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
     dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(64 * kWaves);
     const int variant = (int)tuning().rows_variant;
+    if (variant == 8) {   // two-tile wavefronts on alternate blocks
+        if (a.k2 != nullptr && a.direct) hipLaunchKernelGGL((k_split_rows_pair<true, true, true>), grid, block, 0, st, a);
+        else if (a.k2 != nullptr) hipLaunchKernelGGL((k_split_rows_pair<true, false, true>), grid, block, 0, st, a);
+        else if (a.direct) hipLaunchKernelGGL((k_split_rows_pair<true, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_split_rows_pair<true, false, false>), grid, block, 0, st, a);
+        return hipGetLastError();
+    }
     if (a.k2 != nullptr) {   // local tokens in the same pass: the default ring variant (or the 5-slot one)
         if (a.direct) hipLaunchKernelGGL((k_split_rows<4, true, 1, true, true>), grid, block, 0, st, a);
         else if (variant == 7) hipLaunchKernelGGL((k_split_rows<5, true, 2, false, true>), grid, block, 0, st, a);

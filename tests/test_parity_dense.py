@@ -61,7 +61,7 @@ def test_dense_shared_rows_kernel(orc, B, n):
     _dense_case(B, 8, 2, n, torch.bfloat16, 700 + B + n, shared=True, orc=orc)
 
 
-@pytest.mark.parametrize("variant", list(range(8)))
+@pytest.mark.parametrize("variant", list(range(9)))
 def test_dense_shared_rows_variants(orc, variant):
     """Every 64-row workgroup variant (LDS ring depths and occupancies, blocks in registers) gives the
     oracle's result, several blocks per workgroup and a ragged tail."""
@@ -249,6 +249,25 @@ def test_decode_step_shared_rows_local(orc, B, Hq, n, n_loc):
     """A shared document with more than 16 rows per KV head: the 64-row pass also takes each row's local
     tokens (blocks seen only by that item's rows), then one combine."""
     _step_case(orc, B, Hq, 2, n, max(n_loc), n_loc, torch.bfloat16, 1200 + B + n, shared=True)
+
+
+@pytest.mark.parametrize("variant", [0, 7, 8])
+def test_decode_step_shared_rows_local_variants(orc, variant):
+    """The shared-document step with local tokens through each ring variant that takes them: 64 and 80 rows,
+    ragged and empty local ranges, G = 3, several local blocks per wavefront, one split finished in place."""
+    old = ops.get_tuning("rows_variant")
+    ops.set_tuning("rows_variant", variant)
+    try:
+        _step_case(orc, 16, 8, 2, 3000, 512, [512] * 15 + [300], torch.bfloat16, 1300 + variant, shared=True)
+        _step_case(orc, 20, 8, 2, 5003, 300, [(37 * i) % 301 for i in range(20)], torch.bfloat16, 1310 + variant,
+                   shared=True)
+        _step_case(orc, 11, 6, 2, 2000, 130, [(53 * i) % 130 + 1 for i in range(11)], torch.bfloat16,
+                   1320 + variant, shared=True)
+        _step_case(orc, 16, 8, 2, 200, 700, [700] * 16, torch.bfloat16, 1330 + variant, shared=True)
+        _step_case(orc, 8, 8, 2, 20, 64, [64, 0, 33, 1, 64, 5, 31, 32], torch.bfloat16, 1340 + variant, shared=True)
+        _step_case(orc, 16, 8, 2, 61440 // 8 + 7, 512, [512] * 16, torch.bfloat16, 1350 + variant, shared=True)
+    finally:
+        ops.set_tuning("rows_variant", old)
 
 
 def test_decode_step_fallbacks(orc):
