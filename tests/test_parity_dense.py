@@ -99,6 +99,24 @@ def test_config3_reduced(orc):
     assert_close(out, alpha, mo, ma, torch.bfloat16, "config 3 reduced step")
 
 
+def test_config3_full_size_sampled(orc):
+    """One layer of config 3 at full size (shared 61,440-token document, 16 queries x 32 heads, 512
+    private local tokens each) through dense_decode_step, the call and launch shape the shared36
+    benchmark times; every row of three batch items against the oracle."""
+    cfg = synth.CONFIGS[3]
+    x = synth.make_inputs(cfg, device=DEV)
+    print("case config 3 full size n=%d B=%d" % (cfg.n, cfg.B), flush=True)
+    out, alpha = ops.dense_decode_step(x["q"], x["k"], x["v"], x["k_loc"], x["v_loc"], x["n_loc"])
+    torch.cuda.synchronize()
+    k, v = to_np(x["k"]), to_np(x["v"])
+    for b in (0, 7, 15):
+        q = to_np(x["q"][b:b + 1])
+        ro, ra = orc.dense_attn(q, k, v)
+        mo, ma = orc.merge_local(q, ro, ra, to_np(x["k_loc"][b:b + 1]), to_np(x["v_loc"][b:b + 1]),
+                                 to_np(x["n_loc"][b:b + 1]))
+        assert_close(out[b:b + 1], alpha[b:b + 1], mo, ma, torch.bfloat16, "config 3 full size b=%d" % b)
+
+
 def test_dense_fp32_shared_document(orc):
     _dense_case(3, 8, 2, 2000, torch.float32, 600, shared=True, orc=orc)
 

@@ -179,6 +179,27 @@ def test_config4_reduced_end_to_end(orc):
     assert_close(out, alpha, ro, ra, torch.bfloat16, "config 4 reduced")
 
 
+def test_config4_full_size(orc):
+    """Config 4 at full size (n = 131,072, B = 8, m = n/32 + 128 sink + 128 recent) as the sparse128k
+    benchmark runs it: indices and counts bit-exact for every query head; gather outputs of three
+    sampled (batch item, KV head) slices against the oracle."""
+    cfg = synth.CONFIGS[4]
+    x = synth.make_inputs(cfg, device=DEV)
+    G = cfg.Hq // cfg.Hkv
+    print("case config 4 full size n=%d B=%d m=%d" % (cfg.n, cfg.B, cfg.m), flush=True)
+    idx, cnt, _ = ops.sig_score_topk(x["key_sigs"], x["q_sigs"], cfg.m, cfg.n_sink, cfg.n_recent)
+    out, alpha = ops.gather_attn(x["q"], x["k"], x["v"], idx, cnt)
+    torch.cuda.synchronize()
+    ri, rc, _ = orc.sig_score_topk(sig_np(x["key_sigs"]), sig_np(x["q_sigs"]), cfg.m, cfg.n_sink, cfg.n_recent)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    for b, h in [(0, 0), (3, 5), (7, 7)]:
+        hs = slice(h * G, (h + 1) * G)
+        go, ga = orc.gather_attn(to_np(x["q"][b:b + 1, hs]), to_np(x["k"][b:b + 1, h:h + 1]),
+                                 to_np(x["v"][b:b + 1, h:h + 1]), ri[b:b + 1, hs], rc[b:b + 1, hs])
+        assert_close(out[b:b + 1, hs], alpha[b:b + 1, hs], go, ga, torch.bfloat16, "config 4 b=%d h=%d" % (b, h))
+
+
 def test_gather_clamps_out_of_range_entries(orc):
     """Regression: counts beyond cap (or negative) and positions outside [0, n) are clamped by the
     kernel (results for such rows are undefined, but nothing is read out of bounds); valid rows in
