@@ -209,6 +209,33 @@ def traffic_from_profile(name: str, algorithmic_bytes: int, kind: str = "split_m
         return None
 
 
+def hbm_context(nbytes: int = 4 << 30, reps: int = 5) -> dict:
+    """The box's streaming rates through plain torch kernels, as context for the roofline: a sum over
+    nbytes of float32 (reads nbytes) and a copy of nbytes / 2 (reads and writes it).  Not tuned probes,
+    so they bound the achievable rate from below."""
+    x = torch.ones(nbytes // 4, device="cuda")
+    y = torch.empty(nbytes // 8, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    t = Timer()
+    t.start()
+    for _ in range(reps):
+        x.sum()
+    ms_sum = t.stop_ms() / reps
+    src = x[: nbytes // 8]
+    y.copy_(src)
+    torch.cuda.synchronize()
+    t.start()
+    for _ in range(reps):
+        y.copy_(src)
+    ms_copy = t.stop_ms() / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return {"sum_read_tbps": nbytes / (ms_sum * 1e-3) / 1e12,
+            "copy_read_plus_write_tbps": nbytes / (ms_copy * 1e-3) / 1e12,
+            "bytes": nbytes, "note": "torch.sum and Tensor.copy_ over 4 GiB, event-timed"}
+
+
 def calibrate_copy(nbytes: int, reps: int) -> dict:
     """A plain device-to-device copy of known size (the counter calibration kernel)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -475,11 +502,13 @@ def bench_sigwidth(args, cfg):
 
 
 # -------------------------------------------------------------- CPU oracle ----
-def cpu_baseline_dense(cfg, seconds: float):
-    """The oracle (plain C, fp64) on the host's cores over whole decode steps of the same workload."""
+def cpu_baseline_dense(cfg, seconds: float, threads: int = 0, layers: int = 1):
+    """The oracle (plain C, fp64) on the host's cores (or `threads` of them) over decode steps of the same
+    workload; with layers > 1 each timed step is one layer (every layer has the same shape) and the rate
+    is scaled by the layer count."""
     from oracle import oracle as orc_mod
     orc = orc_mod.default()
-    orc.set_threads(os.cpu_count() or 1)
+    orc.set_threads(threads or os.cpu_count() or 1)
     x = synth.make_inputs(cfg, device="cpu")
 
     def np_(t):
@@ -496,9 +525,12 @@ def cpu_baseline_dense(cfg, seconds: float):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": cfg.B * steps / el, "unit": "queries/s", "cores": orc.get_threads(), "kind": "oracle",
-            "sample": "%d full decode step(s) of the same workload (cached_attn_lse + lse_merge_local "
-                      "definitions, fp64), %.1f s wall" % (steps, el)}
+    what = "full decode step(s)" if layers == 1 else "step(s) of one layer"
+    tail = "" if layers == 1 else "; the rate is divided by the %d layers of a decode step" % layers
+    return {"value": cfg.B * steps / (el * layers), "unit": "queries/s", "cores": orc.get_threads(),
+            "kind": "oracle",
+            "sample": "%d %s of the same workload (cached_attn_lse + lse_merge_local definitions, fp64), "
+                      "%.1f s wall%s" % (steps, what, el, tail)}
 
 
 def cpu_baseline_quadrature(cfg, seconds: float, B: int = 4):
@@ -609,7 +641,13 @@ def main():
             sres["step_frac_of_peak"] = sres["step_tbps"] * 1e12 / HBM_PEAK
             line["sparse"] = sres
         if args.cpu_seconds > 0:
-            line["cpu_baseline"] = cpu_baseline_dense(cfg if layers == 1 else synth.CONFIGS[2], args.cpu_seconds)
+            line["cpu_baseline"] = cpu_baseline_dense(cfg, args.cpu_seconds, layers=layers)
+            if args.workload == "dense61k":
+                one = cpu_baseline_dense(cfg, max(1.0, args.cpu_seconds / 4), threads=1)
+                line["cpu_baseline_one_thread"] = {"value": one["value"], "unit": one["unit"],
+                                                   "cores": one["cores"], "sample": one["sample"]}
+        if args.workload == "dense61k":
+            line["hbm_context"] = hbm_context()
     elif args.workload == "sparse128k":
         cfg = synth.CONFIGS[4]
         res, _ = bench_sparse(args, cfg)
