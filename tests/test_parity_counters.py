@@ -162,3 +162,52 @@ def test_graph_replays_match_eager():
         ops.dense_decode_step(q, k, v, kl, vl, out=ref_o, alpha_out=ref_a, ws=ws_ref)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(alpha, ref_a), "replay %d differs from the eager call" % r
+
+
+def test_graph_replays_match_eager_shared_document(orc):
+    """The shared-document decode step (64-row pass with local tokens, then the combine), captured once and
+    replayed with new inputs and eager calls of other shapes on the same workspace in between: every
+    replay equals an eager call bit for bit, and the last one matches the oracle."""
+    B, Hq, Hkv, n, nl = 16, 32, 8, 5003, 300
+    g0 = torch.Generator().manual_seed(95)
+    q = torch.randn((B, Hq, 128), generator=g0).to(torch.bfloat16).to(DEV)
+    k = torch.randn((1, Hkv, n, 128), generator=g0).to(torch.bfloat16).to(DEV)
+    v = torch.randn((1, Hkv, n, 128), generator=g0).to(torch.bfloat16).to(DEV)
+    kl = torch.randn((B, Hkv, nl, 128), generator=g0).to(torch.bfloat16).to(DEV)
+    vl = torch.randn((B, Hkv, nl, 128), generator=g0).to(torch.bfloat16).to(DEV)
+    n_loc = torch.tensor([(37 * i) % (nl + 1) for i in range(B)], dtype=torch.int32, device=DEV)
+    nb = ops.ws_bytes_dense_decode_step(B, Hq, Hkv, 128, n, 0, nl)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ws_ref = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, 128), device=DEV)
+    alpha = torch.empty((B, Hq), device=DEV)
+    ref_o = torch.empty_like(out)
+    ref_a = torch.empty_like(alpha)
+
+    def step():
+        ops.dense_decode_step(q, k, v, kl, vl, n_loc, out=out, alpha_out=alpha, ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=DEV).manual_seed(96)
+    for r in range(4):
+        print("case shared-document graph replay %d" % r, flush=True)
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+        kl[:, :, : 32 * (r + 1)] = torch.randn((B, Hkv, 32 * (r + 1), 128), generator=gen, device=DEV).to(kl.dtype)
+        k[:, :, : 64 * (r + 1)] = torch.randn((1, Hkv, 64 * (r + 1), 128), generator=gen, device=DEV).to(k.dtype)
+        ops.cached_attn_lse(q[:4, :8].contiguous(), k[:, :2, :3000].contiguous(), v[:, :2, :3000].contiguous(), ws=ws)
+        g.replay()
+        ops.dense_decode_step(q, k, v, kl, vl, n_loc, out=ref_o, alpha_out=ref_a, ws=ws_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(alpha, ref_a), "replay %d differs from the eager call" % r
+    ro, ra = orc.dense_attn(to_np(q), to_np(k), to_np(v))
+    mo, ma = orc.merge_local(to_np(q), ro, ra, to_np(kl), to_np(vl), to_np(n_loc))
+    assert_close(out, alpha, mo, ma, torch.bfloat16, "shared-document replay vs oracle")
