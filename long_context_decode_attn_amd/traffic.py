@@ -21,17 +21,22 @@ def doc_kv_state_bytes(n: int, layers: int, kv_heads: int, d: int, elem_bytes: i
 
 
 def dense_step_bytes(B: int, Hq: int, Hkv: int, d: int, n: int, elem_bytes: int,
-                     shared_doc: bool = False, n_loc_total: int = 0) -> int:
+                     shared_doc: bool = False, n_loc_total: int = 0, fused: bool = False) -> int:
     """cached_attn_lse (+ lse_merge_local) for one layer.
 
-    n_loc_total: sum over batch items of the local tokens merged (0: no merge)."""
+    n_loc_total: sum over batch items of the local tokens merged (0: no merge).
+    fused: the two as one call (dense_decode_step), which reads q once and
+    writes only the merged out and alpha; the two-call form also writes A and
+    alpha and reads them and q again."""
     Bkv = 1 if shared_doc else B
     kv = 2 * Bkv * Hkv * n * d * elem_bytes
     loc = 2 * Hkv * n_loc_total * d * elem_bytes
     q = B * Hq * d * elem_bytes
-    out = B * Hq * (d + 1) * 4                      # A and alpha, fp32
-    merged = B * Hq * (d + 1) * 4 if n_loc_total else 0
-    merge_in = B * Hq * (d + 1) * 4 + B * Hq * d * elem_bytes if n_loc_total else 0
+    out = B * Hq * (d + 1) * 4                      # A and alpha (or out and alpha), fp32
+    if fused or not n_loc_total:
+        return kv + loc + q + out
+    merged = B * Hq * (d + 1) * 4
+    merge_in = B * Hq * (d + 1) * 4 + B * Hq * d * elem_bytes
     return kv + loc + q + out + merged + merge_in
 
 
