@@ -212,6 +212,45 @@ __device__ __forceinline__ bool arrive_last(const Args& a, int64_t unit, int* s_
     return arrive_count(a.ctr + unit, (uint32_t)a.splits, s_flag);
 }
 
+// Exactly kFewSplits splits (the split count of a full-chip launch over one
+// batch item's 8 KV heads): every load of the row (its (m, l) pairs, its
+// partial vectors and the virtual pair) is requested at once, at offsets
+// known at compile time, so the merge waits for one memory round trip; the
+// sums run in the same order as in combine_row's general loop.
+constexpr int kFewSplits = 32;
+
+template <class Args>
+__device__ __forceinline__ void combine_row_few(const Args& a, int64_t bhq, int lane) {
+    const int S = a.splits;
+    const float* ml = reinterpret_cast<const float*>(a.ml + bhq * S);
+    const float* acc = a.acc + bhq * S * kD + 2 * lane;
+    const f32x2 x = load_dev2(ml + 2 * (lane & (kFewSplits - 1)));   // lanes at or past S are ignored
+    f32x2 v[kFewSplits];
+#pragma unroll
+    for (int s = 0; s < kFewSplits; ++s) v[s] = load_dev2(acc + s * kD);
+    const float al_in = a.alpha_in != nullptr ? a.alpha_in[bhq] : -INFINITY;
+    const f32x2 a_in = a.alpha_in != nullptr ? *reinterpret_cast<const f32x2*>(a.a_in + bhq * kD + 2 * lane)
+                                             : f32x2{0.f, 0.f};
+    const bool has = lane < S && x.y > 0.f;
+    const bool virt = al_in > -INFINITY;
+    if (!__any(has) && !virt) {
+        *reinterpret_cast<f32x2*>(a.out + bhq * kD + 2 * lane) = f32x2{0.f, 0.f};
+        if (a.alpha && lane == 0) a.alpha[bhq] = -INFINITY;
+        return;
+    }
+    const float mv = virt ? al_in * kLog2e : kNoMax;
+    const float M = fmaxf(wave_max(has ? x.x : kNoMax), mv);
+    const float w = has ? fast_exp2(x.x - M) : 0.f;
+    f32x2 o = {0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kFewSplits; ++s) o += __shfl(w, s, 64) * v[s];   // split s's weight, in vector registers
+    const float wv = virt ? fast_exp2(mv - M) : 0.f;
+    const float L = wave_sum(w * x.y) + wv;
+    if (virt) o += wv * a_in;
+    *reinterpret_cast<f32x2*>(a.out + bhq * kD + 2 * lane) = o * (1.f / L);
+    if (a.alpha && lane == 0) a.alpha[bhq] = (M + log2f(L)) * kLn2;
+}
+
 // One wave merges the a.splits partial states of query row bhq (and the
 // optional virtual pair (a_in, alpha_in)) into out / alpha, as the combine
 // pass does: M = max m_s, L = sum l_s 2^(m_s - M), A = sum acc_s 2^(m_s - M) / L.
@@ -220,6 +259,10 @@ __device__ __forceinline__ bool arrive_last(const Args& a, int64_t unit, int* s_
 template <class Args>
 __device__ __forceinline__ void combine_row(const Args& a, int64_t bhq, int lane) {
     const int S = a.splits;
+    if (S == kFewSplits) {
+        combine_row_few(a, bhq, lane);
+        return;
+    }
     const float* ml = reinterpret_cast<const float*>(a.ml + bhq * S);
     const float* acc = a.acc + bhq * S * kD + 2 * lane;
     float mloc = kNoMax;
