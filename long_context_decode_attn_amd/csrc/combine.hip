@@ -10,7 +10,8 @@
 // of Eq. (3.4), which makes the same kernel the local-token merge.
 //
 // One workgroup of 256 threads per query row: the slot weights are computed
-// once into LDS, then 8 slot groups x 32 threads x 4 columns read the partial
+// once into LDS (maxima and sums reduced in each wavefront, then across the
+// four through LDS), then 8 slot groups x 32 threads x 4 columns read the partial
 // vectors with independent 16-byte loads and are summed through LDS.
 
 #include "common.h"
@@ -23,13 +24,13 @@ constexpr int kThreads = 256;
 constexpr int kGroups = kThreads / 32;   // slot groups; 32 threads x float4 cover d = 128
 
 __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
+    constexpr int kW = kThreads / 64;
     __shared__ float s_w[1024];
-    __shared__ float s_red[kThreads];
+    __shared__ float s_red[2][kW];   // per-wavefront max, then per-wavefront sum
+    __shared__ int s_anyw[kW];
     __shared__ f32x4 s_acc[kGroups][32];
-    __shared__ float s_M, s_L;
-    __shared__ int s_any;
     const int row = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6;
     const int S = a.slots;
     const float2* ml = a.ml + (int64_t)row * S;
 
@@ -58,17 +59,23 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
             anyloc = 1;
         }
     }
-    s_red[tid] = mloc;
-    if (tid == 0) s_any = 0;
-    __syncthreads();
-    if (anyloc) s_any = 1;
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-        if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
-        __syncthreads();
+    // Wavefront reductions, then one exchange of the kW wavefront values.
+    mloc = wave_max(mloc);
+    const bool anyw = __any(anyloc) != 0;
+    if (lane == 0) {
+        s_red[0][wv_id] = mloc;
+        s_anyw[wv_id] = anyw ? 1 : 0;
     }
-    const bool any = s_any || virt;
-    const float M = fmaxf(s_red[0], virt ? mv : kNoMax);
     __syncthreads();
+    float Mw = s_red[0][0];
+    int anyall = s_anyw[0];
+#pragma unroll
+    for (int k = 1; k < kW; ++k) {
+        Mw = fmaxf(Mw, s_red[0][k]);
+        anyall |= s_anyw[k];
+    }
+    const bool any = anyall != 0 || virt;
+    const float M = fmaxf(Mw, virt ? mv : kNoMax);
     if (!any) {
         if (tid < kD) a.out[(int64_t)row * kD + tid] = 0.f;
         if (a.alpha && tid == 0) a.alpha[row] = -INFINITY;
@@ -82,14 +89,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
         if (s < 1024) s_w[s] = w;
         lloc += w * x.y;
     }
-    s_red[tid] = lloc;
-    __syncthreads();
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-        if (tid < o) s_red[tid] += s_red[tid + o];
-        __syncthreads();
-    }
+    lloc = wave_sum(lloc);
+    if (lane == 0) s_red[1][wv_id] = lloc;
+    __syncthreads();   // also publishes s_w
+    float Ls = 0.f;
+#pragma unroll
+    for (int k = 0; k < kW; ++k) Ls += s_red[1][k];
     const float wv = virt ? fast_exp2(mv - M) : 0.f;
-    const float L = s_red[0] + wv;
+    const float L = Ls + wv;
 
     // Weighted sum of the partial vectors: thread (group g, lane c4) owns columns 4*c4..4*c4+3.
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
