@@ -34,8 +34,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
     const int S = a.slots;
     const float2* ml = a.ml + (int64_t)row * S;
 
-    const bool virt = a.alpha_in != nullptr && a.alpha_in[row] > -INFINITY;
-    const float mv = virt ? a.alpha_in[row] * kLog2e : kNoMax;
+    const float al_in = a.alpha_in != nullptr ? a.alpha_in[row] : -INFINITY;   // one load, requested first
+    const bool virt = al_in > -INFINITY;
+    const float mv = virt ? al_in * kLog2e : kNoMax;
 
     // Request the first kPre slots of each group's partial vectors before
     // anything else; the weights are computed while they are in flight.
@@ -49,10 +50,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
         pre[k] = *reinterpret_cast<const f32x4*>(acc + (int64_t)min(s, S - 1) * kD);   // clamped; unused if s >= S
     }
 
-    // M over non-empty slots (and the virtual pair).
-    float mloc = kNoMax;
-    int anyloc = 0;
-    for (int s = tid; s < S; s += kThreads) {
+    // M over non-empty slots (and the virtual pair).  A thread's first slot
+    // state stays in registers for the weights below (with at most kThreads
+    // slots it is the thread's only one).
+    const float2 x0 = tid < S ? ml[tid] : make_float2(kNoMax, 0.f);
+    float mloc = x0.y > 0.f ? x0.x : kNoMax;
+    int anyloc = x0.y > 0.f ? 1 : 0;
+    for (int s = tid + kThreads; s < S; s += kThreads) {
         const float2 x = ml[s];
         if (x.y > 0.f) {
             mloc = fmaxf(mloc, x.x);
@@ -83,7 +87,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
     }
     // Slot weights w_s = 2^(m_s - M) (0 for empty slots) and L.
     float lloc = 0.f;
-    for (int s = tid; s < S; s += kThreads) {
+    if (tid < S) {
+        const float w = x0.y > 0.f ? fast_exp2(x0.x - M) : 0.f;
+        if (tid < 1024) s_w[tid] = w;
+        lloc = w * x0.y;
+    }
+    for (int s = tid + kThreads; s < S; s += kThreads) {
         const float2 x = ml[s];
         const float w = x.y > 0.f ? fast_exp2(x.x - M) : 0.f;
         if (s < 1024) s_w[s] = w;
