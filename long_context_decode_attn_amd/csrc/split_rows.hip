@@ -380,30 +380,33 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_split_rows_pair(SplitArgs a)
 
     // Local blocks of the half's items go to the 2 * splits wavefronts of the
     // half in turn: wavefront (split, par) takes k = 2*split + par, then every
-    // 2 * splits-th.  The first one is requested with the query fragments and
-    // computed while the ring's first blocks are in flight, so no local block
-    // is held in registers across the document loop.
+    // 2 * splits-th.  The first two are requested with the query fragments and
+    // computed while the ring's first blocks are in flight (the registers of
+    // two blocks fit before the document loop, not across it); any further
+    // ones run after the loop.
     LocalWork lw;
-    BlockRegs lr;
-    int lvalid = 0;
+    BlockRegs lr, lr2;
+    int lvalid = 0, lvalid2 = 0;
     const int64_t lfirst = 2 * (int64_t)split + par, lstep = 2 * (int64_t)a.splits;
     if (LOCAL) {
         lw = local_work_rows(a, rows_w, kPairRows);
         if (lfirst < lw.count) lvalid = load_local_block<NTL>(lr, a, h, lw, lfirst, koff, voff);
+        if (lfirst + lstep < lw.count) lvalid2 = load_local_block<NTL>(lr2, a, h, lw, lfirst + lstep, koff, voff);
     }
     WaveState<2> st;
     load_rows_q(st, a, rows_w, bkv, h, j, c16);
     wait_vm_all();   // only the ring's requests are outstanding from here on
 
-    // A local block k: only the tiles holding the item's rows run (the item's
-    // rows are consecutive, so this is uniform), with the other rows masked.
-    auto local_block = [&](int64_t k) {
-        if (lvalid <= 0) return;
+    // A local block k (in registers r, valid rows v): only the tiles holding
+    // the item's rows run (the item's rows are consecutive, so this is
+    // uniform), with the other rows masked.
+    auto local_block = [&](int64_t k, const BlockRegs& r, int v) {
+        if (v <= 0) return;
         const int item = lw.i0 + (int)(k / lw.nbl);
         const int r0 = rows_w + c16, r1 = rows_w + 16 + c16;
         const int first = item * a.G - rows_w, last = first + a.G - 1;
-        if (first < 16) compute_tile<0>(st, lr, lvalid, a.scale_log2, j, c16, r0 < a.rows && r0 / a.G == item);
-        if (last >= 16) compute_tile<1>(st, lr, lvalid, a.scale_log2, j, c16, r1 < a.rows && r1 / a.G == item);
+        if (first < 16) compute_tile<0>(st, r, v, a.scale_log2, j, c16, r0 < a.rows && r0 / a.G == item);
+        if (last >= 16) compute_tile<1>(st, r, v, a.scale_log2, j, c16, r1 < a.rows && r1 / a.G == item);
     };
 
     const uint32_t lane_off = lds_addr(ring[0]) + 16 * lane;
@@ -414,7 +417,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_split_rows_pair(SplitArgs a)
             request_block<NTL>(ring[k], kh, vh, t_begin + (int64_t)kBlock * kk, n_eff, k < nblk, w, koff, voff);
         }
     }
-    if (LOCAL && lfirst < lw.count) local_block(lfirst);
+    if (LOCAL && lfirst < lw.count) local_block(lfirst, lr, lvalid);
+    if (LOCAL && lfirst + lstep < lw.count) local_block(lfirst + lstep, lr2, lvalid2);
     if (nblk > 0) {
         const int npairs = (nblk + 1) / 2;
         for (int k = 0; k < npairs; ++k) {
@@ -439,10 +443,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_split_rows_pair(SplitArgs a)
     wait_vm_all();   // the empty requests past the end
 
     if (LOCAL) {
-        for (int64_t k = lfirst + lstep; k < lw.count; k += lstep) {
+        for (int64_t k = lfirst + 2 * lstep; k < lw.count; k += lstep) {
             lvalid = load_local_block<NTL>(lr, a, h, lw, k, koff, voff);
             wait_vm_all();
-            local_block(k);
+            local_block(k, lr, lvalid);
         }
     }
 
