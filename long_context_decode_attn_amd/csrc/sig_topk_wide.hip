@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kWThreads = 1024;
 constexpr int kWWaves = kWThreads / 64;
-constexpr int kWMaxBins = 16 * 32 + 1;
 constexpr int kWPer = 16;                       // positions per thread and tile
 constexpr int kWTile = kWThreads * kWPer;
 
