@@ -354,7 +354,8 @@ def bench_sparse(args, cfg, rot=None):
         "gather_bytes": gather_bytes,
         "rotations": rot,
     }
-    res["t_map"] = bench_tmap(args, sets, cfg)
+    if args.tmap:
+        res["t_map"] = bench_tmap(args, sets, cfg)
     return res, sets[0]
 
 
@@ -596,6 +597,8 @@ def main():
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
                     help="skip the sparse-path measurement that rides along with the dense61k line")
+    ap.add_argument("--no-tmap", dest="tmap", action="store_false",
+                    help="skip the T_map timings that ride along with the sparse measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (--steps times), for counter calibration")
