@@ -221,6 +221,28 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
                       float* out, float* alpha_out, float* a_doc, float* alpha_doc,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* dense_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partial states and arrival counters
+ * live in a static device array of the library, one per GPU, held until the
+ * process ends: lcda_noalloc_scratch_bytes() bytes of workspace proper plus a
+ * separate region for the counters.  The call allocates nothing.
+ *
+ *   arguments as in dense_decode_step, without a_doc, alpha_doc, ws, ws_bytes;
+ *   stream must belong to the current device.
+ * Errors: LCDA_EUNSUPPORTED when B*Hq exceeds 8192 query rows, or when
+ * lcda_ws_bytes_dense_decode_step for the shapes exceeds
+ * lcda_noalloc_scratch_bytes() (16 MiB less the counters: a 61,440-token
+ * shared document read by 16 items of 32 query heads needs 8.5 MB); the other
+ * errors of dense_decode_step.  Every call on a GPU uses that GPU's one array:
+ * calls that can overlap on one GPU (work on concurrent streams) race and
+ * must not be issued. */
+int dense_decode_step_noalloc(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,
+                              const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max,
+                              int B, int Hq, int Hkv, int d, int dtype,
+                              float* out, float* alpha_out, void* stream);
+size_t lcda_noalloc_scratch_bytes(void);
+
 /* Workspace bytes each call needs for the given shapes (0 on invalid shapes). */
 size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n,
                                      int64_t kv_batch_stride);

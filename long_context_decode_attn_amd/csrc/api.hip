@@ -27,6 +27,19 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
+}  // namespace
+
+// The same, for the library's other source files.
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -75,14 +88,27 @@ struct PartialLayout {
     size_t ctr_off, ml_off, acc_off, bytes;
 };
 
-PartialLayout partial_layout(int B, int Hq, int splits) {
+PartialLayout partial_layout(int B, int Hq, int splits, bool own_ctr = true) {
     PartialLayout l;
     const size_t slots = (size_t)B * Hq * splits;
     l.ctr_off = 0;
-    l.ml_off = round_up((size_t)B * Hq * sizeof(unsigned long long));
+    l.ml_off = own_ctr ? round_up((size_t)B * Hq * sizeof(unsigned long long)) : 0;
     l.acc_off = l.ml_off + round_up(slots * sizeof(float2));
     l.bytes = l.acc_off + round_up(slots * kD * sizeof(float));
     return l;
+}
+
+// Where a call's scratch memory lives: the workspace (bytes at ws), and the
+// arrival counters either at the start of it (ctr == null) or in a region of
+// their own that holds nothing else.
+struct Scratch {
+    void* ws;
+    size_t bytes;
+    unsigned long long* ctr;
+};
+
+unsigned long long* counters_at(const Scratch& s, const PartialLayout& l) {
+    return s.ctr ? s.ctr : reinterpret_cast<unsigned long long*>(static_cast<char*>(s.ws) + l.ctr_off);
 }
 
 #define RETURN_IF(x)          \
@@ -193,7 +219,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.grid_z = bkv * p.row_groups;
     } else {
         p.kernel = kValu;
-        p.rows_per_group = rows >= 3 ? 4 : rows;
+        p.rows_per_group = rows >= 3 ? 4 : (rows > 0 ? rows : 1);
         p.nt = p.rows_per_group;
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = valu_step_tokens();
@@ -299,10 +325,12 @@ size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap) {
     return partial_layout(B, Hq, p.splits).bytes;
 }
 
-int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int d, int64_t n,
-                    int64_t kv_batch_stride, int dtype, float* out, float* alpha, void* ws, size_t ws_bytes,
-                    void* stream) {
+static int cached_attn_lse_impl(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int d,
+                                int64_t n, int64_t kv_batch_stride, int dtype, float* out, float* alpha,
+                                const Scratch& sc, void* stream) {
     static const char* fn = "cached_attn_lse";
+    void* ws = sc.ws;
+    const size_t ws_bytes = sc.bytes;
     RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
     RETURN_IF(check_dtype(fn, dtype));
     RETURN_IF(check_n(fn, "n", n));
@@ -316,7 +344,7 @@ int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, 
     RETURN_IF(check_ptr(fn, "ws", ws, false));
     const bool shared = kv_batch_stride == 0;
     const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n, shared);
-    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits, sc.ctr == nullptr);
     if (!work) return LCDA_OK;
     if (!ws || ws_bytes < lay.bytes)
         return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
@@ -338,16 +366,25 @@ int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, 
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
-    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
+    a.ctr = counters_at(sc, lay);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(fn, p, a, dtype, B * Hq, out, alpha, nullptr, nullptr, st);
 }
 
-int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, const void* k_loc,
-                    const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq, int Hkv, int d,
-                    int dtype, float* out, float* alpha_out, void* ws, size_t ws_bytes, void* stream) {
+int cached_attn_lse(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int d, int64_t n,
+                    int64_t kv_batch_stride, int dtype, float* out, float* alpha, void* ws, size_t ws_bytes,
+                    void* stream) {
+    return cached_attn_lse_impl(q, k, v, B, Hq, Hkv, d, n, kv_batch_stride, dtype, out, alpha,
+                                Scratch{ws, ws_bytes, nullptr}, stream);
+}
+
+static int lse_merge_local_impl(const void* q, const float* a_in, const float* alpha_in, const void* k_loc,
+                                const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq, int Hkv,
+                                int d, int dtype, float* out, float* alpha_out, const Scratch& sc, void* stream) {
     static const char* fn = "lse_merge_local";
+    void* ws = sc.ws;
+    const size_t ws_bytes = sc.bytes;
     RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
     RETURN_IF(check_dtype(fn, dtype));
     RETURN_IF(check_n(fn, "n_loc_max", n_loc_max));
@@ -363,7 +400,7 @@ int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, con
     RETURN_IF(check_ptr(fn, "ws", ws, false));
     if (work && (const void*)out == (const void*)a_in) return fail(LCDA_EINVAL, "%s: out aliases a_in", fn);
     const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n_loc_max, false);
-    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits, sc.ctr == nullptr);
     if (!work) return LCDA_OK;
     if (!ws || ws_bytes < lay.bytes)
         return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, lay.bytes);
@@ -386,10 +423,17 @@ int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, con
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
-    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
+    a.ctr = counters_at(sc, lay);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(fn, p, a, dtype, B * Hq, out, alpha_out, a_in, alpha_in, st);
+}
+
+int lse_merge_local(const void* q, const float* a_in, const float* alpha_in, const void* k_loc,
+                    const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq, int Hkv, int d,
+                    int dtype, float* out, float* alpha_out, void* ws, size_t ws_bytes, void* stream) {
+    return lse_merge_local_impl(q, a_in, alpha_in, k_loc, v_loc, n_loc, n_loc_max, B, Hq, Hkv, d, dtype, out,
+                                alpha_out, Scratch{ws, ws_bytes, nullptr}, stream);
 }
 
 // Fused decode step: one split pass over the unified token range (cache, then
@@ -411,11 +455,16 @@ size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n,
     return two > fused ? two : fused;
 }
 
-int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,
-                      const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq,
-                      int Hkv, int d, int dtype, float* out, float* alpha_out, float* a_doc, float* alpha_doc,
-                      void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace lcda {
+
+int dense_decode_step_impl(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,
+                           const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B,
+                           int Hq, int Hkv, int d, int dtype, float* out, float* alpha_out, float* a_doc,
+                           float* alpha_doc, void* ws, size_t ws_bytes, unsigned long long* ctr, void* stream) {
     static const char* fn = "dense_decode_step";
+    const Scratch sc{ws, ws_bytes, ctr};
     RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
     RETURN_IF(check_dtype(fn, dtype));
     RETURN_IF(check_n(fn, "n", n));
@@ -447,7 +496,7 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
         // combine.
         const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n, true);
         if (p.kernel == kRows) {
-            const PartialLayout lay = partial_layout(B, Hq, p.splits);
+            const PartialLayout lay = partial_layout(B, Hq, p.splits, ctr == nullptr);
             SplitArgs a{};
             a.q = q;
             a.k = k;
@@ -470,7 +519,7 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
             a.blocks_per_split = p.blocks_per_split;
             a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
             a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
-            a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
+            a.ctr = counters_at(sc, lay);
             a.scale_log2 = kLog2e / sqrtf((float)kD);
             return finish(fn, p, a, dtype, B * Hq, out, alpha_out, nullptr, nullptr,
                           static_cast<hipStream_t>(stream));
@@ -487,12 +536,13 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
             A = reinterpret_cast<float*>(w + w1 + w2);
             al = A + (size_t)B * Hq * kD;
         }
-        RETURN_IF(cached_attn_lse(q, k, v, B, Hq, Hkv, d, n, kv_batch_stride, dtype, A, al, w, w1, stream));
-        return lse_merge_local(q, A, al, k_loc, v_loc, n_loc, n_loc_max, B, Hq, Hkv, d, dtype, out, alpha_out,
-                               w + w1, w2, stream);
+        RETURN_IF(cached_attn_lse_impl(q, k, v, B, Hq, Hkv, d, n, kv_batch_stride, dtype, A, al,
+                                       Scratch{w, w1, ctr}, stream));
+        return lse_merge_local_impl(q, A, al, k_loc, v_loc, n_loc, n_loc_max, B, Hq, Hkv, d, dtype, out, alpha_out,
+                                    Scratch{w + w1, w2, ctr}, stream);
     }
     const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, fused_tokens(n, n_loc_max), false);
-    const PartialLayout lay = partial_layout(B, Hq, p.splits);
+    const PartialLayout lay = partial_layout(B, Hq, p.splits, ctr == nullptr);
     SplitArgs a{};
     a.q = q;
     a.k = k;
@@ -516,9 +566,21 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
     a.blocks_per_split = p.blocks_per_split;
     a.ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.ml_off);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.acc_off);
-    a.ctr = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lay.ctr_off);
+    a.ctr = counters_at(sc, lay);
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     return finish(fn, p, a, dtype, B * Hq, out, alpha_out, nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace lcda
+
+extern "C" {
+
+int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_batch_stride, int64_t n,
+                      const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B, int Hq,
+                      int Hkv, int d, int dtype, float* out, float* alpha_out, float* a_doc, float* alpha_doc,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return dense_decode_step_impl(q, k, v, kv_batch_stride, n, k_loc, v_loc, n_loc, n_loc_max, B, Hq, Hkv, d, dtype,
+                                  out, alpha_out, a_doc, alpha_doc, ws, ws_bytes, nullptr, stream);
 }
 
 // sig_score_topk and sig_score_topk_q.  enc: q, R and bits are given, and the

@@ -53,6 +53,11 @@ struct SplitArgs {
     const float* alpha_in;      // [B, Hq] or null
 };
 
+// The scratch array of dense_decode_step_noalloc: at most this many query
+// rows (B * Hq), and this many bytes in all (arrival counters included).
+constexpr int kNoallocMaxRows = 8192;
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+
 // Launch-shape knobs (process-wide; see lcda_set_tuning).
 struct Tuning {
     int64_t dense_wgs = 256;       // target workgroups, MFMA split with 16/32-row tiles

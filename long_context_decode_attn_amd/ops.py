@@ -25,7 +25,8 @@ EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn"
            "lcda_ws_bytes_sig_score_topk", "lcda_ws_bytes_gather_attn",
            "lcda_last_error", "lcda_version", "lcda_set_tuning", "lcda_get_tuning",
            "dense_decode_step", "lcda_ws_bytes_dense_decode_step", "sig_encode", "sig_score_topk_q",
-           "sig_score_topk_w", "lcda_ws_bytes_sig_score_topk_w")
+           "sig_score_topk_w", "lcda_ws_bytes_sig_score_topk_w", "dense_decode_step_noalloc",
+           "lcda_noalloc_scratch_bytes")
 
 _lib = None
 
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH):
     lib.dense_decode_step.restype = ctypes.c_int
     lib.lcda_ws_bytes_dense_decode_step.argtypes = [i32, i32, i32, i32, i64, i64, i64]
     lib.lcda_ws_bytes_dense_decode_step.restype = ctypes.c_size_t
+    lib.dense_decode_step_noalloc.argtypes = [P, P, P, i64, i64, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P]
+    lib.dense_decode_step_noalloc.restype = ctypes.c_int
+    lib.lcda_noalloc_scratch_bytes.argtypes = []
+    lib.lcda_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.lcda_set_tuning.argtypes = [ctypes.c_char_p, i64]
     lib.lcda_set_tuning.restype = ctypes.c_int
     lib.lcda_get_tuning.argtypes = [ctypes.c_char_p]
@@ -222,6 +227,33 @@ def dense_decode_step(q, k, v, k_loc, v_loc, n_loc=None, out=None, alpha_out=Non
                                w.numel() * w.element_size(), _stream(q.device))
     _check("dense_decode_step", st)
     return out, alpha_out
+
+
+def dense_decode_step_noalloc(q, k, v, k_loc, v_loc, n_loc=None, out=None, alpha_out=None, want_alpha=True):
+    """dense_decode_step with the library's static scratch array instead of a workspace (the call itself
+    allocates nothing; outputs are allocated here unless given).  Returns (out, alpha_out)."""
+    lib = load()
+    B, Hq, d = q.shape
+    k, stride = _as_kv(k, B)
+    v, _ = _as_kv(v, B)
+    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
+    _need(q.is_contiguous() and k_loc.is_contiguous() and v_loc.is_contiguous(), "inputs must be contiguous")
+    _need(q.dtype == k.dtype == v.dtype == k_loc.dtype == v_loc.dtype, "q, K, V, k_loc, v_loc must share a dtype")
+    if n_loc is not None:
+        _need(n_loc.dtype == torch.int32 and n_loc.is_cuda and n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
+    Hkv, n = k.shape[1], k.shape[2]
+    nmax = k_loc.shape[2]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    if want_alpha and alpha_out is None:
+        alpha_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.dense_decode_step_noalloc(_p(q), _p(k), _p(v), stride, n, _p(k_loc), _p(v_loc), _p(n_loc), nmax, B, Hq,
+                                       Hkv, d, _dtype_code(q), _p(out), _p(alpha_out), _stream(q.device))
+    _check("dense_decode_step_noalloc", st)
+    return out, alpha_out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().lcda_noalloc_scratch_bytes())
 
 
 def capacity(n: int, m: int, n_sink: int, n_recent: int) -> int:

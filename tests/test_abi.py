@@ -129,3 +129,31 @@ def test_sig_score_topk_q_rejects(lib):
     st = lib.sig_score_topk_q(fake(), None, 1, fake(), 32, 1, 4, 1, 1000, 10, 2, 2, fake(), 14, fake(), None,
                               fake(), fake(), 1 << 30, None)
     assert st == 1 and b"q is NULL" in lib.lcda_last_error()
+
+
+def test_dense_decode_step_noalloc_rejects(lib):
+    """The no-allocation step refuses shapes whose workspace exceeds its static array, and bad arguments,
+    before any HIP call (the array's address is looked up only for a call that will run)."""
+    cap = lib.lcda_noalloc_scratch_bytes()
+    assert 0 < cap < (16 << 20)
+    B, Hq, Hkv, n = 128, 32, 8, 61440   # a shared document read by 128 items: 21 MB of partial states
+    assert lib.lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, 128, n, 0, 512) > cap
+    st = lib.dense_decode_step_noalloc(fake(), None, None, 0, n, None, None, None, 512, B, Hq, Hkv, 128,
+                                       1, fake(), None, None)
+    assert st == 2 and b"scratch" in lib.lcda_last_error()
+    st = lib.dense_decode_step_noalloc(fake(), fake(), fake(), 0, 1000, fake(), fake(), None, 64, 9000, 1, 1, 128,
+                                       1, fake(), None, None)
+    assert st == 2 and b"8192" in lib.lcda_last_error()
+    # a shape that fits, with a NULL input: the argument check, not the array, answers
+    st = lib.dense_decode_step_noalloc(fake(), None, fake(), 0, 1000, fake(), fake(), None, 64, 2, 8, 2, 128, 1,
+                                       fake(), None, None)
+    assert st == 1 and b"k is NULL" in lib.lcda_last_error()
+    assert lib.dense_decode_step_noalloc(None, None, None, 0, 1000, None, None, None, 64, 0, 8, 2, 128, 1, None, None,
+                                         None) == 0
+
+
+def test_workspace_sizes_of_an_empty_batch(lib):
+    """B = 0 (no rows) sizes to a small workspace for every kernel choice, a shared document included."""
+    for stride in (0, 2 * 1000 * 128):
+        assert lib.lcda_ws_bytes_cached_attn_lse(0, 8, 2, 128, 1000, stride) >= 0
+        assert lib.lcda_ws_bytes_dense_decode_step(0, 8, 2, 128, 1000, stride, 64) >= 0
