@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/lcda.h"
 #include "common.h"
 #include "internal.h"
@@ -149,21 +151,43 @@ int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows
     return hip_status(fn, launch_combine(c, st));
 }
 
-// Workspace of sig_score_topk: the distance histograms of every chunk and of
-// the two window parts.
+// Workspace of sig_score_topk, sized for either TOPK form whatever the launch
+// knobs: the chunked form's distance histograms of every chunk (at most
+// kTopkMaxChunks) and of the two window parts, or the one-launch form's arrival
+// counters, epochs and published part histograms (parts of at least 4096
+// positions, at most 64 per unit).  Both forms start at offset 0; a call uses
+// one of them.
+constexpr int kTopkMaxChunks = 64;
+
 struct TopkLayout {
-    int chunks;
-    size_t hist_off, bytes;
+    size_t bar_off, epoch_off, phist_off;
+    size_t bytes;
 };
 
 TopkLayout topk_layout(int B, int Hq, int Hkv, int64_t n) {
     TopkLayout l;
-    const int64_t cl = topk_chunk_len(n, B * Hkv);
-    l.chunks = (int)ceil_div(n, cl);
-    const size_t rows = (size_t)B * Hq;
-    l.hist_off = 0;
-    l.bytes = l.hist_off + round_up(rows * (l.chunks + 2) * topk_hist_row() * sizeof(uint32_t));
+    const size_t rows = (size_t)B * Hq, units = (size_t)B * Hkv;
+    const size_t chunked = round_up(rows * (kTopkMaxChunks + 2) * topk_hist_row() * sizeof(uint32_t));
+    const size_t max_parts = (size_t)std::min<int64_t>(64, std::max<int64_t>(1, (n + 4095) / 4096));
+    l.bar_off = 0;
+    l.epoch_off = round_up(units * sizeof(unsigned long long));
+    l.phist_off = l.epoch_off + round_up(units * sizeof(uint32_t));
+    const size_t unit = l.phist_off + round_up(units * max_parts * 3 * 4 * topk_unit_row_words() * sizeof(uint32_t));
+    l.bytes = std::max(chunked, unit);
     return l;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = c;
+    }
+    return cache[dev];
 }
 
 }  // namespace
@@ -278,6 +302,8 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
     else if (!strcmp(key, "topk_subs") && value <= 64) t.topk_subs = value;
     else if (!strcmp(key, "topk_wgs") && value > 0) t.topk_wgs = value;
+    else if (!strcmp(key, "topk_kernel") && value <= 1) t.topk_kernel = value;
+    else if (!strcmp(key, "topk_spin") && value <= (1 << 20)) t.topk_spin = value;
     else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
     return LCDA_OK;
 }
@@ -299,6 +325,8 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "gather_variant")) return t.gather_variant;
     if (!strcmp(key, "topk_subs")) return t.topk_subs;
     if (!strcmp(key, "topk_wgs")) return t.topk_wgs;
+    if (!strcmp(key, "topk_kernel")) return t.topk_kernel;
+    if (!strcmp(key, "topk_spin")) return t.topk_spin;
     return -1;
 }
 
@@ -632,11 +660,25 @@ static int topk_impl(const char* fn, const uint32_t* key_sigs, uint32_t* q_sigs,
     a.idx = idx;
     a.count = count;
     a.scores = scores;
-    a.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.hist_off);
-    a.chunks = lay.chunks;
-    a.chunk_len = topk_chunk_len(n, B * Hkv);
+    char* w = static_cast<char*>(ws);
+    // One launch with the distances in LDS where the grid fits the device one
+    // workgroup per CU; otherwise the chunked passes.
+    const int part = (n > 0 && tuning().topk_kernel == 1) ? topk_unit_part(n, B * Hkv, a.G, device_cus()) : 0;
+    if (part > 0) {
+        a.parts = (int)ceil_div(n, part);
+        a.part_len = part;
+        a.spin_max = (int)tuning().topk_spin;
+        a.bar = reinterpret_cast<unsigned long long*>(w + lay.bar_off);
+        a.epoch = reinterpret_cast<uint32_t*>(w + lay.epoch_off);
+        a.phist = reinterpret_cast<uint32_t*>(w + lay.phist_off);
+        a.chunks = 1;
+    } else {
+        a.hist = reinterpret_cast<uint32_t*>(w);
+        a.chunk_len = topk_chunk_len(n, B * Hkv);
+        a.chunks = n > 0 ? (int)ceil_div(n, a.chunk_len) : 0;
+    }
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (enc && lay.chunks == 0) {   // no positions: the codes still come back, from the encoder
+    if (enc && a.chunks == 0) {   // no positions: the codes still come back, from the encoder
         EncodeArgs e{};
         e.x = q;
         e.bf16 = q_dtype == LCDA_BF16;

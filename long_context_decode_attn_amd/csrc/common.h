@@ -142,6 +142,9 @@ __device__ __forceinline__ void store_dev(float2* p, float2 x) {
 __device__ __forceinline__ void store_dev(uint32_t* p, uint32_t x) {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t load_dev_u32(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint64_t load_dev_u64(const void* p) {   // 8-byte aligned
     return __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);

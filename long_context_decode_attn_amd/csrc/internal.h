@@ -81,6 +81,11 @@ struct Tuning {
     int64_t gather_variant = 0;    // GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads
     int64_t topk_subs = 0;         // TOPK: 4096-position sub-chunks per chunk (0: from topk_wgs)
     int64_t topk_wgs = 512;        // TOPK: workgroups a call aims at when topk_subs is 0
+    int64_t topk_kernel = 1;       // TOPK: 1 = one launch with the distances kept in LDS and a histogram
+                                   // exchange where the grid fits the device, 0 = chunked histogram +
+                                   // compaction passes
+    int64_t topk_spin = 1 << 14;   // TOPK one-launch form: polls of the exchange wait before a workgroup counts
+                                   // its partners' parts itself (0: at once; for tests of that path)
 };
 Tuning& tuning();
 
@@ -169,8 +174,22 @@ struct TopkArgs {
     uint32_t* q_codes;          // [B, Hq]: where the encoded query codes go
     int chunks;                 // ceil(n / chunk_len) <= 64
     int64_t chunk_len;
+    // One launch with a histogram exchange (sig_topk_unit.hip): each (b, KV
+    // head) unit's positions in `parts` parts of part_len positions.
+    int parts;
+    int part_len;
+    unsigned long long* bar;    // ws: [B * Hkv] arrival counters
+    uint32_t* epoch;            // ws: [B * Hkv] release epochs
+    uint32_t* phist;            // ws: [B * Hkv][parts][3][4][topk_unit_row_words()] published histograms
+    int spin_max;               // polls of the exchange wait
 };
 int topk_chunk_len(int64_t n, int units);   // units: B * Hkv
+// One launch per call with a histogram exchange (sig_topk_unit.hip): positions
+// per part of a (b, KV head) unit, 0 when that form does not apply (G > 4, or
+// the grid of units x parts exceeds `cus` workgroups, one per CU).
+int topk_unit_part(int64_t n, int units, int G, int cus);
+int topk_unit_row_words();
+hipError_t launch_topk_unit(const TopkArgs& a, hipStream_t st);
 int topk_hist_row();
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 

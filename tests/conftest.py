@@ -18,3 +18,14 @@ def orc():
     from oracle import oracle as o
     o.build()
     return o.default()
+
+
+@pytest.fixture(params=[1, 0], ids=["unit", "chunked"])
+def topk_kernel(request):
+    """Both TOPK forms: one launch with the distances in LDS and a histogram exchange (the default where the
+    grid fits the device) and the chunked histogram + compaction passes."""
+    from long_context_decode_attn_amd import ops
+    old = ops.get_tuning("topk_kernel")
+    ops.set_tuning("topk_kernel", request.param)
+    yield request.param
+    ops.set_tuning("topk_kernel", old)

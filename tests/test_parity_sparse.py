@@ -38,7 +38,7 @@ def _topk_case(orc, B, Hq, Hkv, n, m, s, r, seed, pool=None, scores=True, cap=No
     return ks, qs, idx, cnt
 
 
-def test_four_bit_example(orc):
+def test_four_bit_example(orc, topk_kernel):
     """HashAttention's illustrative example: query 1011 vs keys 1011 / 1001 / 0110 -> distances 0 / 1 / 3."""
     ks = torch.tensor([[[0b1011, 0b1001, 0b0110]]], dtype=torch.int32)
     qs = torch.tensor([[0b1011]], dtype=torch.int32)
@@ -52,8 +52,38 @@ def test_four_bit_example(orc):
     (100, 10, 60, 50), (4095, 300, 16, 64), (4096, 300, 16, 64), (4097, 300, 16, 64), (10001, 1000, 128, 128),
     (20000, 625, 0, 0), (20000, 0, 0, 0), (20000, 19000, 5, 5), (9000, 50, 4100, 20),
 ])
-def test_topk_shapes(orc, n, m, s, r):
+def test_topk_shapes(orc, n, m, s, r, topk_kernel):
     _topk_case(orc, 2, 8, 2, n, m, s, r, 10 + n + m)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,n,m,s,r", [
+    (8, 32, 8, 32768, 1024, 128, 128),       # 4 parts of 8,192 per (b, KV head), 2 dwords per thread
+    (16, 32, 8, 65536, 2048, 128, 128),      # 2 parts of 32,768 (8 dwords per thread, swizzled LDS)
+    (16, 32, 8, 65535, 2048, 3000, 40000),   # ragged last part, windows spanning whole parts
+    (4, 32, 8, 131072, 4096, 128, 128),      # 8 parts of 16,384
+    (2, 32, 8, 131071, 4096, 1, 1),          # 16 parts of 8,192, ragged
+    (16, 24, 8, 40000, 1250, 64, 64),        # G = 3
+    (4, 8, 8, 100000, 60000, 0, 0),          # G = 1, most positions selected
+    (8, 32, 8, 32768, 32768, 0, 0),          # full budget
+    (8, 32, 8, 32768, 0, 5, 9),              # windows only
+])
+def test_topk_unit_shapes(orc, B, Hq, Hkv, n, m, s, r):
+    """The one-launch TOPK at every part size (1 to 8 dwords of distance bytes per thread and head) with
+    several parts per (b, KV head) exchanging their histograms; ragged ends, windows spanning whole parts,
+    G = 1 and 3, a full budget and windows only."""
+    _topk_case(orc, B, Hq, Hkv, n, m, s, r, 500 + n % 101 + m, scores=n * B * Hq <= (1 << 23))
+
+
+def test_topk_unit_exchange_fallback(orc):
+    """With a zero wait the workgroups that do not arrive last count their partners' parts from the codes
+    themselves: the same indices (the path taken when the workgroups of a launch are not all resident)."""
+    old = ops.get_tuning("topk_spin")
+    ops.set_tuning("topk_spin", 0)
+    try:
+        _topk_case(orc, 8, 32, 8, 32768, 1024, 128, 128, 611, scores=False)
+        _topk_case(orc, 2, 32, 8, 131071, 4096, 300, 7000, 612, scores=False)
+    finally:
+        ops.set_tuning("topk_spin", old)
 
 
 @pytest.mark.parametrize("n,m,s,r", [(300001, 5000, 5000, 3000), (270000, 4096, 128, 128), (524288, 8192, 128, 128),
@@ -79,17 +109,17 @@ def test_topk_chunk_sizes(orc, subs):
 
 
 @pytest.mark.parametrize("pool", [1, 2, 5])
-def test_topk_massive_ties(orc, pool):
+def test_topk_massive_ties(orc, pool, topk_kernel):
     """Few distinct signatures: almost every position ties; the lower position must win."""
     _topk_case(orc, 1, 4, 1, 9000, 700, 8, 8, 77 + pool, pool=pool)
 
 
-def test_topk_group_sizes(orc):
+def test_topk_group_sizes(orc, topk_kernel):
     for G in (1, 2, 3, 5, 8):
         _topk_case(orc, 1, 2 * G, 2, 5000, 200, 16, 16, 90 + G)
 
 
-def test_topk_larger_cap(orc):
+def test_topk_larger_cap(orc, topk_kernel):
     ks, qs, idx, cnt = _topk_case(orc, 1, 4, 1, 3000, 100, 10, 10, 55, cap=500)
     assert np.all(idx.cpu().numpy()[..., cnt.max().item():] == -1)
 

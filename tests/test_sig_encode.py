@@ -77,7 +77,7 @@ def test_append_key_codes_into_cache_layout(orc):
     (1, 16, 2, 70000, 3000, 5000, 9000, torch.bfloat16, 32),
     (2, 8, 2, 0, 10, 2, 2, torch.bfloat16, 32),
 ])
-def test_topk_with_encoded_queries(orc, B, Hq, Hkv, n, m, s, r, dtype, bits):
+def test_topk_with_encoded_queries(orc, B, Hq, Hkv, n, m, s, r, dtype, bits, topk_kernel):
     """Indices, counts and the returned query codes bit-exact against the oracle's encode + select, and the
     same indices as the unfused GPU calls."""
     g = torch.Generator().manual_seed(630 + n + Hq)
