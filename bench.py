@@ -266,7 +266,8 @@ class SparseSet:
         self.cnt = torch.zeros((B, Hq), dtype=torch.int32, device=device)
         self.o = torch.empty((B, Hq, 128), device=device)
         self.oa = torch.empty((B, Hq), device=device)
-        nb = max(ops.ws_bytes_sig_score_topk(B, Hq, Hkv, n), ops.ws_bytes_gather_attn(B, Hq, Hkv, 128, self.cap))
+        nb = max(ops.ws_bytes_sig_score_topk(B, Hq, Hkv, n), ops.ws_bytes_gather_attn(B, Hq, Hkv, 128, self.cap),
+                 ops.ws_bytes_sparse_decode_step(B, Hq, Hkv, 128, n, self.cap))
         self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
 
     def topk(self):
@@ -278,9 +279,15 @@ class SparseSet:
         ops.gather_attn(self.x["q"], self.x["k"], self.x["v"], self.idx, self.cnt, out=self.o, alpha=self.oa,
                         ws=self.ws)
 
-    def step(self):
+    def step_two_calls(self):
         self.topk()
         self.gather()
+
+    def step(self):
+        c = self.cfg
+        ops.sparse_decode_step(self.x["key_sigs"], self.x["q_sigs"], self.x["q"], self.x["k"], self.x["v"], c.m,
+                               c.n_sink, c.n_recent, cap=self.cap, idx=self.idx, count=self.cnt, out=self.o,
+                               alpha=self.oa, ws=self.ws)
 
     # T_map (random projection): the query codes, and the codes of one new key per (b, KV head)
     def tmap_setup(self):
@@ -330,6 +337,7 @@ def bench_sparse(args, cfg, rot=None):
 
     steps = args.steps
     ms_step = run_steps([s.step for s in sets], steps, args.warmup, args.graph) / steps
+    ms_two = run_steps([s.step_two_calls for s in sets], steps, args.warmup, args.graph) / steps
     ms_g = run_steps([s.gather for s in sets], steps, args.warmup, args.graph) / steps
     ms_t = run_steps([s.topk for s in sets], steps, args.warmup, args.graph) / steps
     G = cfg.Hq // cfg.Hkv
@@ -347,6 +355,8 @@ def bench_sparse(args, cfg, rot=None):
         "step_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "unique_rows": float(np.mean(uniq)),
         "per_head_rows": float(np.mean(per_head_rows)),
+        "two_call_ms_per_step": ms_two,
+        "two_call_tbps": step_bytes / (ms_two * 1e-3) / 1e12,
         "sig_score_topk_us": ms_t * 1e3,
         "gather_attn_us": ms_g * 1e3,
         "topk_sig_tbps": sig_bytes / (ms_t * 1e-3) / 1e12,

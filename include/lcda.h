@@ -191,6 +191,30 @@ int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_st
                 int B, int Hq, int Hkv, int d, int64_t n, int dtype,
                 float* out, float* alpha, void* ws, size_t ws_bytes, void* stream);
 
+/* Fused sparse decode step: sig_score_topk followed by gather_attn, in one
+ * launch where possible.
+ *
+ * idx and count are sig_score_topk's (the selected set I of each query head,
+ * ascending, -1 padded); out and alpha are gather_attn's over them
+ * ("HashAttention ...", slides "Only selection is approximate; selected KV
+ * stay in full form" and "Token-level sparsity still needs a careful
+ * kernel": T = T_scan + T_TOPK + T_selected attention, here without a launch
+ * or an index round trip between the terms).  The workgroups that select a
+ * (batch item, KV head)'s positions then read those rows of the cache and
+ * merge their partial softmax states exactly, as the split-KV pass does.
+ * Results equal the two calls' up to floating-point summation order.  Falls
+ * back to the two calls for shapes the one-launch form does not take (more
+ * than 4 query heads per KV head, or a grid beyond one workgroup per CU).
+ *
+ *   key_sigs, q_sigs, m, n_sink, n_recent, idx, cap, count   as in sig_score_topk
+ *   q, k, v, kv_batch_stride, n, dtype, out, alpha           as in gather_attn
+ *   ws   at least lcda_ws_bytes_sparse_decode_step(...) bytes
+ */
+int sparse_decode_step(const uint32_t* key_sigs, const uint32_t* q_sigs, const void* q, const void* k,
+                       const void* v, int64_t kv_batch_stride, int B, int Hq, int Hkv, int d, int64_t n,
+                       int dtype, int64_t m, int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap,
+                       int32_t* count, float* out, float* alpha, void* ws, size_t ws_bytes, void* stream);
+
 /* Fused dense decode step: cached_attn_lse followed by lse_merge_local, in
  * one pass where possible.
  *
@@ -252,6 +276,7 @@ size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap);
 size_t lcda_ws_bytes_sig_score_topk_w(int B, int Hq, int64_t n);
 size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n,
                                        int64_t kv_batch_stride, int64_t n_loc_max);
+size_t lcda_ws_bytes_sparse_decode_step(int B, int Hq, int Hkv, int d, int64_t n, int64_t cap);
 
 /* Text of the last non-OK status returned on the calling thread. */
 const char* lcda_last_error(void);

@@ -304,6 +304,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "topk_wgs") && value > 0) t.topk_wgs = value;
     else if (!strcmp(key, "topk_kernel") && value <= 1) t.topk_kernel = value;
     else if (!strcmp(key, "topk_spin") && value <= (1 << 20)) t.topk_spin = value;
+    else if (!strcmp(key, "sparse_fused") && value <= 1) t.sparse_fused = value;
     else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
     return LCDA_OK;
 }
@@ -327,6 +328,7 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "topk_wgs")) return t.topk_wgs;
     if (!strcmp(key, "topk_kernel")) return t.topk_kernel;
     if (!strcmp(key, "topk_spin")) return t.topk_spin;
+    if (!strcmp(key, "sparse_fused")) return t.sparse_fused;
     return -1;
 }
 
@@ -849,6 +851,113 @@ int gather_attn(const void* q, const void* k, const void* v, int64_t kv_batch_st
     a.scale_log2 = kLog2e / sqrtf((float)kD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     return finish(fn, p, a, dtype, B * Hq, out, alpha, nullptr, nullptr, st);
+}
+
+// Fused sparse decode step: SCORE + TOPK + GATHER-ATT in one launch where the
+// one-launch TOPK form applies (every part of the launch resident at once,
+// G <= 4); otherwise sig_score_topk then gather_attn.  Workspace: the TOPK
+// layout, then the merge counters and the parts' partial states.
+struct SparseLayout {
+    size_t bar2_off, pml_off, pacc_off, bytes;
+};
+
+static SparseLayout sparse_layout(int B, int Hq, int Hkv, int64_t n) {
+    SparseLayout l;
+    const size_t rows = (size_t)B * Hq, units = (size_t)B * Hkv;
+    const size_t max_parts = (size_t)std::min<int64_t>(64, std::max<int64_t>(1, (n + 4095) / 4096));
+    l.bar2_off = topk_layout(B, Hq, Hkv, n).bytes;
+    l.pml_off = l.bar2_off + round_up(units * sizeof(unsigned long long));
+    l.pacc_off = l.pml_off + round_up(rows * max_parts * sizeof(float2));
+    l.bytes = l.pacc_off + round_up(rows * max_parts * kD * sizeof(float));
+    return l;
+}
+
+size_t lcda_ws_bytes_sparse_decode_step(int B, int Hq, int Hkv, int d, int64_t n, int64_t cap) {
+    if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX || cap < 0 || cap > INT32_MAX)
+        return 0;
+    const size_t fused = sparse_layout(B, Hq, Hkv, n).bytes;
+    const size_t two = std::max(lcda_ws_bytes_sig_score_topk(B, Hq, Hkv, n), lcda_ws_bytes_gather_attn(B, Hq, Hkv, d, cap));
+    return std::max(fused, two);
+}
+
+int sparse_decode_step(const uint32_t* key_sigs, const uint32_t* q_sigs, const void* q, const void* k, const void* v,
+                       int64_t kv_batch_stride, int B, int Hq, int Hkv, int d, int64_t n, int dtype, int64_t m,
+                       int64_t n_sink, int64_t n_recent, int32_t* idx, int64_t cap, int32_t* count, float* out,
+                       float* alpha, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "sparse_decode_step";
+    RETURN_IF(check_heads(fn, B, Hq, Hkv, d));
+    RETURN_IF(check_dtype(fn, dtype));
+    RETURN_IF(check_n(fn, "n", n));
+    RETURN_IF(check_kv_stride(fn, kv_batch_stride, Hkv, n, dtype));
+    if (Hq / Hkv > 8) return fail(LCDA_EUNSUPPORTED, "%s: more than 8 query heads per KV head", fn);
+    if (m < 0 || n_sink < 0 || n_recent < 0) return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be >= 0", fn);
+    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX)
+        return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be <= INT32_MAX", fn);
+    if (cap < 0 || cap > INT32_MAX) return fail(LCDA_EINVAL, "%s: cap = %lld out of range", fn, (long long)cap);
+    const int64_t need = std::min(n, m + n_sink + n_recent);
+    if (cap < need)
+        return fail(LCDA_EINVAL, "%s: cap = %lld < min(n, m + n_sink + n_recent) = %lld", fn, (long long)cap,
+                    (long long)need);
+    const bool work = B > 0;
+    RETURN_IF(check_ptr(fn, "key_sigs", key_sigs, work && n > 0));
+    RETURN_IF(check_ptr(fn, "q_sigs", q_sigs, work));
+    RETURN_IF(check_ptr(fn, "q", q, work));
+    RETURN_IF(check_ptr(fn, "k", k, work && n > 0));
+    RETURN_IF(check_ptr(fn, "v", v, work && n > 0));
+    RETURN_IF(check_ptr(fn, "idx", idx, work && cap > 0));
+    RETURN_IF(check_ptr(fn, "count", count, work));
+    RETURN_IF(check_ptr(fn, "out", out, work));
+    RETURN_IF(check_ptr(fn, "alpha", alpha, false));
+    RETURN_IF(check_ptr(fn, "ws", ws, false));
+    if (!work) return LCDA_OK;
+    const size_t need_ws = lcda_ws_bytes_sparse_decode_step(B, Hq, Hkv, d, n, cap);
+    if (!ws || ws_bytes < need_ws)
+        return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, need_ws);
+    const int G = Hq / Hkv;
+    const int part = (n > 0 && tuning().topk_kernel == 1 && tuning().sparse_fused == 1)
+                         ? topk_unit_part(n, B * Hkv, G, device_cus())
+                         : 0;
+    if (part == 0) {   // the two calls
+        RETURN_IF(sig_score_topk(key_sigs, q_sigs, B, Hq, Hkv, n, m, n_sink, n_recent, idx, cap, count, nullptr, ws,
+                                 ws_bytes, stream));
+        return gather_attn(q, k, v, kv_batch_stride, idx, count, cap, B, Hq, Hkv, d, n, dtype, out, alpha, ws,
+                           ws_bytes, stream);
+    }
+    const TopkLayout lay = topk_layout(B, Hq, Hkv, n);
+    const SparseLayout sl = sparse_layout(B, Hq, Hkv, n);
+    char* w = static_cast<char*>(ws);
+    TopkArgs a{};
+    a.key_sigs = key_sigs;
+    a.q_sigs = q_sigs;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.n = n;
+    a.m = m;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.cap = cap;
+    a.idx = idx;
+    a.count = count;
+    a.chunks = 1;
+    a.parts = (int)ceil_div(n, part);
+    a.part_len = part;
+    a.spin_max = (int)tuning().topk_spin;
+    a.bar = reinterpret_cast<unsigned long long*>(w + lay.bar_off);
+    a.epoch = reinterpret_cast<uint32_t*>(w + lay.epoch_off);
+    a.phist = reinterpret_cast<uint32_t*>(w + lay.phist_off);
+    a.gq = q;
+    a.gk = k;
+    a.gv = v;
+    a.kv_batch_stride = kv_batch_stride;
+    a.out = out;
+    a.alpha = alpha;
+    a.bar2 = reinterpret_cast<unsigned long long*>(w + sl.bar2_off);
+    a.pml = reinterpret_cast<float2*>(w + sl.pml_off);
+    a.pacc = reinterpret_cast<float*>(w + sl.pacc_off);
+    a.scale_log2 = kLog2e / sqrtf((float)kD);
+    return hip_status(fn, launch_topk_unit(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -84,6 +84,8 @@ struct Tuning {
     int64_t topk_kernel = 1;       // TOPK: 1 = one launch with the distances kept in LDS and a histogram
                                    // exchange where the grid fits the device, 0 = chunked histogram +
                                    // compaction passes
+    int64_t sparse_fused = 0;      // sparse_decode_step: 1 = SCORE + TOPK + GATHER-ATT in one launch where that
+                                   // form applies, 0 = sig_score_topk then gather_attn
     int64_t topk_spin = 1 << 14;   // TOPK one-launch form: polls of the exchange wait before a workgroup counts
                                    // its partners' parts itself (0: at once; for tests of that path)
 };
@@ -182,6 +184,18 @@ struct TopkArgs {
     uint32_t* epoch;            // ws: [B * Hkv] release epochs
     uint32_t* phist;            // ws: [B * Hkv][parts][3][4][topk_unit_row_words()] published histograms
     int spin_max;               // polls of the exchange wait
+    // GATHER-ATT of the selected rows in the same launch (sparse_decode_step;
+    // one-launch form only): gk == null means TOPK alone.
+    const void* gq;             // [B, Hq, 128]
+    const void* gk;             // cache as in SplitArgs::k
+    const void* gv;
+    int64_t kv_batch_stride;    // elements; 0 = one shared document
+    float* out;                 // [B, Hq, 128]
+    float* alpha;               // [B, Hq] or null
+    float2* pml;                // ws: [B * Hq][parts] partial (m, l) of each part
+    float* pacc;                // ws: [B * Hq][parts][128] partial sums of each part
+    unsigned long long* bar2;   // ws: [B * Hkv] arrival counters of the merge
+    float scale_log2;           // log2(e) / sqrt(d)
 };
 int topk_chunk_len(int64_t n, int units);   // units: B * Hkv
 // One launch per call with a histogram exchange (sig_topk_unit.hip): positions
@@ -189,7 +203,8 @@ int topk_chunk_len(int64_t n, int units);   // units: B * Hkv
 // the grid of units x parts exceeds `cus` workgroups, one per CU).
 int topk_unit_part(int64_t n, int units, int G, int cus);
 int topk_unit_row_words();
-hipError_t launch_topk_unit(const TopkArgs& a, hipStream_t st);
+// dtype: the rows' type when a.gk is set (LCDA_F32 or LCDA_BF16).
+hipError_t launch_topk_unit(const TopkArgs& a, int dtype, hipStream_t st);
 int topk_hist_row();
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 

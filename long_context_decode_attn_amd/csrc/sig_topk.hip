@@ -738,7 +738,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(k_topk_empty, dim3(a.Hq, a.B), dim3(64), 0, st, a);
         return hipGetLastError();
     }
-    if (a.parts > 0) return launch_topk_unit(a, st);
+    if (a.parts > 0) return launch_topk_unit(a, 0, st);
     const dim3 grid(a.chunks, a.Hkv, a.B), block(256);
     const bool vec = a.n % 4 == 0;
     const bool sc = a.scores != nullptr;

@@ -43,9 +43,22 @@
 //      workgroup scan of the tie counts gives each thread the ties it takes, a
 //      second of the selected counts its output offset; it stores its
 //      positions in order.
+// With the rows of the cache (sparse_decode_step) the same workgroups then run
+// GATHER-ATT ("HashAttention ...", slide "Only selection is approximate;
+// selected KV stay in full form": attention renormalised over the selected
+// rows, read straight from the cache by position):
+//   5. each part's selected positions of every head also go into an LDS list
+//      (as offsets in the part); 16 / G wavefronts per query head walk the
+//      head's list, four rows per load instruction (16 lanes per row, 8 values
+//      per lane), with an online softmax in base 2, and merge into one partial
+//      state (m, l, acc) per head and part;
+//   6. the last workgroup of the unit to publish its partial states merges the
+//      parts exactly through their maxima (the split identity of the dense path).
 // The workspace holds the counters, epochs and histograms; the counter word is
 // (tag << 32 | arrivals) as for the split pass (see arrive_count), so no call
 // needs it cleared, and every call leaves it at (tag, 0).
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -190,14 +203,221 @@ __device__ __forceinline__ void zero_counts(UnitSmem<D>& sm) {
     for (int k = threadIdx.x; k < 2 * 4 * kUBins; k += kUT) (&sm.win[0][0][0])[k] = 0u;
 }
 
-// D: dwords per thread and head; a part holds P = 4096 D positions.
-template <int D, bool SCORES>
+
+// Rows of 128 values as 8 floats per lane (16 lanes per row).
+template <typename T>
+struct GRow;
+template <>
+struct GRow<float> {
+    u32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = ld16_nt(p);
+        b = ld16_nt(p + 4);
+    }
+    __device__ __forceinline__ void to_float(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = __uint_as_float(a[e]);
+            x[4 + e] = __uint_as_float(b[e]);
+        }
+    }
+};
+template <>
+struct GRow<uint16_t> {
+    u32x4 a;
+    __device__ __forceinline__ void load(const uint16_t* p) { a = ld16_nt(p); }
+    __device__ __forceinline__ void to_float(float (&x)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16_lo(a[e]);
+            x[2 * e + 1] = bf16_hi(a[e]);
+        }
+    }
+};
+
+// The arguments combine_row reads: the parts' partial states of a query row.
+struct PartMerge {
+    int splits;
+    const float2* ml;
+    const float* acc;
+    const float* alpha_in;
+    const float* a_in;
+    float* out;
+    float* alpha;
+};
+
+// GATHER-ATT over this part's selected positions of each query head, then the
+// merge of the parts (see the file comment, steps 5 and 6).
+template <typename T, int D>
+__device__ void gather_part(const TopkArgs& a, UnitSmem<D>& sm, const uint16_t* lst, bool in_lds, const int (&cntg)[4],
+                            const int (&lbase)[4], int unit, int part, int64_t row0, int b, int h, int pbeg) {
+    constexpr int U = sizeof(T) == 2 ? 4 : 2;   // rows per lane group and step (fewer for fp32 rows)
+    constexpr int kStep = 4 * U;         // rows per wavefront and step
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform values in scalar registers
+    const int j = lane >> 4, c16 = lane & 15;
+    const int G = a.G, Q = a.parts;
+    const int Wh = kUW / G;              // wavefronts per head (G <= 4)
+    const int gw = w / Wh, wi = w % Wh;  // this wavefront's head (gw >= G: idle) and its rank
+    float m = kNoMax, l = 0.f, acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (gw < G) {
+        const int64_t row = row0 + gw;
+        const int cnt = __builtin_amdgcn_readfirstlane(gw == 0 ? cntg[0] : gw == 1 ? cntg[1] : gw == 2 ? cntg[2] : cntg[3]);
+        const int lb = __builtin_amdgcn_readfirstlane(gw == 0 ? lbase[0] : gw == 1 ? lbase[1] : gw == 2 ? lbase[2] : lbase[3]);
+        const int64_t head = (a.kv_batch_stride == 0 ? 0 : (int64_t)b * a.kv_batch_stride) + (int64_t)h * a.n * kD;
+        const T* kh = static_cast<const T*>(a.gk) + head + 8 * c16;
+        const T* vh = static_cast<const T*>(a.gv) + head + 8 * c16;
+        const int32_t* ilist = a.idx + row * a.cap + sm.s_sel[gw][3];   // the part's entries of the index list
+        float qv[8];
+        {
+            GRow<T> x;
+            x.load(static_cast<const T*>(a.gq) + row * kD + 8 * c16);
+            x.to_float(qv);
+        }
+        struct Step {
+            GRow<T> k[U], v[U];
+        };
+        // The rows of entries t0 + 4 u + j of the part's list (clamped to the
+        // last entry; rows past cnt are masked in compute).  LISTED: the
+        // positions come from the LDS list; otherwise from the index list the
+        // workgroup has written (a list too long for LDS).
+        auto fetch = [&](Step& st, int t0, auto listed) {
+            int pos[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int t = min(t0 + 4 * u + j, cnt - 1);
+                if constexpr (decltype(listed)::value) pos[u] = pbeg + (int)lst[lb + t];
+                else pos[u] = (int)load_dev_u32(reinterpret_cast<const uint32_t*>(ilist) + t);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                st.k[u].load(kh + (int64_t)pos[u] * kD);
+                st.v[u].load(vh + (int64_t)pos[u] * kD);
+            }
+        };
+        auto compute = [&](const Step& st, int t0) {
+            float s[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float kf[8];
+                st.k[u].to_float(kf);
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = fmaf(qv[e], kf[e], d);
+                d = sum16(d) * a.scale_log2;
+                s[u] = t0 + 4 * u + j < cnt ? d : -INFINITY;
+            }
+            float bm = s[0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) bm = fmaxf(bm, s[u]);
+            const float mn = fmaxf(m, bm);
+            const float sc = fast_exp2(m - mn);
+            m = mn;
+            l *= sc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float vf[8];
+                st.v[u].to_float(vf);
+                const float p = fast_exp2(s[u] - m);
+                l += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+            }
+        };
+        // Software pipeline: the rows of the next step are requested before the
+        // current step is computed, unconditionally (entries past the list are
+        // clamped to its last one), so that waiting for the current step's rows
+        // never waits for the next step's.
+        auto walk = [&](auto listed) {
+            int t0 = wi * kStep;
+            const int stride = Wh * kStep;
+            if (t0 >= cnt) return;
+            Step s0, s1;
+            fetch(s0, t0, listed);
+            while (true) {
+                fetch(s1, t0 + stride, listed);
+                compute(s0, t0);
+                t0 += stride;
+                if (t0 >= cnt) break;
+                fetch(s0, t0 + stride, listed);
+                compute(s1, t0);
+                t0 += stride;
+                if (t0 >= cnt) break;
+            }
+        };
+        if (in_lds) walk(std::true_type{});
+        else walk(std::false_type{});
+    }
+    // Merge the 4 lane groups of the wavefront, then the head's wavefronts
+    // through LDS (the counters' space is free now).
+    {
+        const float M = max_xor32(max_xor16(m));
+        const float wt = fast_exp2(m - M);
+        const float L = sum_xor32(sum_xor16(l * wt));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = sum_xor32(sum_xor16(acc[e] * wt));
+        float* so = reinterpret_cast<float*>(sm.cnt);          // [kUW][kD] sums
+        float2* sml = reinterpret_cast<float2*>(so + kUW * kD); // [kUW] (m, l)
+        if (j == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) so[w * kD + 8 * c16 + e] = acc[e];
+            if (c16 == 0) sml[w] = make_float2(M, L);
+        }
+        __syncthreads();
+        // Wavefront wi == 0 of head gw: the part's state of the head (lane:
+        // columns 2 lane, 2 lane + 1), published for the merge of the parts.
+        if (gw < G && wi == 0) {
+            float Mx = kNoMax;
+            for (int k = 0; k < Wh; ++k) Mx = fmaxf(Mx, sml[w + k].x);
+            float Lx = 0.f, x0 = 0.f, x1 = 0.f;
+            for (int k = 0; k < Wh; ++k) {
+                const float2 ml = sml[w + k];
+                const float f = ml.y > 0.f ? fast_exp2(ml.x - Mx) : 0.f;
+                Lx += f * ml.y;
+                x0 += f * so[(w + k) * kD + 2 * lane];
+                x1 += f * so[(w + k) * kD + 2 * lane + 1];
+            }
+            const int64_t slot = (row0 + gw) * Q + part;
+            if (Q == 1) {   // one part: the row is finished here
+                const bool has = Lx > 0.f;
+                const float r = has ? 1.f / Lx : 0.f;
+                a.out[(row0 + gw) * kD + 2 * lane] = x0 * r;
+                a.out[(row0 + gw) * kD + 2 * lane + 1] = x1 * r;
+                if (a.alpha && lane == 0) a.alpha[row0 + gw] = has ? (Mx + log2f(Lx)) * kLn2 : -INFINITY;
+            } else {
+                store_dev(a.pacc + slot * kD + 2 * lane, x0);
+                store_dev(a.pacc + slot * kD + 2 * lane + 1, x1);
+                if (lane == 0) store_dev(a.pml + slot, make_float2(Mx, Lx));
+            }
+        }
+    }
+    if (Q == 1) return;
+    // ---- 6. the last workgroup of the unit merges the parts ----------------------------------
+    if (!arrive_count(a.bar2 + unit, (uint32_t)Q, &sm.s_flag)) return;
+    if (w < G) {
+        PartMerge pm{Q, a.pml, a.pacc, nullptr, nullptr, a.out, a.alpha};
+        combine_row(pm, row0 + w, lane);
+    }
+}
+
+// D: dwords per thread and head; a part holds P = 4096 D positions.  T: the
+// rows' type for the fused GATHER-ATT (float or uint16_t for bf16), void for
+// TOPK alone.
+template <int D, bool SCORES, typename T>
 __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
     constexpr int P = 4 * kUT * D;
     __shared__ UnitSmem<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int Q = a.parts;
-    const int unit = blockIdx.x / Q, part = blockIdx.x % Q;
+    // Workgroup -> (unit, part): part-major, so that with a multiple of 8 units
+    // the parts of a unit run on one XCD (workgroups go round the 8 XCDs in
+    // turn) and every XCD holds every part position equally.
+    const int units = a.B * a.Hkv;
+    const int unit = blockIdx.x % units, part = blockIdx.x / units;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
     const int G = a.G;
     const int n = (int)a.n;
@@ -209,8 +429,14 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
     const bool vec = (n & 3) == 0;   // uniform
 
     // ---- 1. distances ------------------------------------------------------------------
-    // Step s: positions pbeg + 4 (1024 s + tid) + e, e < 4; every step's codes
-    // are requested at once.
+    // The query codes first (so that waiting for them is not waiting for all the
+    // codes), then step s: positions pbeg + 4 (1024 s + tid) + e, e < 4; every
+    // step's codes are requested at once.
+    uint32_t q[4];
+    if (a.q == nullptr) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) q[g] = a.q_sigs[row0 + min(g, G - 1)];
+    }
     u32x4 xc[D];
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -222,7 +448,6 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
             for (int e = 0; e < 4; ++e) xc[s][e] = ks[min(i + e, n - 1)];
         }
     }
-    uint32_t q[4];
     if (a.q != nullptr) {   // uniform: the query codes are encoded here (T_map), while the codes load
         static_assert(sizeof(sm.dist) + sizeof(sm.cnt) >= (kD * 32 + 4 * kD) * 4,
                       "R and the query rows fit the distances' and counters' LDS");
@@ -248,9 +473,6 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
         for (int g = 0; g < 4; ++g) q[g] = sm.s_code[min(g, G - 1)];
         if (part == 0 && tid < G) a.q_codes[row0 + tid] = sm.s_code[tid];
         __syncthreads();   // the staging area is about to hold distances
-    } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) q[g] = a.q_sigs[row0 + min(g, G - 1)];
     }
     zero_counts(sm);
     __syncthreads();
@@ -497,6 +719,19 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
     }
     uint32_t oe01, oe23, ot01, ot23;
     block_scan2(nsel[0] | (nsel[1] << 16), nsel[2] | (nsel[3] << 16), sm.s_w, oe01, oe23, ot01, ot23);
+    // The part's selected positions of head g: cntg[g] of them, listed in LDS
+    // (offsets from pbeg, after the lists of the heads before) when they fit.
+    constexpr bool kGather = !std::is_void<T>::value;
+    int cntg[4], lbase[4];
+    int lsum = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        cntg[g] = g < G ? (int)(((g < 2 ? ot01 : ot23) >> (16 * (g & 1))) & 0xFFFFu) : 0;
+        lbase[g] = lsum;
+        lsum += cntg[g];
+    }
+    uint16_t* lst = reinterpret_cast<uint16_t*>(&sm.dist[0][0]);
+    const bool in_lds = kGather && lsum <= (int)(sizeof(sm.dist) / 2);   // uniform
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         if (g < G) {
@@ -508,10 +743,12 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
             const __amdgpu_buffer_rsrc_t ro =
                 __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)(min(a.cap, a.n) * 4), kRsrcWord3);
             uint32_t pos4 = 4u * ((uint32_t)sm.s_sel[g][3] + local);
+            int li = lbase[g] + (int)local;
             uint32_t s = sel[g];
             while (s) {
                 const int bit = __builtin_ctz(s);
                 __builtin_amdgcn_raw_buffer_store_b32(P0 + bit, ro, pos4, 0, 0);
+                if (in_lds) lst[li++] = (uint16_t)(P0 + bit - pbeg);
                 pos4 += 4u;
                 s &= s - 1u;
             }
@@ -520,6 +757,11 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
                 for (int64_t i = (int64_t)total + tid; i < a.cap; i += kUT) out[i] = -1;
             }
         }
+    }
+    if constexpr (kGather) {
+        wait_vm_all();      // the index stores are acknowledged (a list too long for LDS is read back)
+        __syncthreads();
+        gather_part<T>(a, sm, lst, in_lds, cntg, lbase, unit, part, row0, b, h, pbeg);
     }
 }
 
@@ -540,16 +782,20 @@ int topk_unit_part(int64_t n, int units, int G, int cus) {
 
 int topk_unit_row_words() { return kURow; }
 
-hipError_t launch_topk_unit(const TopkArgs& a, hipStream_t st) {
+hipError_t launch_topk_unit(const TopkArgs& a, int dtype, hipStream_t st) {
     const int D = a.part_len / 4096;
     if (a.B <= 0 || a.G > 4 || a.parts <= 0 || a.part_len != 4096 * D || (D != 1 && D != 2 && D != 4 && D != 8))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.B * a.Hkv * a.parts)), block(kUT);
     const bool sc = a.scores != nullptr;
+    const int kind = a.gk == nullptr ? 0 : (dtype == 0 ? 1 : 2);
+#define LCDA_UNIT3(DD, SC, TT) hipLaunchKernelGGL((k_topk_unit<DD, SC, TT>), grid, block, 0, st, a)
 #define LCDA_UNIT(DD)                                                                                      \
     do {                                                                                                   \
-        if (sc) hipLaunchKernelGGL((k_topk_unit<DD, true>), grid, block, 0, st, a);                       \
-        else hipLaunchKernelGGL((k_topk_unit<DD, false>), grid, block, 0, st, a);                         \
+        if (kind == 1) LCDA_UNIT3(DD, false, float);                                                      \
+        else if (kind == 2) LCDA_UNIT3(DD, false, uint16_t);                                              \
+        else if (sc) LCDA_UNIT3(DD, true, void);                                                          \
+        else LCDA_UNIT3(DD, false, void);                                                                 \
     } while (0)
     switch (D) {
         case 1: LCDA_UNIT(1); break;
@@ -558,6 +804,7 @@ hipError_t launch_topk_unit(const TopkArgs& a, hipStream_t st) {
         default: LCDA_UNIT(8); break;
     }
 #undef LCDA_UNIT
+#undef LCDA_UNIT3
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn"
            "lcda_last_error", "lcda_version", "lcda_set_tuning", "lcda_get_tuning",
            "dense_decode_step", "lcda_ws_bytes_dense_decode_step", "sig_encode", "sig_score_topk_q",
            "sig_score_topk_w", "lcda_ws_bytes_sig_score_topk_w", "dense_decode_step_noalloc",
-           "lcda_noalloc_scratch_bytes")
+           "lcda_noalloc_scratch_bytes", "sparse_decode_step", "lcda_ws_bytes_sparse_decode_step")
 
 _lib = None
 
@@ -77,6 +77,11 @@ def load(path: str = LIB_PATH):
     lib.dense_decode_step_noalloc.restype = ctypes.c_int
     lib.lcda_noalloc_scratch_bytes.argtypes = []
     lib.lcda_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.sparse_decode_step.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i64, i32, i64, i64, i64, P, i64, P, P,
+                                       P, P, sz, P]
+    lib.sparse_decode_step.restype = ctypes.c_int
+    lib.lcda_ws_bytes_sparse_decode_step.argtypes = [i32, i32, i32, i32, i64, i64]
+    lib.lcda_ws_bytes_sparse_decode_step.restype = ctypes.c_size_t
     lib.lcda_set_tuning.argtypes = [ctypes.c_char_p, i64]
     lib.lcda_set_tuning.restype = ctypes.c_int
     lib.lcda_get_tuning.argtypes = [ctypes.c_char_p]
@@ -378,6 +383,42 @@ def gather_attn(q, k, v, idx, count, out=None, alpha=None, ws=None, want_alpha=T
                          _p(out), _p(alpha), _p(w), w.numel() * w.element_size(), _stream(q.device))
     _check("gather_attn", st)
     return out, alpha
+
+
+def ws_bytes_sparse_decode_step(B, Hq, Hkv, d, n, cap) -> int:
+    return int(load().lcda_ws_bytes_sparse_decode_step(B, Hq, Hkv, d, n, cap))
+
+
+def sparse_decode_step(key_sigs, q_sigs, q, k, v, m, n_sink, n_recent, cap=None, idx=None, count=None, out=None,
+                       alpha=None, ws=None, want_alpha=True):
+    """SCORE + TOPK + GATHER-ATT in one launch where possible.  key_sigs [B, Hkv, n], q_sigs [B, Hq] (int32
+    storage of uint32 codes); q [B, Hq, 128]; K, V [B, Hkv, n, 128] (or a shared [1, Hkv, n, 128]).
+
+    Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, out [B, Hq, 128] fp32, alpha [B, Hq] fp32)."""
+    lib = load()
+    B, Hq, d = q.shape
+    k, stride = _as_kv(k, B)
+    v, _ = _as_kv(v, B)
+    _need(key_sigs.dtype in (torch.int32, torch.uint32) and q_sigs.dtype == key_sigs.dtype, "signatures must be 32-bit")
+    _need(key_sigs.is_contiguous() and q_sigs.is_contiguous() and q.is_contiguous(), "inputs must be contiguous")
+    _need(q.dtype == k.dtype == v.dtype, "q, K, V must share a dtype")
+    Hkv, n = k.shape[1], k.shape[2]
+    _need(tuple(key_sigs.shape) == (B, Hkv, n), "key_sigs must be [B, Hkv, n]")
+    _need(tuple(q_sigs.shape) == (B, Hq), "q_sigs must be [B, Hq]")
+    cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
+    dev = q.device
+    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
+    if want_alpha and alpha is None:
+        alpha = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    nb = lib.lcda_ws_bytes_sparse_decode_step(B, Hq, Hkv, d, n, cap)
+    w = _ws(nb, dev, ws)
+    st = lib.sparse_decode_step(_p(key_sigs), _p(q_sigs), _p(q), _p(k), _p(v), stride, B, Hq, Hkv, d, n, _dtype_code(q),
+                                int(m), int(n_sink), int(n_recent), _p(idx), cap, _p(count), _p(out), _p(alpha), _p(w),
+                                w.numel() * w.element_size(), _stream(dev))
+    _check("sparse_decode_step", st)
+    return idx, count, out, alpha
 
 
 def set_tuning(key: str, value: int) -> None:
