@@ -612,6 +612,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (--steps times), for counter calibration")
+    ap.add_argument("--tuning", action="append", default=[], metavar="KEY=VALUE",
+                    help="set a launch-shape knob (lcda_set_tuning) before measuring; may be repeated")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -626,6 +628,9 @@ def main():
         print(json.dumps(calibrate_copy(args.calibrate_copy << 20, args.steps)))
         return
     ops.load()
+    for kv in args.tuning:
+        key, _, val = kv.partition("=")
+        ops.set_tuning(key, int(val))
     dev_name = torch.cuda.get_device_name(0)
 
     line = {"metric": METRIC, "unit": "queries/s", "n_gpus": 1, "warmup": args.warmup,

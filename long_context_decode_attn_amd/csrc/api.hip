@@ -154,16 +154,18 @@ int finish(const char* fn, const SplitPlan& p, SplitArgs& a, int dtype, int rows
 // Workspace of sig_score_topk, sized for either TOPK form whatever the launch
 // knobs: the chunked form's distance histograms of every chunk (at most
 // kTopkMaxChunks) and of the two window parts, or the one-launch form's arrival
-// counters, epochs and published part histograms (parts of at least 4096
-// positions, at most 64 per unit).  Both forms start at offset 0; a call uses
-// one of them.
+// counters, epochs, published part histograms (at most 64 parts per unit) and
+// step records.  Both forms start at offset 0; a call uses one of them.
 constexpr int kTopkMaxChunks = 64;
 
 struct TopkLayout {
-    size_t bar_off, epoch_off, phist_off;
+    size_t bar_off, epoch_off, phist_off, rbar_off, repoch_off, srec_off;
     size_t bytes;
 };
 
+// The chunked passes' histograms, or the one-launch form's counters, epochs,
+// published histograms and step records (whichever is larger: the two forms
+// share the space, and which one runs does not change the size).
 TopkLayout topk_layout(int B, int Hq, int Hkv, int64_t n) {
     TopkLayout l;
     const size_t rows = (size_t)B * Hq, units = (size_t)B * Hkv;
@@ -172,9 +174,22 @@ TopkLayout topk_layout(int B, int Hq, int Hkv, int64_t n) {
     l.bar_off = 0;
     l.epoch_off = round_up(units * sizeof(unsigned long long));
     l.phist_off = l.epoch_off + round_up(units * sizeof(uint32_t));
-    const size_t unit = l.phist_off + round_up(units * max_parts * 3 * 4 * topk_unit_row_words() * sizeof(uint32_t));
+    l.rbar_off = l.phist_off + round_up(units * max_parts * 4 * topk_unit_row_words() * sizeof(uint32_t));
+    l.repoch_off = l.rbar_off + round_up(units * sizeof(unsigned long long));
+    l.srec_off = l.repoch_off + round_up(units * sizeof(uint32_t));
+    const size_t unit = l.srec_off + round_up(units * topk_unit_rec_words() * sizeof(uint32_t));
     l.bytes = std::max(chunked, unit);
     return l;
+}
+
+// The one-launch form's exchange buffers in workspace w.
+void set_unit_ws(TopkArgs& a, char* w, const TopkLayout& l) {
+    a.bar = reinterpret_cast<unsigned long long*>(w + l.bar_off);
+    a.epoch = reinterpret_cast<uint32_t*>(w + l.epoch_off);
+    a.phist = reinterpret_cast<uint32_t*>(w + l.phist_off);
+    a.rbar = reinterpret_cast<unsigned long long*>(w + l.rbar_off);
+    a.repoch = reinterpret_cast<uint32_t*>(w + l.repoch_off);
+    a.srec = reinterpret_cast<uint32_t*>(w + l.srec_off);
 }
 
 // Compute units of the current device (cached per device).
@@ -670,9 +685,7 @@ static int topk_impl(const char* fn, const uint32_t* key_sigs, uint32_t* q_sigs,
         a.parts = (int)ceil_div(n, part);
         a.part_len = part;
         a.spin_max = (int)tuning().topk_spin;
-        a.bar = reinterpret_cast<unsigned long long*>(w + lay.bar_off);
-        a.epoch = reinterpret_cast<uint32_t*>(w + lay.epoch_off);
-        a.phist = reinterpret_cast<uint32_t*>(w + lay.phist_off);
+        set_unit_ws(a, w, lay);
         a.chunks = 1;
     } else {
         a.hist = reinterpret_cast<uint32_t*>(w);
@@ -944,9 +957,7 @@ int sparse_decode_step(const uint32_t* key_sigs, const uint32_t* q_sigs, const v
     a.parts = (int)ceil_div(n, part);
     a.part_len = part;
     a.spin_max = (int)tuning().topk_spin;
-    a.bar = reinterpret_cast<unsigned long long*>(w + lay.bar_off);
-    a.epoch = reinterpret_cast<uint32_t*>(w + lay.epoch_off);
-    a.phist = reinterpret_cast<uint32_t*>(w + lay.phist_off);
+    set_unit_ws(a, w, lay);
     a.gq = q;
     a.gk = k;
     a.gv = v;

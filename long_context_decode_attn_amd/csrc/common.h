@@ -167,44 +167,48 @@ __device__ __forceinline__ uint32_t ctr_tag(const unsigned long long* c) {
     return x;
 }
 
+// One arrival at counter c, made by one thread once the workgroup's published
+// stores are acknowledged: returns the number of arrivals so far, this one
+// included, and restores (tag, 0) when that is `target`.  Normally one
+// fetch-add; a counter word without its tag (never used, or overwritten) is
+// replaced by (tag, 1) with a compare-exchange by the first arrival to find it
+// so, and the others then count on the valid word (the exchange loop ends once
+// any of them has installed it).
+__device__ __forceinline__ uint32_t arrive_one(unsigned long long* c, uint32_t target) {
+    const uint32_t tag = ctr_tag(c);
+    const unsigned long long valid0 = (unsigned long long)tag << 32;
+    unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t count;
+    if ((uint32_t)(old >> 32) == tag) {
+        count = (uint32_t)old + 1u;
+    } else {
+        unsigned long long cur = old + 1ull;
+        while (true) {
+            if ((uint32_t)(cur >> 32) == tag) {
+                old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                count = (uint32_t)old + 1u;
+                break;
+            }
+            if (__hip_atomic_compare_exchange_strong(c, &cur, valid0 | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)) {
+                count = 1u;
+                break;
+            }
+        }
+    }
+    if (count == target) __hip_atomic_store(c, valid0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return count;
+}
+
 // Arrival of one workgroup at counter c, after every thread wrote what it
 // publishes with device-scope stores: returns true, in every thread, in the
 // last of `target` workgroups to arrive.  The counter holds
 // (tag << 32 | arrivals); between calls it is (tag, 0), which the last arrival
-// restores.  Normally an arrival is one fetch-add.  A counter word without its
-// tag (never used, or overwritten) is replaced by (tag, 1) with a
-// compare-exchange by the first workgroup to find it so; the others then count
-// on the valid word.  The exchange loop only runs in that case and ends once
-// any workgroup has installed the word.
+// restores (see arrive_one).
 __device__ __forceinline__ bool arrive_count(unsigned long long* c, uint32_t target, int* s_flag) {
     wait_vm_all();    // this thread's device-scope stores are acknowledged
     __syncthreads();  // ... in every thread of the workgroup
-    if (threadIdx.x == 0) {
-        const uint32_t tag = ctr_tag(c);
-        const unsigned long long valid0 = (unsigned long long)tag << 32;
-        unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t count;
-        if ((uint32_t)(old >> 32) == tag) {
-            count = (uint32_t)old + 1u;
-        } else {
-            unsigned long long cur = old + 1ull;
-            while (true) {
-                if ((uint32_t)(cur >> 32) == tag) {
-                    old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    count = (uint32_t)old + 1u;
-                    break;
-                }
-                if (__hip_atomic_compare_exchange_strong(c, &cur, valid0 | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT)) {
-                    count = 1u;
-                    break;
-                }
-            }
-        }
-        const bool last = count == target;
-        if (last) __hip_atomic_store(c, valid0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = last ? 1 : 0;
-    }
+    if (threadIdx.x == 0) *s_flag = arrive_one(c, target) == target ? 1 : 0;
     __syncthreads();
     return *s_flag != 0;
 }

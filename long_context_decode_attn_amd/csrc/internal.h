@@ -176,14 +176,18 @@ struct TopkArgs {
     uint32_t* q_codes;          // [B, Hq]: where the encoded query codes go
     int chunks;                 // ceil(n / chunk_len) <= 64
     int64_t chunk_len;
-    // One launch with a histogram exchange (sig_topk_unit.hip): each (b, KV
-    // head) unit's positions in `parts` parts of part_len positions.
+    // One launch with two exchanges (sig_topk_unit.hip): each (b, KV head)
+    // unit's steps of 4,096 positions dealt round robin to `parts` workgroups,
+    // part_len / 4096 steps each.
     int parts;
     int part_len;
-    unsigned long long* bar;    // ws: [B * Hkv] arrival counters
-    uint32_t* epoch;            // ws: [B * Hkv] release epochs
-    uint32_t* phist;            // ws: [B * Hkv][parts][3][4][topk_unit_row_words()] published histograms
-    int spin_max;               // polls of the exchange wait
+    unsigned long long* bar;    // ws: [B * Hkv] arrival counters of the histogram exchange
+    uint32_t* epoch;            // ws: [B * Hkv] its release epochs
+    uint32_t* phist;            // ws: [B * Hkv][parts][4][topk_unit_row_words()] published histograms
+    unsigned long long* rbar;   // ws: [B * Hkv] arrival counters of the step-record exchange
+    uint32_t* repoch;           // ws: [B * Hkv] its release epochs
+    uint32_t* srec;             // ws: [B * Hkv][topk_unit_rec_words()] published step records
+    int spin_max;               // polls of an exchange wait
     // GATHER-ATT of the selected rows in the same launch (sparse_decode_step;
     // one-launch form only): gk == null means TOPK alone.
     const void* gq;             // [B, Hq, 128]
@@ -198,11 +202,13 @@ struct TopkArgs {
     float scale_log2;           // log2(e) / sqrt(d)
 };
 int topk_chunk_len(int64_t n, int units);   // units: B * Hkv
-// One launch per call with a histogram exchange (sig_topk_unit.hip): positions
-// per part of a (b, KV head) unit, 0 when that form does not apply (G > 4, or
-// the grid of units x parts exceeds `cus` workgroups, one per CU).
+// One launch per call with exchanges between workgroups (sig_topk_unit.hip):
+// positions per part (4096 x steps) of a (b, KV head) unit, 0 when that form
+// does not apply (G > 4, more than 64 steps of 4,096 positions, or the grid of
+// units x parts exceeds `cus` workgroups, one per CU).
 int topk_unit_part(int64_t n, int units, int G, int cus);
 int topk_unit_row_words();
+int topk_unit_rec_words();
 // dtype: the rows' type when a.gk is set (LCDA_F32 or LCDA_BF16).
 hipError_t launch_topk_unit(const TopkArgs& a, int dtype, hipStream_t st);
 int topk_hist_row();

@@ -1,6 +1,7 @@
 // sig_topk_unit.hip - HashAttention SCORE + TOPK over 32-bit signatures in one
-// launch: the distances are computed once and kept in LDS, and the workgroups
-// that share a (batch item, KV head) exchange their histograms.
+// launch (and, for sparse_decode_step, GATHER-ATT over the selected rows in the
+// same launch): the distances are computed once and kept in LDS, and the
+// workgroups that share a (batch item, KV head) exchange what they counted.
 //
 // SCORE(k_i, q) = -popcount(h_i XOR h_q) ("HashAttention: Semantic Sparsity
 // for Faster Inference", slide "A 32-bit signature makes scoring cheap",
@@ -13,50 +14,54 @@
 // quota: every position with d < t is in, and of the positions with d == t the
 // lowest `quota` are.
 //
-// Work unit: one (b, KV head) with its G <= 4 query heads, whose n positions
-// are cut into Q parts of P positions; one workgroup of 16 wavefronts per
-// part, all of a launch resident at once (the host launches this kernel only
-// when the grid fits the device one workgroup per CU).
-//   1. The part's codes are read once (each load instruction of a wavefront
+// Work unit: one (b, KV head) with its G <= 4 query heads.  Its n positions are
+// cut into steps of 4,096, dealt round robin to the unit's Q workgroups (step s
+// to workgroup s mod Q, D = 1, 2, 4 or 8 steps each), so that the lowest
+// positions - where the tie rule puts the ties it takes, and with them most of
+// the selected rows - are spread over all of them.  One workgroup of 16
+// wavefronts per (unit, part); the host launches this kernel only when the
+// grid fits the device one workgroup per CU.
+//   1. Each step's codes are read once (one load instruction of a wavefront
 //      covers 1 KB of consecutive codes) and every (position, query head)
 //      distance goes into a 33-bin histogram (one LDS copy per lane, so that
 //      the 64 increments of one instruction fall into distinct banks; two
 //      heads share a copy's word as 16-bit counts) and, as one byte, into the
-//      part's LDS distance array, head by head.  The sink and recent window portions of the part get histograms
-//      of their own.
-//   2. Every workgroup publishes its three histograms per head, as cumulative
-//      counts (C[d] = positions with distance below d), with device-scope stores and arrives at the unit's counter; the last to
-//      arrive releases the others by advancing the unit's epoch word.  A
-//      workgroup that waits too long (its partners not resident) computes the
-//      missing histograms from the codes itself, so the result never depends
-//      on co-residency.
-//   3. One wavefront per query head reads every part's histograms (lane =
-//      part): t and the quota, the ties before this part, and every part's
-//      output count (its positions below t, the ties it takes - the lowest
-//      ones first - and its window positions outside the top m), hence this
-//      part's output offset.
-//   4. Each thread owns 4 D consecutive positions of the part and compares
+//      part's LDS distance array, head by head.
+//   2. Every workgroup publishes its histograms (cumulative counts, C[d] =
+//      positions with distance below d) with device-scope stores and arrives
+//      at the unit's counter; the last to arrive releases the others by
+//      advancing the unit's epoch word.  One wavefront per query head then
+//      finds t and the quota from the summed histograms.
+//   3. Each thread owns 4 D consecutive positions of one step and compares
 //      their distance bytes, four at a time, with t and t + 1 (byte-parallel
 //      subtraction: every byte is below 128, so the sign bit of byte j of
 //      (d | 0x80) - t says whether d_j >= t); a dot product with 1, 2, 4, 8
-//      turns four sign bits into a nibble of the thread's position masks.  A
-//      workgroup scan of the tie counts gives each thread the ties it takes, a
-//      second of the selected counts its output offset; it stores its
-//      positions in order.
+//      turns four sign bits into a nibble of the thread's position masks.  Per
+//      step the workgroup counts the positions below t, the ties and the
+//      window positions, and the workgroups exchange these step records the
+//      same way; one wavefront per query head (lane = step) turns them into
+//      the ties before each step (the ties taken are the lowest ones) and each
+//      step's output count and offset.
+//   4. Scans of the tie counts and of the selected counts inside each step
+//      place every thread's positions; it stores them in order.
+// A workgroup that waits too long for its partners (not resident together)
+// counts what they publish from the codes itself, so the result never depends
+// on co-residency.
 // With the rows of the cache (sparse_decode_step) the same workgroups then run
 // GATHER-ATT ("HashAttention ...", slide "Only selection is approximate;
 // selected KV stay in full form": attention renormalised over the selected
 // rows, read straight from the cache by position):
-//   5. each part's selected positions of every head also go into an LDS list
-//      (as offsets in the part); 16 / G wavefronts per query head walk the
-//      head's list, four rows per load instruction (16 lanes per row, 8 values
-//      per lane), with an online softmax in base 2, and merge into one partial
-//      state (m, l, acc) per head and part;
+//   5. the part's selected positions of every head also go into an LDS list;
+//      16 / G wavefronts per query head walk the head's list, four rows per load
+//      instruction (16 lanes per row, 8 values per lane), with an online softmax
+//      in base 2, and merge into one partial state (m, l, acc) per head and
+//      part;
 //   6. the last workgroup of the unit to publish its partial states merges the
 //      parts exactly through their maxima (the split identity of the dense path).
-// The workspace holds the counters, epochs and histograms; the counter word is
-// (tag << 32 | arrivals) as for the split pass (see arrive_count), so no call
-// needs it cleared, and every call leaves it at (tag, 0).
+// The workspace holds the counters, epochs, histograms and step records; the
+// counter words are (tag << 32 | arrivals) as for the split pass (see
+// arrive_one), so no call needs them cleared, and every call leaves them at
+// (tag, 0).
 
 #include <type_traits>
 
@@ -69,19 +74,28 @@ namespace {
 
 constexpr int kUT = 1024;                       // threads per workgroup
 constexpr int kUW = kUT / 64;                   // wavefronts
+constexpr int kStepPos = 4 * kUT;               // positions per step
 constexpr int kUBins = 33;
 constexpr int kURow = 36;                       // words per published histogram row (34 cumulative counts)
+constexpr int kRec = 8;                         // words per step record of a head (7 counts)
+constexpr int kMaxSteps = 64;                   // steps per unit (one lane each)
 constexpr uint32_t kHi = 0x80808080u;
 constexpr uint32_t kPadDist = 0x7Fu;            // distance byte of a position past the end: never < t, never t
+
+// A step record of one head: its positions below t, its ties (d == t), its
+// window positions, and the sink (ws) and recent (wr) window positions below t
+// and at t.
+enum { kBelow = 0, kTies, kWin, kWsBelow, kWsTies, kWrBelow, kWrTies, kRecCount };
 
 template <int D>
 struct __align__(16) UnitSmem {
     uint32_t dist[4][kUT * D];                  // [head][dword]: the part's distances, a byte per position
     uint32_t cnt[2 * (kUBins + 1) * 64];        // [head pair][bin][lane]: heads 2p, 2p + 1 in the low and high
                                                 // 16 bits; bin 33 takes positions past the end
-    uint32_t win[2][4][kUBins];                 // the part's sink and recent window portions
-    uint32_t s_w[2][kUW];                       // block scans
-    int s_sel[4][4];                            // per head: t, quota, ties before the part, output offset
+    uint32_t rec[D][4][kRec];                   // [local step][head] records
+    uint32_t s_w[2][kUW];                       // segment scans
+    int s_sel[4][2];                            // per head: t, quota
+    int s_step[D][4][3];                        // [local step][head]: ties before the step, output offset, count
     int s_total[4];
     uint32_t s_code[4];
     int s_flag;
@@ -101,10 +115,13 @@ __device__ __forceinline__ uint32_t lane_val(uint32_t x, int l) {   // l uniform
     return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
 }
 
-// Exclusive prefixes of x0 and x1 over the workgroup's threads in order, and
-// their totals.  Ends with a barrier after its last LDS read.
-__device__ __forceinline__ void block_scan2(uint32_t x0, uint32_t x1, uint32_t (*s_w)[kUW], uint32_t& e0,
-                                            uint32_t& e1, uint32_t& t0, uint32_t& t1) {
+__device__ __forceinline__ uint32_t wave_total(uint32_t x) { return lane_val(scan_incl(x), 63); }
+
+// Exclusive prefixes of x0 and x1 over the threads of the calling thread's
+// segment: the run of whole wavefronts from wavefront seg0 to the next
+// segment's first.  Ends with a barrier after its last LDS read.
+__device__ __forceinline__ void seg_scan2(uint32_t x0, uint32_t x1, int seg0, uint32_t (*s_w)[kUW], uint32_t& e0,
+                                          uint32_t& e1) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint32_t i0 = scan_incl(x0), i1 = scan_incl(x1);
     if (lane == 63) {
@@ -112,26 +129,23 @@ __device__ __forceinline__ void block_scan2(uint32_t x0, uint32_t x1, uint32_t (
         s_w[1][w] = i1;
     }
     __syncthreads();
-    uint32_t b0 = 0, b1 = 0, a0 = 0, a1 = 0;
+    uint32_t b0 = 0, b1 = 0;
 #pragma unroll
     for (int k = 0; k < kUW; ++k) {
-        const uint32_t v0 = s_w[0][k], v1 = s_w[1][k];
-        b0 += k < w ? v0 : 0u;
-        b1 += k < w ? v1 : 0u;
-        a0 += v0;
-        a1 += v1;
+        const bool in = k >= seg0 && k < w;
+        b0 += in ? s_w[0][k] : 0u;
+        b1 += in ? s_w[1][k] : 0u;
     }
     __syncthreads();
     e0 = b0 + i0 - x0;
     e1 = b1 + i1 - x1;
-    t0 = a0;
-    t1 = a1;
 }
 
-// Dword dw (positions 4 dw .. 4 dw + 3) of a head's distance array: thread T of
-// the compaction owns dwords D T .. D T + D - 1.  With D = 8 (two 16-byte
-// chunks per thread) the chunks of a thread are swapped for odd T / 8, so that
-// 16 neighbouring threads' reads of one chunk each fall into distinct banks.
+// Dword dw of a head's distance array (local positions 4 dw .. 4 dw + 3; local
+// step dw / 1024): thread T of the compaction owns dwords D T .. D T + D - 1.
+// With D = 8 (two 16-byte chunks per thread) the chunks of a thread are
+// swapped for odd T / 8, so that 16 neighbouring threads' reads of one chunk
+// each fall into distinct banks.
 template <int D>
 __device__ __forceinline__ int dist_slot(int dw) {
     if (D != 8) return dw;
@@ -147,62 +161,123 @@ __device__ __forceinline__ uint32_t low_bits(int64_t c) {
 // The four sign bits of a dword of distance bytes as a nibble.
 __device__ __forceinline__ uint32_t nibble(uint32_t s) { return __builtin_amdgcn_udot4(s >> 7, 0x08040201u, 0u, false); }
 
-// Histograms of the positions [beg, end) of a unit for heads g < G, counted
-// into the LDS copies (which the caller has zeroed) and, for the positions in
-// the windows, into win; reads the codes from memory.  The fallback of a
-// workgroup whose partners did not arrive in time.
-template <int D>
-__device__ void count_part(const TopkArgs& a, UnitSmem<D>& sm, const uint32_t* ks, const uint32_t (&q)[4], int beg,
-                           int end, int s_end, int r_beg) {
-    const int lane = threadIdx.x & 63;
-    for (int i = beg + (int)threadIdx.x; i < end; i += kUT) {
-        const uint32_t x = ks[i];
-        const int pt = i < s_end ? 0 : (i >= r_beg ? 1 : -1);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if (g < a.G) {
-                const uint32_t d = (uint32_t)__builtin_popcount(x ^ q[g]);
-                __hip_atomic_fetch_add(&sm.cnt[(((g >> 1) * (kUBins + 1) + d) << 6) + lane], 1u << (16 * (g & 1)),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (pt >= 0)
-                    __hip_atomic_fetch_add(&sm.win[pt][g][d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-        }
-    }
-}
+// Global step of local step ls of workgroup `part` (of Q).
+__device__ __forceinline__ int global_step(int ls, int Q, int part) { return ls * Q + part; }
 
-// Publish the part's histograms as cumulative counts: row (kind, head) of
-// prow = [part, sink, recent][head][kURow] gets C[d], d = 0 .. 33, the number
-// of the kind's positions with distance below d.  Wavefront 4 kind + head
-// (lane = bin) sums the bin over the lane copies and scans over the bins.
-template <int D>
-__device__ __forceinline__ void publish(const TopkArgs& a, const UnitSmem<D>& sm, uint32_t* prow) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (w >= 12) return;
-    const int kind = w >> 2, g = w & 3;
-    uint32_t v = 0;
-    if (g < a.G && lane < kUBins) {
-        if (kind == 0) {
-            const uint32_t* r = sm.cnt + (((g >> 1) * (kUBins + 1) + lane) << 6);
-            const int sh = 16 * (g & 1);
-#pragma unroll 8
-            for (int c = 0; c < 64; ++c) v += (r[(c + lane) & 63] >> sh) & 0xFFFFu;   // lane-rotated: distinct banks
-        } else {
-            v = sm.win[kind - 1][g][lane];
-        }
+// The window positions are [0, s_end) and [r_beg, n): every one of them is
+// selected, for every head, and they take the first s_end and the last
+// n - r_beg entries of each index list.  The unit's workgroups share them out
+// in contiguous runs [w0, w1) of the window sequence (k -> k below s_end, else
+// r_beg + k - s_end).
+struct Windows {
+    int s_end, r_beg, n;
+    int w0, w1;   // this workgroup's run
+    __device__ __forceinline__ int count() const { return s_end + (n - r_beg); }
+    __device__ __forceinline__ int pos(int k) const { return k < s_end ? k : r_beg + (k - s_end); }
+    // Window positions of global step gs: the sink portion (a prefix of the
+    // step) and the recent portion (a suffix).
+    __device__ __forceinline__ int sink_in(int gs) const {
+        const int sb = gs * kStepPos, se = min(n, sb + kStepPos);
+        return max(0, min(se, s_end) - sb);
     }
-    const uint32_t incl = scan_incl(v);
-    uint32_t* row = prow + (kind * 4 + g) * kURow;
-    if (lane < kUBins) store_dev(row + lane + 1, incl);
-    if (lane == 0) store_dev(row, 0u);
+    __device__ __forceinline__ int recent_in(int gs) const {
+        const int sb = gs * kStepPos, se = min(n, sb + kStepPos);
+        return max(0, se - max(sb, r_beg));
+    }
+};
+
+// Thread 0 of one of the unit's Q workgroups, once the workgroup's published
+// stores are acknowledged: arrival at counter c and, but for the last to
+// arrive, a wait of at most spin_max polls for the epoch word ep to move on
+// from e, the value it held before any of them arrived (the last arrival
+// advances it).  Returns whether the workgroup was released.
+__device__ __forceinline__ int arrive_wait(unsigned long long* c, uint32_t* ep, uint32_t e, uint32_t Q, int spin_max) {
+    if (arrive_one(c, Q) == Q) {
+        __hip_atomic_store(ep, e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return 1;
+    }
+    for (int it = 0; it < spin_max; ++it) {
+        if (__hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != e) return 1;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return 0;
 }
 
 template <int D>
 __device__ __forceinline__ void zero_counts(UnitSmem<D>& sm) {
     for (int k = threadIdx.x; k < 2 * (kUBins + 1) * 64; k += kUT) sm.cnt[k] = 0u;
-    for (int k = threadIdx.x; k < 2 * 4 * kUBins; k += kUT) (&sm.win[0][0][0])[k] = 0u;
 }
 
+// Histograms of part p's steps for heads g < G, counted from the codes into the
+// LDS copies (zeroed by the caller): the fallback of a workgroup whose
+// partners did not arrive in time.
+template <int D>
+__device__ void count_part(const TopkArgs& a, UnitSmem<D>& sm, const uint32_t* ks, const uint32_t (&q)[4], int p) {
+    const int lane = threadIdx.x & 63;
+    const int n = (int)a.n;
+    for (int ls = 0; ls < D; ++ls) {
+        const int beg = global_step(ls, a.parts, p) * kStepPos;
+        for (int i = beg + (int)threadIdx.x; i < min(n, beg + kStepPos); i += kUT) {
+            const uint32_t x = ks[i];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (g < a.G) {
+                    const uint32_t d = (uint32_t)__builtin_popcount(x ^ q[g]);
+                    __hip_atomic_fetch_add(&sm.cnt[(((g >> 1) * (kUBins + 1) + d) << 6) + lane], 1u << (16 * (g & 1)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            }
+        }
+    }
+}
+
+// Publish the histograms in the LDS copies as cumulative counts: row g of prow
+// ([head][kURow]) gets C[d], d = 0 .. 33.  Wavefront g (lane = bin) sums the
+// bin over the lane copies and scans over the bins.
+template <int D>
+__device__ __forceinline__ void publish_hist(const TopkArgs& a, const UnitSmem<D>& sm, uint32_t* prow) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (w >= 4) return;
+    uint32_t v = 0;
+    if (w < a.G && lane < kUBins) {
+        const uint32_t* r = sm.cnt + (((w >> 1) * (kUBins + 1) + lane) << 6);
+        const int sh = 16 * (w & 1);
+#pragma unroll 8
+        for (int c = 0; c < 64; ++c) v += (r[(c + lane) & 63] >> sh) & 0xFFFFu;   // lane-rotated: distinct banks
+    }
+    const uint32_t incl = scan_incl(v);
+    uint32_t* row = prow + w * kURow;
+    if (lane < kUBins) store_dev(row + lane + 1, incl);
+    if (lane == 0) store_dev(row, 0u);
+}
+
+// Adds the calling wavefront's share of a step record (per head g < G: bit
+// masks of positions below t and at t, and the window masks) to rec[g], with
+// one LDS atomic per count.  Every lane of the wavefront takes part; its
+// positions lie in one step.
+__device__ __forceinline__ void add_records(uint32_t (*rec)[kRec], int G, const uint32_t* lt4, const uint32_t* eq4,
+                                            uint32_t ws, uint32_t wr) {
+    const uint32_t win = (uint32_t)__builtin_popcount(ws | wr);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        if (g < G) {
+            const uint32_t l = lt4[g], e = eq4[g];
+            const uint32_t v0 = (uint32_t)__builtin_popcount(l) | ((uint32_t)__builtin_popcount(e) << 16);
+            const uint32_t v1 = win | ((uint32_t)__builtin_popcount(l & ws) << 16);
+            const uint32_t v2 = (uint32_t)__builtin_popcount(e & ws) | ((uint32_t)__builtin_popcount(l & wr) << 16);
+            const uint32_t v3 = (uint32_t)__builtin_popcount(e & wr);
+            const uint32_t s0 = wave_total(v0), s1 = wave_total(v1), s2 = wave_total(v2), s3 = wave_total(v3);
+            if ((threadIdx.x & 63) == 0) {
+                uint32_t* r = rec[g];
+                const uint32_t add[kRecCount] = {s0 & 0xFFFFu, s0 >> 16, s1 & 0xFFFFu, s1 >> 16, s2 & 0xFFFFu,
+                                                 s2 >> 16, s3};
+#pragma unroll
+                for (int k = 0; k < kRecCount; ++k)
+                    __hip_atomic_fetch_add(r + k, add[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+}
 
 // Rows of 128 values as 8 floats per lane (16 lanes per row).
 template <typename T>
@@ -246,13 +321,18 @@ struct PartMerge {
     float* alpha;
 };
 
-// GATHER-ATT over this part's selected positions of each query head, then the
-// merge of the parts (see the file comment, steps 5 and 6).
+// GATHER-ATT over this part's share of the selected positions of each query
+// head, then the merge of the parts (see the file comment, steps 5 and 6).
+// Head g's share: the part's cntg[g] selected positions outside the windows,
+// local step by local step - in LDS from lbase[g] (local position numbers
+// 4096 ls + offset in the step) when in_lds, else in the index list at each
+// local step's output offset past its sink portion - then the part's run of
+// window positions.
 template <typename T, int D>
 __device__ void gather_part(const TopkArgs& a, UnitSmem<D>& sm, const uint16_t* lst, bool in_lds, const int (&cntg)[4],
-                            const int (&lbase)[4], int unit, int part, int64_t row0, int b, int h, int pbeg) {
+                            const int (&lbase)[4], const Windows& win, int unit, int part, int64_t row0, int b, int h) {
     constexpr int U = sizeof(T) == 2 ? 4 : 2;   // rows per lane group and step (fewer for fp32 rows)
-    constexpr int kStep = 4 * U;         // rows per wavefront and step
+    constexpr int kStep = 4 * U;                 // rows per wavefront and step
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform values in scalar registers
     const int j = lane >> 4, c16 = lane & 15;
@@ -264,12 +344,14 @@ __device__ void gather_part(const TopkArgs& a, UnitSmem<D>& sm, const uint16_t* 
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (gw < G) {
         const int64_t row = row0 + gw;
-        const int cnt = __builtin_amdgcn_readfirstlane(gw == 0 ? cntg[0] : gw == 1 ? cntg[1] : gw == 2 ? cntg[2] : cntg[3]);
+        const int own = __builtin_amdgcn_readfirstlane(gw == 0 ? cntg[0] : gw == 1 ? cntg[1] : gw == 2 ? cntg[2] : cntg[3]);
+        const int wbeg = __builtin_amdgcn_readfirstlane(win.w0 - own);   // entry t >= own: window entry wbeg + t
+        const int cnt = own + (win.w1 - win.w0);
         const int lb = __builtin_amdgcn_readfirstlane(gw == 0 ? lbase[0] : gw == 1 ? lbase[1] : gw == 2 ? lbase[2] : lbase[3]);
         const int64_t head = (a.kv_batch_stride == 0 ? 0 : (int64_t)b * a.kv_batch_stride) + (int64_t)h * a.n * kD;
         const T* kh = static_cast<const T*>(a.gk) + head + 8 * c16;
         const T* vh = static_cast<const T*>(a.gv) + head + 8 * c16;
-        const int32_t* ilist = a.idx + row * a.cap + sm.s_sel[gw][3];   // the part's entries of the index list
+        const uint32_t* ilist = reinterpret_cast<const uint32_t*>(a.idx + row * a.cap);
         float qv[8];
         {
             GRow<T> x;
@@ -279,17 +361,37 @@ __device__ void gather_part(const TopkArgs& a, UnitSmem<D>& sm, const uint16_t* 
         struct Step {
             GRow<T> k[U], v[U];
         };
-        // The rows of entries t0 + 4 u + j of the part's list (clamped to the
-        // last entry; rows past cnt are masked in compute).  LISTED: the
-        // positions come from the LDS list; otherwise from the index list the
-        // workgroup has written (a list too long for LDS).
+        // Own entry t of the head's list -> its position, from the index list
+        // the workgroup has written (a list too long for LDS).
+        auto from_idx = [&](int t) -> int {
+            int ls = 0, base = 0;
+#pragma unroll
+            for (int k = 0; k < D - 1; ++k) {
+                const int gs = global_step(k, Q, part);
+                const int c = sm.s_step[k][gw][2] - win.sink_in(gs) - win.recent_in(gs);   // 0 past the end
+                if (ls == k && t >= base + c) {
+                    ls = k + 1;
+                    base += c;
+                }
+            }
+            const int gs = global_step(ls, Q, part);
+            return (int)load_dev_u32(ilist + sm.s_step[ls][gw][1] + win.sink_in(gs) + (t - base));
+        };
+        // The rows of entries t0 + 4 u + j of the list (clamped to the last
+        // entry; rows past cnt are masked in compute).
         auto fetch = [&](Step& st, int t0, auto listed) {
             int pos[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int t = min(t0 + 4 * u + j, cnt - 1);
-                if constexpr (decltype(listed)::value) pos[u] = pbeg + (int)lst[lb + t];
-                else pos[u] = (int)load_dev_u32(reinterpret_cast<const uint32_t*>(ilist) + t);
+                if (t >= own) {
+                    pos[u] = win.pos(wbeg + t);
+                } else if constexpr (decltype(listed)::value) {
+                    const int loc = (int)lst[lb + t];
+                    pos[u] = global_step(loc >> 12, Q, part) * kStepPos + (loc & (kStepPos - 1));
+                } else {
+                    pos[u] = from_idx(t);
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -398,40 +500,47 @@ __device__ void gather_part(const TopkArgs& a, UnitSmem<D>& sm, const uint16_t* 
     if (Q == 1) return;
     // ---- 6. the last workgroup of the unit merges the parts ----------------------------------
     if (!arrive_count(a.bar2 + unit, (uint32_t)Q, &sm.s_flag)) return;
-    if (w < G) {
+    const int wv = tid >> 6;
+    if (wv < G) {
         PartMerge pm{Q, a.pml, a.pacc, nullptr, nullptr, a.out, a.alpha};
-        combine_row(pm, row0 + w, lane);
+        combine_row(pm, row0 + wv, lane);
     }
 }
 
-// D: dwords per thread and head; a part holds P = 4096 D positions.  T: the
-// rows' type for the fused GATHER-ATT (float or uint16_t for bf16), void for
-// TOPK alone.
+// D: steps of 4,096 positions per workgroup (1024 D dwords of distances per
+// head).  T: the rows' type for the fused GATHER-ATT (float or uint16_t for
+// bf16), void for TOPK alone.
 template <int D, bool SCORES, typename T>
 __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
-    constexpr int P = 4 * kUT * D;
+    constexpr bool kGather = !std::is_void<T>::value;
     __shared__ UnitSmem<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int Q = a.parts;
     // Workgroup -> (unit, part): part-major, so that with a multiple of 8 units
     // the parts of a unit run on one XCD (workgroups go round the 8 XCDs in
-    // turn) and every XCD holds every part position equally.
+    // turn).
     const int units = a.B * a.Hkv;
     const int unit = blockIdx.x % units, part = blockIdx.x / units;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
     const int G = a.G;
     const int n = (int)a.n;
-    const int pbeg = part * P, pend = min(n, pbeg + P);
+    const int NS = (n + kStepPos - 1) / kStepPos;   // the unit's steps (<= kMaxSteps)
     const uint32_t* ks = a.key_sigs + ((int64_t)b * a.Hkv + h) * a.n;
     const int64_t row0 = (int64_t)b * a.Hq + (int64_t)h * G;
     const int s_end = (int)min(a.n_sink, a.n);
     const int r_beg = (int)max((int64_t)s_end, a.n - a.n_recent);
     const bool vec = (n & 3) == 0;   // uniform
+    // Thread 0: the exchanges' epochs as they stand before this call's arrivals.
+    uint32_t e_hist = 0, e_rec = 0;
+    if (tid == 0 && Q > 1) {
+        e_hist = __hip_atomic_load(a.epoch + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        e_rec = __hip_atomic_load(a.repoch + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- 1. distances ------------------------------------------------------------------
     // The query codes first (so that waiting for them is not waiting for all the
-    // codes), then step s: positions pbeg + 4 (1024 s + tid) + e, e < 4; every
-    // step's codes are requested at once.
+    // codes), then local step ls: positions 4096 global_step(ls) + 4 tid + e,
+    // e < 4; every step's codes are requested at once.
     uint32_t q[4];
     if (a.q == nullptr) {
 #pragma unroll
@@ -439,13 +548,13 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
     }
     u32x4 xc[D];
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-        const int i = pbeg + 4 * (kUT * s + tid);
+    for (int ls = 0; ls < D; ++ls) {
+        const int i = global_step(ls, Q, part) * kStepPos + 4 * tid;
         if (vec) {
-            xc[s] = ld16(ks + min(i, n - 4));
+            xc[ls] = ld16(ks + min(i, n - 4));
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xc[s][e] = ks[min(i + e, n - 1)];
+            for (int e = 0; e < 4; ++e) xc[ls][e] = ks[min(i + e, n - 1)];
         }
     }
     if (a.q != nullptr) {   // uniform: the query codes are encoded here (T_map), while the codes load
@@ -475,21 +584,23 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
         __syncthreads();   // the staging area is about to hold distances
     }
     zero_counts(sm);
+    for (int k = tid; k < D * 4 * kRec; k += kUT) (&sm.rec[0][0][0])[k] = 0u;
     __syncthreads();
 
     uint32_t* mycnt = sm.cnt + lane;
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-        const int i = pbeg + 4 * (kUT * s + tid);
-        const int dw = dist_slot<D>(kUT * s + tid);
-        if (pbeg + 4 * kUT * (s + 1) <= n) {   // uniform: every position of the step is below n
+    for (int ls = 0; ls < D; ++ls) {
+        const int gs = global_step(ls, Q, part);
+        const int i = gs * kStepPos + 4 * tid;
+        const int dw = dist_slot<D>(kUT * ls + tid);
+        if ((gs + 1) * kStepPos <= n) {   // uniform: every position of the step is below n
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 if (g < G) {   // uniform
                     uint32_t pk = 0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t d = (uint32_t)__builtin_popcount(xc[s][e] ^ q[g]);
+                        const uint32_t d = (uint32_t)__builtin_popcount(xc[ls][e] ^ q[g]);
                         __hip_atomic_fetch_add(mycnt + (((g >> 1) * (kUBins + 1) + d) << 6), 1u << (16 * (g & 1)),
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                         pk |= d << (8 * e);
@@ -506,7 +617,7 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const bool ok = i + e < n;
-                        const uint32_t d = ok ? (uint32_t)__builtin_popcount(xc[s][e] ^ q[g]) : (uint32_t)kUBins;
+                        const uint32_t d = ok ? (uint32_t)__builtin_popcount(xc[ls][e] ^ q[g]) : (uint32_t)kUBins;
                         __hip_atomic_fetch_add(mycnt + (((g >> 1) * (kUBins + 1) + d) << 6), 1u << (16 * (g & 1)),
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                         pk |= (ok ? d : kPadDist) << (8 * e);
@@ -518,102 +629,40 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
         }
     }
     __syncthreads();
-    // Window portions of the part, from the distance bytes.
-    {
-        const int wb0 = pbeg, we0 = min(pend, s_end);           // sink portion [wb0, we0)
-        const int wb1 = max(pbeg, r_beg), we1 = pend;          // recent portion [wb1, we1)
-        for (int k = tid; k < max(we0 - wb0, 0) + max(we1 - wb1, 0); k += kUT) {
-            const int pt = k < max(we0 - wb0, 0) ? 0 : 1;
-            const int i = pt == 0 ? wb0 + k : wb1 + (k - max(we0 - wb0, 0));
-            const int r = i - pbeg;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                if (g < G) {
-                    const uint32_t d = (sm.dist[g][dist_slot<D>(r >> 2)] >> (8 * (r & 3))) & 0xFFu;
-                    __hip_atomic_fetch_add(&sm.win[pt][g][d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
-            }
-        }
-    }
-    __syncthreads();
 
-    // ---- 2. exchange --------------------------------------------------------------------------
-    uint32_t* phist = a.phist + (int64_t)unit * Q * 3 * 4 * kURow;
-    publish(a, sm, phist + (int64_t)part * 3 * 4 * kURow);
-    wait_vm_all();      // this thread's histogram stores are acknowledged
-    __syncthreads();    // ... in every thread
+    // ---- 2. histogram exchange, threshold and quota ---------------------------------------
+    uint32_t* phist = a.phist + (int64_t)unit * Q * 4 * kURow;
+    publish_hist(a, sm, phist + (int64_t)part * 4 * kURow);
     if (Q > 1) {
-        if (tid == 0) {
-            uint32_t* ep = a.epoch + unit;
-            const uint32_t e = __hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            wait_vm_all();  // the epoch is read before this workgroup arrives
-            unsigned long long* c = a.bar + unit;
-            const uint32_t tag = ctr_tag(c);
-            const unsigned long long valid0 = (unsigned long long)tag << 32;
-            unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            uint32_t count;
-            if ((uint32_t)(old >> 32) == tag) {
-                count = (uint32_t)old + 1u;
-            } else {   // a word this library did not leave: install (tag, 1) or count on the installed word
-                unsigned long long cur = old + 1ull;
-                while (true) {
-                    if ((uint32_t)(cur >> 32) == tag) {
-                        old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        count = (uint32_t)old + 1u;
-                        break;
-                    }
-                    if (__hip_atomic_compare_exchange_strong(c, &cur, valid0 | 1ull, __ATOMIC_RELAXED,
-                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                        count = 1u;
-                        break;
-                    }
-                }
-            }
-            int released = 0;
-            if (count == (uint32_t)Q) {   // the last to arrive: reset the counter, then release the others
-                __hip_atomic_store(c, valid0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(ep, e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                released = 1;
-            } else {
-                for (int it = 0; it < a.spin_max; ++it) {
-                    if (__hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != e) {
-                        released = 1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            sm.s_flag = released;
-        }
+        wait_vm_all();      // this thread's histogram stores are acknowledged
+        __syncthreads();    // ... in every thread
+        if (tid == 0) sm.s_flag = arrive_wait(a.bar + unit, a.epoch + unit, e_hist, (uint32_t)Q, a.spin_max);
         __syncthreads();
         if (!sm.s_flag) {   // uniform: the partners did not arrive in time; count their parts here
             for (int p = 0; p < Q; ++p) {
                 if (p == part) continue;
                 zero_counts(sm);
                 __syncthreads();
-                count_part(a, sm, ks, q, p * P, min(n, p * P + P), s_end, r_beg);
+                count_part(a, sm, ks, q, p);
                 __syncthreads();
-                publish(a, sm, phist + (int64_t)p * 3 * 4 * kURow);
+                publish_hist(a, sm, phist + (int64_t)p * 4 * kURow);
                 __syncthreads();
             }
-            wait_vm_all();
-            __syncthreads();
         }
     }
-
-    // ---- 3. selection: one wavefront per query head ------------------------------------------
-    // Row (p, kind, g) of phist: C_p[d], d = 0 .. 33.
-    auto crow = [&](int p, int kind, int g) { return phist + (((int64_t)p * 3 + kind) * 4 + g) * kURow; };
-    if (w < G) {
+    wait_vm_all();
+    __syncthreads();
+    if (w < G) {   // one wavefront per query head
         const int g = w;
-        // Lane d: S[d] = positions of the unit with distance <= d; the requests
+        // Lane d: S[d] = the unit's positions with distance <= d; the requests
         // of up to 8 parts are issued together.
         uint32_t S = 0;
         if (lane < kUBins) {
             for (int p0 = 0; p0 < Q; p0 += 8) {
                 uint32_t v[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = p0 + k < Q ? load_dev_u32(crow(p0 + k, 0, g) + lane + 1) : 0u;
+                for (int k = 0; k < 8; ++k)
+                    v[k] = p0 + k < Q ? load_dev_u32(phist + ((int64_t)(p0 + k) * 4 + g) * kURow + lane + 1) : 0u;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) S += v[k];
             }
@@ -622,60 +671,27 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
         const uint64_t reach = __ballot(lane < kUBins && meff > 0 && S >= meff);
         const int t = reach ? (int)__builtin_ctzll(reach) : -1;
         const uint32_t below_all = t > 0 ? lane_val(S, t - 1) : 0u;
-        const uint32_t quota = t >= 0 ? meff - below_all : 0u;
-        // Lane p (a part): positions below t, ties, and the same for its window
-        // portions, from C_p[t] and C_p[t + 1] of each kind.
-        const int qb = lane * P, qe = min(n, qb + P);
-        const bool part_ok = lane < Q && t >= 0;
-        const bool in_s = part_ok && qb < s_end, in_r = part_ok && qe > r_beg;
-        const int tt = t >= 0 ? t : 0;
-        uint32_t c0 = 0, c1 = 0, s0 = 0, s1 = 0, r0 = 0, r1 = 0;
-        if (part_ok) {
-            c0 = load_dev_u32(crow(lane, 0, g) + tt);
-            c1 = load_dev_u32(crow(lane, 0, g) + tt + 1);
-        }
-        if (in_s) {
-            s0 = load_dev_u32(crow(lane, 1, g) + tt);
-            s1 = load_dev_u32(crow(lane, 1, g) + tt + 1);
-        }
-        if (in_r) {
-            r0 = load_dev_u32(crow(lane, 2, g) + tt);
-            r1 = load_dev_u32(crow(lane, 2, g) + tt + 1);
-        }
-        const uint32_t below = c0, ties = c1 - c0, ws_t = s1 - s0, wr_t = r1 - r0;
-        const uint32_t ties_before = scan_incl(ties) - ties;
-        const uint32_t taken = quota > ties_before ? min(quota - ties_before, ties) : 0u;
-        // The ties a part takes are its lowest ones: the sink portion (a prefix
-        // of the part) takes the first of them, the recent portion (a suffix)
-        // what is left after the ties before it.
-        const uint32_t tk_s = min(ws_t, taken);
-        const uint32_t tk_r = taken > ties - wr_t ? min(taken - (ties - wr_t), wr_t) : 0u;
-        const uint32_t win_n = (uint32_t)(max(min(qe, s_end) - qb, 0) + max(qe - max(qb, r_beg), 0));
-        const uint32_t cnt = lane < Q ? below + taken + win_n - (s0 + tk_s + r0 + tk_r) : 0u;
-        const uint32_t cincl = scan_incl(cnt);
-        // Every lane takes part in the reads (readlane outside divergent code).
-        const uint32_t my_tb = lane_val(ties_before, part);
-        const uint32_t my_off = lane_val(cincl, part) - lane_val(cnt, part);
-        const uint32_t total = lane_val(cincl, 63);
         if (lane == 0) {
             sm.s_sel[g][0] = t;
-            sm.s_sel[g][1] = (int)quota;
-            sm.s_sel[g][2] = (int)my_tb;
-            sm.s_sel[g][3] = (int)my_off;
-            sm.s_total[g] = (int)total;
+            sm.s_sel[g][1] = t >= 0 ? (int)(meff - below_all) : 0;
         }
     }
     __syncthreads();
 
-    // ---- 4. ordered compaction -----------------------------------------------------------------
-    // Thread tid: positions P0 .. P0 + 4 D - 1 of the part (bit j of its masks).
-    const int P0 = pbeg + 4 * D * tid;
-    uint32_t lt[4], eq[4], tiesv[4];
+    // ---- 3. masks, step records and their exchange ------------------------------------------
+    // Thread tid: local dwords D tid .. D tid + D - 1, all in local step ls_me;
+    // bit j of its masks is position P0 + j.
+    const int ls_me = (D * tid) >> 10;
+    const int P0 = global_step(ls_me, Q, part) * kStepPos + 4 * ((D * tid) & 1023);
+    int tg[4];
+    uint32_t lt[4], eq[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        lt[g] = eq[g] = tiesv[g] = 0u;
+        lt[g] = eq[g] = 0u;
+        tg[g] = -1;
         if (g < G) {
             const int t = sm.s_sel[g][0];
+            tg[g] = t;
             const uint32_t T0 = t >= 0 ? (uint32_t)t * 0x01010101u : 0u;   // t = -1 (m = 0): nothing below
             const uint32_t T1 = t >= 0 ? (uint32_t)(t + 1) * 0x01010101u : 0u;
             uint32_t l = 0, le = 0;
@@ -687,23 +703,113 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
             }
             lt[g] = l;
             eq[g] = le & ~l;
-            tiesv[g] = __builtin_popcount(eq[g]);
         }
     }
-    uint32_t te01, te23, tt01, tt23;
-    block_scan2(tiesv[0] | (tiesv[1] << 16), tiesv[2] | (tiesv[3] << 16), sm.s_w, te01, te23, tt01, tt23);
-    const uint32_t winm = (low_bits(s_end - P0) | ~low_bits(r_beg - P0)) & low_bits(n - P0) & low_bits(4 * D);
+    const uint32_t vmask = low_bits(n - P0) & low_bits(4 * D);
+    const uint32_t wsm = low_bits(s_end - P0) & vmask;
+    const uint32_t wrm = ~low_bits(r_beg - P0) & vmask;
+    add_records(sm.rec[ls_me], G, lt, eq, wsm, wrm);
+    __syncthreads();
+    uint32_t* grec = a.srec + (int64_t)unit * kMaxSteps * 4 * kRec;   // [global step][head][kRec]
+    for (int k = tid; k < D * 4 * kRec; k += kUT) {
+        const int ls = k / (4 * kRec), rest = k % (4 * kRec);
+        const int gs = global_step(ls, Q, part);
+        if (gs < NS) store_dev(grec + (int64_t)gs * 4 * kRec + rest, (&sm.rec[ls][0][0])[rest]);
+    }
+    if (Q > 1) {
+        wait_vm_all();
+        __syncthreads();
+        if (tid == 0) sm.s_flag = arrive_wait(a.rbar + unit, a.repoch + unit, e_rec, (uint32_t)Q, a.spin_max);
+        __syncthreads();
+        if (!sm.s_flag) {   // uniform: count the other workgroups' steps here, four positions per thread
+            for (int gs = 0; gs < NS; ++gs) {
+                if (gs % Q == part) continue;
+                for (int k = tid; k < 4 * kRec; k += kUT) (&sm.rec[0][0][0])[k] = 0u;
+                __syncthreads();
+                const int p0 = gs * kStepPos + 4 * tid;
+                uint32_t l4[4], e4[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    l4[g] = e4[g] = 0u;
+                    if (g < G && tg[g] >= 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (p0 + e < n) {
+                                const int d = __builtin_popcount(ks[p0 + e] ^ q[g]);
+                                l4[g] |= (d < tg[g] ? 1u : 0u) << e;
+                                e4[g] |= (d == tg[g] ? 1u : 0u) << e;
+                            }
+                        }
+                    }
+                }
+                const uint32_t vm = low_bits(n - p0) & 0xFu;
+                add_records(sm.rec[0], G, l4, e4, low_bits(s_end - p0) & vm, ~low_bits(r_beg - p0) & vm);
+                __syncthreads();
+                for (int k = tid; k < 4 * kRec; k += kUT)
+                    store_dev(grec + (int64_t)gs * 4 * kRec + k, (&sm.rec[0][0][0])[k]);
+                __syncthreads();
+            }
+        }
+    }
+    wait_vm_all();
+    __syncthreads();
+    // One wavefront per query head, lane = global step: the ties before each
+    // step, the ties it takes, its output count and offset.
+    if (w < G) {
+        const int g = w;
+        const uint32_t quota = (uint32_t)sm.s_sel[g][1];
+        uint32_t r[kRecCount];
+#pragma unroll
+        for (int k = 0; k < kRecCount; ++k)
+            r[k] = lane < NS ? load_dev_u32(grec + ((int64_t)lane * 4 + g) * kRec + k) : 0u;
+        const uint32_t ties = r[kTies];
+        const uint32_t ties_before = scan_incl(ties) - ties;
+        const uint32_t taken = quota > ties_before ? min(quota - ties_before, ties) : 0u;
+        // The ties a step takes are its lowest ones: its sink window portion (a
+        // prefix of the step) holds the first of them, its recent portion (a
+        // suffix) what is left after the ties before that portion.
+        const uint32_t tk_s = min(r[kWsTies], taken);
+        const uint32_t tk_r = taken > ties - r[kWrTies] ? min(taken - (ties - r[kWrTies]), r[kWrTies]) : 0u;
+        const uint32_t cnt = r[kBelow] + taken + r[kWin] - (r[kWsBelow] + tk_s + r[kWrBelow] + tk_r);
+        const uint32_t cincl = scan_incl(cnt);
+        const uint32_t total = lane_val(cincl, 63);
+#pragma unroll
+        for (int ls = 0; ls < D; ++ls) {   // every lane takes part in the reads (readlane outside divergent code)
+            const int gs = global_step(ls, Q, part);
+            const int gl = min(gs, kMaxSteps - 1);
+            const uint32_t tb = lane_val(ties_before, gl), off = lane_val(cincl - cnt, gl), c = lane_val(cnt, gl);
+            if (lane == 0) {
+                sm.s_step[ls][g][0] = (int)tb;
+                sm.s_step[ls][g][1] = (int)off;
+                sm.s_step[ls][g][2] = gs < NS ? (int)c : 0;
+            }
+        }
+        if (lane == 0) sm.s_total[g] = (int)total;
+    }
+    __syncthreads();
+
+    // ---- 4. ordered compaction --------------------------------------------------------------
+    const int seg0 = (ls_me * (kUT / D)) >> 6;   // first wavefront of this thread's step
+    uint32_t te01, te23;
+    {
+        uint32_t tv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) tv[g] = (uint32_t)__builtin_popcount(eq[g]);
+        seg_scan2(tv[0] | (tv[1] << 16), tv[2] | (tv[3] << 16), seg0, sm.s_w, te01, te23);
+    }
+    const uint32_t winm = wsm | wrm;
     uint32_t sel[4], nsel[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         sel[g] = nsel[g] = 0u;
         if (g < G) {
+            const uint32_t ties = (uint32_t)__builtin_popcount(eq[g]);
             const uint32_t local = ((g < 2 ? te01 : te23) >> (16 * (g & 1))) & 0xFFFFu;
-            const uint32_t before = (uint32_t)sm.s_sel[g][2] + local;
+            const uint32_t before = (uint32_t)sm.s_step[ls_me][g][0] + local;
             const uint32_t quota = (uint32_t)sm.s_sel[g][1];
-            const uint32_t take = quota > before ? min(quota - before, tiesv[g]) : 0u;
+            const uint32_t take = quota > before ? min(quota - before, ties) : 0u;
             uint32_t tk = 0;
-            if (take == tiesv[g]) {
+            if (take == ties) {
                 tk = eq[g];
             } else {   // the one thread where the quota ends: its lowest `take` ties
                 uint32_t e = eq[g];
@@ -717,21 +823,40 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
             nsel[g] = __builtin_popcount(sel[g]);
         }
     }
-    uint32_t oe01, oe23, ot01, ot23;
-    block_scan2(nsel[0] | (nsel[1] << 16), nsel[2] | (nsel[3] << 16), sm.s_w, oe01, oe23, ot01, ot23);
-    // The part's selected positions of head g: cntg[g] of them, listed in LDS
-    // (offsets from pbeg, after the lists of the heads before) when they fit.
-    constexpr bool kGather = !std::is_void<T>::value;
+    uint32_t oe01, oe23;
+    seg_scan2(nsel[0] | (nsel[1] << 16), nsel[2] | (nsel[3] << 16), seg0, sm.s_w, oe01, oe23);
+    // The window positions' entries are stored by all the unit's workgroups,
+    // each its run of them; a thread stores its other selected positions.  The
+    // part's selected positions of head g outside the windows, cntg[g] of them,
+    // are also listed in LDS (local position numbers, after the lists of the
+    // heads before) when they fit.  The distance array is no longer read.
+    Windows win;
+    win.s_end = s_end;
+    win.r_beg = r_beg;
+    win.n = n;
+    win.w0 = (int)((int64_t)win.count() * part / Q);
+    win.w1 = (int)((int64_t)win.count() * (part + 1) / Q);
     int cntg[4], lbase[4];
     int lsum = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        cntg[g] = g < G ? (int)(((g < 2 ? ot01 : ot23) >> (16 * (g & 1))) & 0xFFFFu) : 0;
+        int c = 0;
+#pragma unroll
+        for (int ls = 0; ls < D; ++ls) {
+            const int gs = global_step(ls, Q, part);
+            c += g < G && gs < NS ? sm.s_step[ls][g][2] - win.sink_in(gs) - win.recent_in(gs) : 0;
+        }
+        cntg[g] = c;
         lbase[g] = lsum;
-        lsum += cntg[g];
+        lsum += c;
     }
     uint16_t* lst = reinterpret_cast<uint16_t*>(&sm.dist[0][0]);
     const bool in_lds = kGather && lsum <= (int)(sizeof(sm.dist) / 2);   // uniform
+    const int loc0 = 4 * D * tid;   // local position number of bit 0 (local step ls_me = loc0 >> 12)
+    // Window positions of this thread's step before P0.
+    const int sb_me = global_step(ls_me, Q, part) * kStepPos;
+    const int wpre = max(0, min(P0, s_end) - sb_me) + max(0, P0 - max(sb_me, r_beg));
+    const uint32_t other = ~winm;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         if (g < G) {
@@ -742,15 +867,27 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
             // min(cap, n) entries (the count is at most both).
             const __amdgpu_buffer_rsrc_t ro =
                 __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)(min(a.cap, a.n) * 4), kRsrcWord3);
-            uint32_t pos4 = 4u * ((uint32_t)sm.s_sel[g][3] + local);
-            int li = lbase[g] + (int)local;
-            uint32_t s = sel[g];
+            const uint32_t base4 = 4u * ((uint32_t)sm.s_step[ls_me][g][1] + local);
+            int li = lbase[g] + (int)local - wpre;   // after this head's entries of the local steps before
+#pragma unroll
+            for (int ls = 0; ls < D; ++ls) {
+                const int gs = global_step(ls, Q, part);
+                li += ls < ls_me ? sm.s_step[ls][g][2] - win.sink_in(gs) - win.recent_in(gs) : 0;
+            }
+            const uint32_t sg = sel[g];
+            uint32_t s = sg & other;
             while (s) {
                 const int bit = __builtin_ctz(s);
-                __builtin_amdgcn_raw_buffer_store_b32(P0 + bit, ro, pos4, 0, 0);
-                if (in_lds) lst[li++] = (uint16_t)(P0 + bit - pbeg);
-                pos4 += 4u;
+                const uint32_t below = (uint32_t)__builtin_popcount(sg & ((1u << bit) - 1u));
+                __builtin_amdgcn_raw_buffer_store_b32(P0 + bit, ro, base4 + 4u * below, 0, 0);
+                if (in_lds) lst[li++] = (uint16_t)(loc0 + bit);
                 s &= s - 1u;
+            }
+            // This workgroup's run of window entries: the sink portion at the
+            // head of the list, the recent portion at its end.
+            for (int k = win.w0 + tid; k < win.w1; k += kUT) {
+                const int o = k < s_end ? k : total - (n - r_beg) + (k - s_end);
+                __builtin_amdgcn_raw_buffer_store_b32(win.pos(k), ro, 4u * (uint32_t)o, 0, 0);
             }
             if (part == 0) {
                 if (tid == 0) a.count[row0 + g] = total;
@@ -759,32 +896,36 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
         }
     }
     if constexpr (kGather) {
-        wait_vm_all();      // the index stores are acknowledged (a list too long for LDS is read back)
+        if (!in_lds) wait_vm_all();   // the index stores are acknowledged: the list is read back from them
         __syncthreads();
-        gather_part<T>(a, sm, lst, in_lds, cntg, lbase, unit, part, row0, b, h, pbeg);
+        gather_part<T>(a, sm, lst, in_lds, cntg, lbase, win, unit, part, row0, b, h);
     }
 }
 
 }  // namespace
 
 // Positions per part for a unit of n positions when `units` units share the
-// device's `cus` compute units: parts of 4096 D positions (D = 1, 2, 4, 8),
-// the smallest D with units * parts <= cus; 0 when none fits or G > 4.
+// device's `cus` compute units: D steps of 4,096 positions (D = 1, 2, 4, 8),
+// the smallest D with units * ceil(steps / D) <= cus; 0 when none fits, G > 4,
+// or the unit has more than kMaxSteps steps.
 int topk_unit_part(int64_t n, int units, int G, int cus) {
     if (n <= 0 || G > 4 || units <= 0) return 0;
+    const int64_t steps = (n + kStepPos - 1) / kStepPos;
+    if (steps > kMaxSteps) return 0;
     for (int D = 1; D <= 8; D *= 2) {
-        const int64_t P = 4096 * (int64_t)D;
-        const int64_t parts = (n + P - 1) / P;
-        if (parts <= 64 && (int64_t)units * parts <= cus) return (int)P;
+        const int64_t parts = (steps + D - 1) / D;
+        if ((int64_t)units * parts <= cus) return kStepPos * D;
     }
     return 0;
 }
 
 int topk_unit_row_words() { return kURow; }
+int topk_unit_rec_words() { return kMaxSteps * 4 * kRec; }
 
 hipError_t launch_topk_unit(const TopkArgs& a, int dtype, hipStream_t st) {
-    const int D = a.part_len / 4096;
-    if (a.B <= 0 || a.G > 4 || a.parts <= 0 || a.part_len != 4096 * D || (D != 1 && D != 2 && D != 4 && D != 8))
+    const int D = a.part_len / kStepPos;
+    if (a.B <= 0 || a.G > 4 || a.parts <= 0 || a.part_len != kStepPos * D || (D != 1 && D != 2 && D != 4 && D != 8) ||
+        a.n <= 0 || (a.n + kStepPos - 1) / kStepPos > kMaxSteps || a.parts != (int)((a.n + a.part_len - 1) / a.part_len))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.B * a.Hkv * a.parts)), block(kUT);
     const bool sc = a.scores != nullptr;
