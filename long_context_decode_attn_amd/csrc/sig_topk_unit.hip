@@ -34,9 +34,9 @@
 //      finds t and the quota from the summed histograms.
 //   3. Each thread owns 4 D consecutive positions of one step and compares
 //      their distance bytes, four at a time, with t and t + 1 (byte-parallel
-//      subtraction: every byte is below 128, so the sign bit of byte j of
-//      (d | 0x80) - t says whether d_j >= t); a dot product with 1, 2, 4, 8
-//      turns four sign bits into a nibble of the thread's position masks.  Per
+//      subtraction: the bytes are stored as d | 0x80, so the sign bit of byte
+//      j of (d | 0x80) - t says whether d_j >= t); dot products with powers of
+//      two gather eight sign bits into a byte of the thread's masks.  Per
 //      step the workgroup counts the positions below t, the ties and the
 //      window positions, and the workgroups exchange these step records the
 //      same way; one wavefront per query head (lane = step) turns them into
@@ -80,16 +80,15 @@ constexpr int kURow = 36;                       // words per published histogram
 constexpr int kRec = 8;                         // words per step record of a head (7 counts)
 constexpr int kMaxSteps = 64;                   // steps per unit (one lane each)
 constexpr uint32_t kHi = 0x80808080u;
-constexpr uint32_t kPadDist = 0x7Fu;            // distance byte of a position past the end: never < t, never t
+constexpr uint32_t kPadDist = 0x7Fu;            // distance of a position past the end: never < t, never t
 
-// A step record of one head: its positions below t, its ties (d == t), its
-// window positions, and the sink (ws) and recent (wr) window positions below t
-// and at t.
-enum { kBelow = 0, kTies, kWin, kWsBelow, kWsTies, kWrBelow, kWrTies, kRecCount };
+// A step record of one head: its positions below t, its ties (d == t), and
+// the sink (ws) and recent (wr) window positions below t and at t.
+enum { kBelow = 0, kTies, kWsBelow, kWsTies, kWrBelow, kWrTies, kRecCount };
 
 template <int D>
 struct __align__(16) UnitSmem {
-    uint32_t dist[4][kUT * D];                  // [head][dword]: the part's distances, a byte per position
+    uint32_t dist[4][kUT * D];                  // [head][dword]: the part's distances, a byte d | 0x80 per position
     uint32_t cnt[2 * (kUBins + 1) * 64];        // [head pair][bin][lane]: heads 2p, 2p + 1 in the low and high
                                                 // 16 bits; bin 33 takes positions past the end
     uint32_t rec[D][4][kRec];                   // [local step][head] records
@@ -158,8 +157,15 @@ __device__ __forceinline__ uint32_t low_bits(int64_t c) {
     return c <= 0 ? 0u : (c >= 32 ? 0xFFFFFFFFu : ((1u << (int)c) - 1u));
 }
 
-// The four sign bits of a dword of distance bytes as a nibble.
-__device__ __forceinline__ uint32_t nibble(uint32_t s) { return __builtin_amdgcn_udot4(s >> 7, 0x08040201u, 0u, false); }
+// Bits 8 k .. 8 k + 7 = flags of positions 8 k .. 8 k + 7 for two dwords of
+// distance bytes (each byte d | 0x80), 4 k and 4 k + 1 of the thread: bit 7 of
+// byte e of ~(A - T) is set iff d_e < t.  Two dot products with weights
+// 1, 2, 4, 8 and 16, 32, 64, 128 gather the eight sign bits as 128 x byte.
+__device__ __forceinline__ uint32_t below8(uint32_t A0, uint32_t A1, uint32_t T, bool two) {
+    uint32_t r = __builtin_amdgcn_udot4(~(A0 - T) & kHi, 0x08040201u, 0u, false);
+    if (two) r = __builtin_amdgcn_udot4(~(A1 - T) & kHi, 0x80402010u, r, false);
+    return r;   // 128 x the 8 flags
+}
 
 // Global step of local step ls of workgroup `part` (of Q).
 __device__ __forceinline__ int global_step(int ls, int Q, int part) { return ls * Q + part; }
@@ -254,26 +260,31 @@ __device__ __forceinline__ void publish_hist(const TopkArgs& a, const UnitSmem<D
 // Adds the calling wavefront's share of a step record (per head g < G: bit
 // masks of positions below t and at t, and the window masks) to rec[g], with
 // one LDS atomic per count.  Every lane of the wavefront takes part; its
-// positions lie in one step.
+// positions lie in one step.  The window counts are only summed in the
+// wavefronts that hold window positions.
 __device__ __forceinline__ void add_records(uint32_t (*rec)[kRec], int G, const uint32_t* lt4, const uint32_t* eq4,
                                             uint32_t ws, uint32_t wr) {
-    const uint32_t win = (uint32_t)__builtin_popcount(ws | wr);
+    const bool anyw = __builtin_amdgcn_ballot_w64((ws | wr) != 0u) != 0;   // uniform
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         if (g < G) {
             const uint32_t l = lt4[g], e = eq4[g];
-            const uint32_t v0 = (uint32_t)__builtin_popcount(l) | ((uint32_t)__builtin_popcount(e) << 16);
-            const uint32_t v1 = win | ((uint32_t)__builtin_popcount(l & ws) << 16);
-            const uint32_t v2 = (uint32_t)__builtin_popcount(e & ws) | ((uint32_t)__builtin_popcount(l & wr) << 16);
-            const uint32_t v3 = (uint32_t)__builtin_popcount(e & wr);
-            const uint32_t s0 = wave_total(v0), s1 = wave_total(v1), s2 = wave_total(v2), s3 = wave_total(v3);
+            const uint32_t s0 = wave_total((uint32_t)__builtin_popcount(l) | ((uint32_t)__builtin_popcount(e) << 16));
+            uint32_t s1 = 0, s2 = 0;
+            if (anyw) {
+                s1 = wave_total((uint32_t)__builtin_popcount(l & ws) | ((uint32_t)__builtin_popcount(e & ws) << 16));
+                s2 = wave_total((uint32_t)__builtin_popcount(l & wr) | ((uint32_t)__builtin_popcount(e & wr) << 16));
+            }
             if ((threadIdx.x & 63) == 0) {
                 uint32_t* r = rec[g];
-                const uint32_t add[kRecCount] = {s0 & 0xFFFFu, s0 >> 16, s1 & 0xFFFFu, s1 >> 16, s2 & 0xFFFFu,
-                                                 s2 >> 16, s3};
-#pragma unroll
-                for (int k = 0; k < kRecCount; ++k)
-                    __hip_atomic_fetch_add(r + k, add[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(r + kBelow, s0 & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(r + kTies, s0 >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (anyw) {
+                    __hip_atomic_fetch_add(r + kWsBelow, s1 & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_add(r + kWsTies, s1 >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_add(r + kWrBelow, s2 & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_add(r + kWrTies, s2 >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
             }
         }
     }
@@ -597,7 +608,7 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 if (g < G) {   // uniform
-                    uint32_t pk = 0;
+                    uint32_t pk = kHi;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t d = (uint32_t)__builtin_popcount(xc[ls][e] ^ q[g]);
@@ -613,7 +624,7 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 if (g < G) {
-                    uint32_t pk = 0;
+                    uint32_t pk = kHi;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const bool ok = i + e < n;
@@ -696,10 +707,12 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
             const uint32_t T1 = t >= 0 ? (uint32_t)(t + 1) * 0x01010101u : 0u;
             uint32_t l = 0, le = 0;
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                const uint32_t A = sm.dist[g][dist_slot<D>(D * tid + j)] | kHi;
-                l |= nibble(~(A - T0) & kHi) << (4 * j);
-                le |= nibble(~(A - T1) & kHi) << (4 * j);
+            for (int j = 0; j < D; j += 2) {
+                const uint32_t A0 = sm.dist[g][dist_slot<D>(D * tid + j)];
+                const uint32_t A1 = j + 1 < D ? sm.dist[g][dist_slot<D>(D * tid + j + 1)] : 0u;
+                const uint32_t r0 = below8(A0, A1, T0, j + 1 < D), r1 = below8(A0, A1, T1, j + 1 < D);
+                l |= j == 0 ? r0 >> 7 : r0 << (4 * j - 7);
+                le |= j == 0 ? r1 >> 7 : r1 << (4 * j - 7);
             }
             lt[g] = l;
             eq[g] = le & ~l;
@@ -770,7 +783,10 @@ __global__ __launch_bounds__(kUT) void k_topk_unit(TopkArgs a) {
         // suffix) what is left after the ties before that portion.
         const uint32_t tk_s = min(r[kWsTies], taken);
         const uint32_t tk_r = taken > ties - r[kWrTies] ? min(taken - (ties - r[kWrTies]), r[kWrTies]) : 0u;
-        const uint32_t cnt = r[kBelow] + taken + r[kWin] - (r[kWsBelow] + tk_s + r[kWrBelow] + tk_r);
+        // The step's window positions: its sink and recent portions.
+        const int sb = lane * kStepPos, se = min(n, sb + kStepPos);
+        const uint32_t win_n = lane < NS ? (uint32_t)(max(0, min(se, s_end) - sb) + max(0, se - max(sb, r_beg))) : 0u;
+        const uint32_t cnt = r[kBelow] + taken + win_n - (r[kWsBelow] + tk_s + r[kWrBelow] + tk_r);
         const uint32_t cincl = scan_incl(cnt);
         const uint32_t total = lane_val(cincl, 63);
 #pragma unroll
