@@ -75,27 +75,57 @@ def maybe_graph(fn, use_graph: bool):
     return g.replay
 
 
-def run_steps(step_fns, steps: int, warmup: int, use_graph: bool) -> float:
-    """Time exactly `steps` steps, step i running step_fns[i % len(step_fns)]; returns ms.
+def run_steps_stats(step_fns, steps: int, warmup: int, use_graph: bool, replays: int = 20) -> dict:
+    """Time exactly `steps` steps, step i running step_fns[i % len(step_fns)], as R = min(replays, steps)
+    back-to-back replays of steps // R steps (and one replay of the remainder, if any), each bracketed by HIP
+    events on the current stream.
 
-    With use_graph the warmup steps and the timed steps are each captured into one
-    HIP graph (one replay each), so the timed region holds exactly `steps` steps
-    and no per-step host launch."""
+    With use_graph the warmup steps, a replay and the remainder are each captured into one HIP graph, so the
+    timed region holds exactly `steps` steps and no per-step host launch.  Returns the whole region's time and
+    the median, 10th and 90th percentiles of the replays' time per step."""
+    R = max(1, min(replays, steps))
+    per = steps // R
+    rem = steps - per * R
+
     def seq(count):
         def f():
             for i in range(count):
                 step_fns[i % len(step_fns)]()
         return f
     warm = maybe_graph(seq(max(warmup, 1)), use_graph)
-    main_ = maybe_graph(seq(steps), use_graph)
+    one = maybe_graph(seq(per), use_graph)
+    tail = maybe_graph(seq(rem), use_graph) if rem else None
     warm()
     torch.cuda.synchronize()
-    t = Timer()
-    t.start()
-    main_()
-    ms = t.stop_ms()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(R + 2)]
+    ev[0].record()
+    for r in range(R):
+        one()
+        ev[r + 1].record()
+    last = R
+    if tail is not None:
+        tail()
+        ev[R + 1].record()
+        last = R + 1
+    ev[last].synchronize()
+    total = ev[0].elapsed_time(ev[last])
     torch.cuda.synchronize()
-    return ms
+    per_step = [ev[r].elapsed_time(ev[r + 1]) / per for r in range(R)]
+    pct = lambda f: float(np.percentile(per_step, f))
+    return {"ms": total, "ms_per_step": total / steps, "replays": R, "steps_per_replay": per,
+            "median_ms_per_step": pct(50), "p10_ms_per_step": pct(10), "p90_ms_per_step": pct(90)}
+
+
+def run_steps(step_fns, steps: int, warmup: int, use_graph: bool) -> float:
+    """Time exactly `steps` steps (see run_steps_stats); returns ms."""
+    return run_steps_stats(step_fns, steps, warmup, use_graph)["ms"]
+
+
+def replay_stats(st: dict) -> dict:
+    """The per-step spread over the timed replays, in microseconds."""
+    return {"replays": st["replays"], "steps_per_replay": st["steps_per_replay"],
+            "median_us_per_step": st["median_ms_per_step"] * 1e3, "p10_us_per_step": st["p10_ms_per_step"] * 1e3,
+            "p90_us_per_step": st["p90_ms_per_step"] * 1e3}
 
 
 # ------------------------------------------------------------------ dense ----
@@ -146,7 +176,8 @@ def bench_dense(args, cfg, layers=1):
         return f
 
     steps = args.steps
-    ms_step = run_steps([make(r, "step") for r in range(rot)], steps, args.warmup, args.graph) / steps
+    st = run_steps_stats([make(r, "step") for r in range(rot)], steps, args.warmup, args.graph)
+    ms_step = st["ms_per_step"]
     # the same step as the two separate calls, and the dominant call alone
     ms_two = run_steps([make(r, "step_two_calls") for r in range(rot)], steps, args.warmup, args.graph) / steps
     ms_a = run_steps([make(r, "attn") for r in range(rot)], steps, args.warmup, args.graph) / (steps * layers)
@@ -181,6 +212,7 @@ def bench_dense(args, cfg, layers=1):
                                 "avg_launch_us is the per-layer time of the pair)"),
                      "bytes_per_launch": layer_bytes, "avg_launch_us": launch_us},
         "rotations": rot,
+        "step_spread": replay_stats(st),
         "two_call_ms_per_step": ms_two,
         "two_call_tbps": two_call_bytes / (ms_two * 1e-3) / 1e12,
         "cached_attn_lse_us": ms_a * 1e3,
@@ -212,15 +244,32 @@ def traffic_from_profile(name: str, algorithmic_bytes: int, kind: str = "split_m
         return None
 
 
-def hbm_context(nbytes: int = 4 << 30, reps: int = 5) -> dict:
-    """The box's streaming rates through plain torch kernels, as context for the roofline: a sum over
-    nbytes of float32 (reads nbytes) and a copy of nbytes / 2 (reads and writes it).  Not tuned probes,
-    so they bound the achievable rate from below."""
+def hbm_context(nbytes: int = 4 << 30, reps: int = 5, probe_bytes: int = 8 << 30) -> dict:
+    """The box's measured read ceiling: the library's streaming-read probe (lcda_stream_read, a hand-written
+    kernel in which each workgroup streams one contiguous share with up to sixteen 16-byte nontemporal loads
+    per thread in flight) over probe_bytes at several grid sizes, best rate kept; and, as context, a float32
+    sum over nbytes (reads nbytes) and a copy of nbytes / 2 (reads and writes it) through plain torch
+    kernels."""
+    buf = torch.empty(probe_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    t = Timer()
+    probe = {}
+    for per_cu in (1, 2, 4, 8):
+        wgs = cus * per_cu
+        ops.stream_read(buf, wgs, sink)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            t.start()
+            ops.stream_read(buf, wgs, sink)
+            best = min(best, t.stop_ms())
+        probe["%d_workgroups" % wgs] = probe_bytes / (best * 1e-3) / 1e12
+    del buf
     x = torch.ones(nbytes // 4, device="cuda")
     y = torch.empty(nbytes // 8, device="cuda")
     x.sum()
     torch.cuda.synchronize()
-    t = Timer()
     t.start()
     for _ in range(reps):
         x.sum()
@@ -234,9 +283,12 @@ def hbm_context(nbytes: int = 4 << 30, reps: int = 5) -> dict:
     ms_copy = t.stop_ms() / reps
     del x, y
     torch.cuda.empty_cache()
-    return {"sum_read_tbps": nbytes / (ms_sum * 1e-3) / 1e12,
+    return {"stream_read_peak_tbps": max(probe.values()), "stream_read_tbps_by_grid": probe,
+            "sum_read_tbps": nbytes / (ms_sum * 1e-3) / 1e12,
             "copy_read_plus_write_tbps": nbytes / (ms_copy * 1e-3) / 1e12,
-            "bytes": nbytes, "note": "torch.sum and Tensor.copy_ over 4 GiB, event-timed"}
+            "bytes": nbytes, "probe_bytes": probe_bytes,
+            "note": "lcda_stream_read over 8 GiB (best of %d per grid, fastest grid); torch.sum and Tensor.copy_ "
+                    "over 4 GiB; event-timed" % reps}
 
 
 def calibrate_copy(nbytes: int, reps: int) -> dict:
@@ -336,7 +388,8 @@ def bench_sparse(args, cfg, rot=None):
     torch.cuda.synchronize()
 
     steps = args.steps
-    ms_step = run_steps([s.step for s in sets], steps, args.warmup, args.graph) / steps
+    st = run_steps_stats([s.step for s in sets], steps, args.warmup, args.graph)
+    ms_step = st["ms_per_step"]
     ms_two = run_steps([s.step_two_calls for s in sets], steps, args.warmup, args.graph) / steps
     ms_g = run_steps([s.gather for s in sets], steps, args.warmup, args.graph) / steps
     ms_t = run_steps([s.topk for s in sets], steps, args.warmup, args.graph) / steps
@@ -363,6 +416,7 @@ def bench_sparse(args, cfg, rot=None):
         "gather_tbps": gather_bytes / (ms_g * 1e-3) / 1e12,
         "gather_bytes": gather_bytes,
         "rotations": rot,
+        "step_spread": replay_stats(st),
     }
     if args.tmap:
         res["t_map"] = bench_tmap(args, sets, cfg)
@@ -422,7 +476,8 @@ def bench_needles(args, cfg):
     sets = [NeedleSet(cfg, r) for r in range(rot)]
     torch.cuda.synchronize()
     steps = args.steps
-    ms_s = run_steps([s.step for s in sets], steps, args.warmup, args.graph) / steps
+    st = run_steps_stats([s.step for s in sets], steps, args.warmup, args.graph)
+    ms_s = st["ms_per_step"]
     ms_g = run_steps([s.gather for s in sets], steps, args.warmup, args.graph) / steps
     ms_t = run_steps([s.topk for s in sets], steps, args.warmup, args.graph) / steps
     ms_d = run_steps([s.dense for s in sets], steps, args.warmup, args.graph) / steps
@@ -452,6 +507,7 @@ def bench_needles(args, cfg):
         "speedup_sparse_over_dense": ms_d / ms_s,
         "unique_rows": float(np.mean(uniq)),
         "rotations": rot,
+        "step_spread": replay_stats(st),
     }
     res.update(needle_quality(sets[0], cfg))
     return res
@@ -516,14 +572,20 @@ def bench_sigwidth(args, cfg):
 
 
 # -------------------------------------------------------------- CPU oracle ----
-def cpu_baseline_dense(cfg, seconds: float, threads: int = 0, layers: int = 1):
+def host_copy(x: dict) -> dict:
+    """Host copies of an input set's tensors (the very arrays uploaded for the timed steps)."""
+    return {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
+
+
+def cpu_baseline_dense(cfg, seconds: float, threads: int = 0, layers: int = 1, x=None):
     """The oracle (plain C, fp64) on the host's cores (or `threads` of them) over decode steps of the same
-    workload; with layers > 1 each timed step is one layer (every layer has the same shape) and the rate
-    is scaled by the layer count."""
+    workload: x is the input set the GPU timed (rotation 0; copied to the host here), else one drawn afresh;
+    with layers > 1 each timed step is one layer (every layer has the same shape) and the rate is scaled by
+    the layer count."""
     from oracle import oracle as orc_mod
     orc = orc_mod.default()
     orc.set_threads(threads or os.cpu_count() or 1)
-    x = synth.make_inputs(cfg, device="cpu")
+    x = host_copy(x) if x is not None else synth.make_inputs(cfg, device="cpu")
 
     def np_(t):
         t = t.contiguous()
@@ -541,10 +603,11 @@ def cpu_baseline_dense(cfg, seconds: float, threads: int = 0, layers: int = 1):
             break
     what = "full decode step(s)" if layers == 1 else "step(s) of one layer"
     tail = "" if layers == 1 else "; the rate is divided by the %d layers of a decode step" % layers
+    src = "on host copies of the arrays the GPU timed" if x is not None else "on inputs drawn on the host"
     return {"value": cfg.B * steps / (el * layers), "unit": "queries/s", "cores": orc.get_threads(),
             "kind": "oracle",
-            "sample": "%d %s of the same workload (cached_attn_lse + lse_merge_local definitions, fp64), "
-                      "%.1f s wall%s" % (steps, what, el, tail)}
+            "sample": "%d %s of %s (cached_attn_lse + lse_merge_local definitions, fp64) %s, %.1f s wall%s"
+                      % (steps, what, cfg.name, src, el, tail)}
 
 
 def cpu_baseline_quadrature(cfg, seconds: float, B: int = 4):
@@ -569,11 +632,17 @@ def cpu_baseline_quadrature(cfg, seconds: float, B: int = 4):
                       % (steps, B, el)}
 
 
-def cpu_baseline_sparse(cfg, seconds: float, B: int = 1):
+def cpu_baseline_sparse(cfg, seconds: float, B: int = 1, x=None):
+    """The oracle's SCORE + TOPK + GATHER-ATT on the first B batch items of x (the input set the GPU timed,
+    copied to the host), else of a set drawn on the host."""
     from oracle import oracle as orc_mod
     orc = orc_mod.default()
     orc.set_threads(os.cpu_count() or 1)
-    x = synth.make_inputs(cfg, device="cpu", B=B)
+    if x is not None:
+        x = {k: (v[:B].cpu() if torch.is_tensor(v) and v.dim() > 0 and v.shape[0] == cfg.B else v)
+             for k, v in x.items() if k in ("q", "k", "v", "key_sigs", "q_sigs")}
+    else:
+        x = synth.make_inputs(cfg, device="cpu", B=B)
 
     def np_(t):
         t = t.contiguous()
@@ -591,8 +660,8 @@ def cpu_baseline_sparse(cfg, seconds: float, B: int = 1):
         if el >= seconds:
             break
     return {"value": B * steps / el, "unit": "queries/s", "cores": orc.get_threads(), "kind": "oracle",
-            "sample": "%d step(s) of %d batch item(s) of the same workload (SCORE+TOPK+GATHER-ATT definitions, "
-                      "fp64), %.1f s wall" % (steps, B, el)}
+            "sample": "%d step(s) of the first %d batch item(s) of the timed input set, copied to the host "
+                      "(SCORE+TOPK+GATHER-ATT definitions, fp64), %.1f s wall" % (steps, B, el)}
 
 
 # ------------------------------------------------------------------- main ----
@@ -605,8 +674,8 @@ def main():
                     choices=["dense61k", "shared36", "sparse128k", "needles512k", "quadrature", "sigwidth"])
     ap.add_argument("--rot", type=int, default=0, help="input sets cycled (0: workload default)")
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="launch eagerly instead of a HIP graph")
-    ap.add_argument("--no-sparse", dest="sparse", action="store_false",
-                    help="skip the sparse-path measurement that rides along with the dense61k line")
+    ap.add_argument("--no-extra", "--no-sparse", dest="extra", action="store_false",
+                    help="skip the sparse128k, shared36 and needles512k entries that ride along with the dense61k line")
     ap.add_argument("--no-tmap", dest="tmap", action="store_false",
                     help="skip the T_map timings that ride along with the sparse measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0: skip)")
@@ -640,7 +709,7 @@ def main():
     if args.workload in ("dense61k", "shared36"):
         cfg = synth.CONFIGS[2 if args.workload == "dense61k" else 3]
         layers = cfg.layers
-        res, _ = bench_dense(args, cfg, layers)
+        res, timed = bench_dense(args, cfg, layers)
         line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"],
                      "roofline": res["roofline"]})
         line["config"] = {"workload": args.workload + ": " + cfg.name, "batch": cfg.B, "n": cfg.n, "layers": layers,
@@ -650,28 +719,61 @@ def main():
                         "workgroup per (batch, KV head) does the LSE combine" if not cfg.shared_doc else
                         "36 x dense_decode_step over one shared document (cached_attn_lse + lse_merge_local as "
                         "one 64-row split-KV pass that also takes each row's local tokens, then one combine)")
+        line["step_spread"] = res["step_spread"]
         line["cached_attn_lse_us"] = res["cached_attn_lse_us"]
         line["two_call_ms_per_step"] = res["two_call_ms_per_step"]
         line["two_call_tbps"] = res["two_call_tbps"]
         line["step_bytes"] = res["step_bytes"]
         line["step_tbps"] = res["step_tbps"]
         line["step_frac_of_peak"] = res["step_tbps"] * 1e12 / HBM_PEAK
-        if args.workload == "dense61k" and args.sparse:
+        shared_timed = None
+        if args.workload == "dense61k" and args.extra:
+            # The other target workloads ride along as entries of the same line.
             sres, _ = bench_sparse(args, synth.CONFIGS[4])
             sres["workload"] = "sparse128k: " + synth.CONFIGS[4].name
             sres["step_frac_of_peak"] = sres["step_tbps"] * 1e12 / HBM_PEAK
             line["sparse"] = sres
+            torch.cuda.empty_cache()
+            c3 = synth.CONFIGS[3]
+            dres, shared_timed = bench_dense(args, c3, c3.layers)
+            dres["workload"] = "shared36: " + c3.name
+            dres["layer_us"] = dres["ms_per_step"] * 1e3 / c3.layers
+            dres["step_frac_of_peak"] = dres["step_tbps"] * 1e12 / HBM_PEAK
+            line["shared36"] = dres
+            shared_timed = host_copy(shared_timed.x)
+            torch.cuda.empty_cache()
+            nres = bench_needles(args, synth.CONFIGS[5])
+            nres["workload"] = "needles512k: " + synth.CONFIGS[5].name
+            nres["sparse_step_frac_of_peak"] = nres["sparse_step_tbps"] * 1e12 / HBM_PEAK
+            line["needles512k"] = nres
+            torch.cuda.empty_cache()
         if args.cpu_seconds > 0:
-            line["cpu_baseline"] = cpu_baseline_dense(cfg, args.cpu_seconds, layers=layers)
+            line["cpu_baseline"] = cpu_baseline_dense(cfg, args.cpu_seconds, layers=layers, x=timed.x)
             if args.workload == "dense61k":
-                one = cpu_baseline_dense(cfg, max(1.0, args.cpu_seconds / 4), threads=1)
+                # One thread: this workload, the small reference case, and one layer of the shared document.
+                short = max(1.0, args.cpu_seconds / 4)
+                one = cpu_baseline_dense(cfg, short, threads=1, x=timed.x)
                 line["cpu_baseline_one_thread"] = {"value": one["value"], "unit": one["unit"],
                                                    "cores": one["cores"], "sample": one["sample"]}
+                c1 = synth.CONFIGS[1]
+                tiny = cpu_baseline_dense(c1, short, threads=1, x=synth.make_inputs(c1, device="cuda"))
+                line["cpu_baseline_one_thread_tiny"] = {"value": tiny["value"], "unit": tiny["unit"],
+                                                        "cores": tiny["cores"], "sample": tiny["sample"]}
+                if shared_timed is not None:
+                    c3 = synth.CONFIGS[3]
+                    lay = cpu_baseline_dense(c3, short, threads=1, x=shared_timed)
+                    line["cpu_baseline_one_thread_shared36_layer"] = {
+                        "value": lay["value"], "unit": "queries/s through one layer", "cores": lay["cores"],
+                        "sample": lay["sample"]}
         if args.workload == "dense61k":
-            line["hbm_context"] = hbm_context()
+            ctx = hbm_context()
+            line["hbm_context"] = ctx
+            peak = ctx["stream_read_peak_tbps"] * 1e12
+            line["roofline"]["measured_read_peak"] = peak / 1e9
+            line["roofline"]["frac_of_measured_read_peak"] = line["roofline"]["achieved"] * 1e9 / peak
     elif args.workload == "sparse128k":
         cfg = synth.CONFIGS[4]
-        res, _ = bench_sparse(args, cfg)
+        res, timed = bench_sparse(args, cfg)
         line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"]})
         ach = res["gather_tbps"] * 1e12
         line["roofline"] = {"bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -683,7 +785,7 @@ def main():
         line["config"] = {"workload": "sparse128k: " + cfg.name, "launch": launch}
         line["detail"] = res
         if args.cpu_seconds > 0:
-            line["cpu_baseline"] = cpu_baseline_sparse(cfg, args.cpu_seconds)
+            line["cpu_baseline"] = cpu_baseline_sparse(cfg, args.cpu_seconds, x=timed.x)
     elif args.workload == "sigwidth":
         cfg = synth.CONFIGS[4]
         res = bench_sigwidth(args, cfg)

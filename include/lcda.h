@@ -317,10 +317,30 @@ const char* lcda_version(void);
  *                    more where a head would otherwise exceed 64 chunks); 0 picks
  *                    the count that gives about topk_wgs workgroups (0)
  *   "topk_wgs"       TOPK scans: workgroups a call aims at when topk_subs is 0 (512)
+ *   "topk_kernel"    TOPK form: 1 = one launch that keeps the distances in LDS and
+ *                    exchanges counts between the workgroups of a (b, KV head),
+ *                    where its grid fits the device one workgroup per CU (at most 4
+ *                    query heads per KV head and 64 steps of 4,096 positions);
+ *                    0 = the chunked passes (1)
+ *   "topk_spin"      one-launch TOPK: polls of a workgroup waiting for its partners
+ *                    before it counts their share itself (16384, at most 2^20)
+ *   "sparse_fused"   sparse_decode_step: 1 = SCORE + TOPK + GATHER-ATT in the one
+ *                    TOPK launch where that form applies; 0 = sig_score_topk then
+ *                    gather_attn (0)
  * Returns LCDA_EINVAL for an unknown key or a negative (or, except
  * direct_blocks, zero) value.  lcda_get_tuning returns -1 for an unknown key. */
 int lcda_set_tuning(const char* key, int64_t value);
 int64_t lcda_get_tuning(const char* key);
+
+/* Streaming-read probe (not part of the method): reads `bytes` of device memory
+ * at buf (16-byte aligned, bytes a multiple of 16) once, with `workgroups`
+ * workgroups of 512 threads each keeping up to sixteen 16-byte nontemporal loads
+ * in flight, and folds the words read into one value per thread; sink[0] (device,
+ * 4 bytes) is written only by a thread whose value equals `never`.  Its rate is
+ * the measured read ceiling that the kernels' HBM fractions are set against, next
+ * to the published peak.  LCDA_EINVAL for a null or misaligned buf or sink, or
+ * workgroups outside 1 .. 2^20; bytes = 0 does nothing. */
+int lcda_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, uint32_t never, void* stream);
 
 #ifdef __cplusplus
 }

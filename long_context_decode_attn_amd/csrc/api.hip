@@ -640,9 +640,11 @@ static int topk_impl(const char* fn, const uint32_t* key_sigs, uint32_t* q_sigs,
     RETURN_IF(check_n(fn, "n", n));
     if (m < 0 || n_sink < 0 || n_recent < 0)
         return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be >= 0", fn);
+    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX)   // before the sum below: no overflow
+        return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be <= INT32_MAX", fn);
     if (cap < 0 || cap > INT32_MAX) return fail(LCDA_EINVAL, "%s: cap = %lld out of range", fn, (long long)cap);
     const int64_t need = (m + n_sink + n_recent < n) ? m + n_sink + n_recent : n;
-    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX || cap < need)
+    if (cap < need)
         return fail(LCDA_EINVAL, "%s: cap = %lld < min(n, m + n_sink + n_recent) = %lld", fn, (long long)cap,
                     (long long)need);
     const bool work = B > 0;
@@ -746,9 +748,11 @@ int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, in
     RETURN_IF(check_n(fn, "n", n));
     if (m < 0 || n_sink < 0 || n_recent < 0)
         return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be >= 0", fn);
+    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX)   // before the sum below: no overflow
+        return fail(LCDA_EINVAL, "%s: m, n_sink and n_recent must be <= INT32_MAX", fn);
     if (cap < 0 || cap > INT32_MAX) return fail(LCDA_EINVAL, "%s: cap = %lld out of range", fn, (long long)cap);
     const int64_t need = (m + n_sink + n_recent < n) ? m + n_sink + n_recent : n;
-    if (m > INT32_MAX || n_sink > INT32_MAX || n_recent > INT32_MAX || cap < need)
+    if (cap < need)
         return fail(LCDA_EINVAL, "%s: cap = %lld < min(n, m + n_sink + n_recent) = %lld", fn, (long long)cap,
                     (long long)need);
     const bool work = B > 0;

@@ -214,4 +214,7 @@ hipError_t launch_topk_unit(const TopkArgs& a, int dtype, hipStream_t st);
 int topk_hist_row();
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
+// Records the formatted text that lcda_last_error returns and returns code.
+int set_error(int code, const char* fmt, ...);
+
 }  // namespace lcda

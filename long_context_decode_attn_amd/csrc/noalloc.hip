@@ -27,7 +27,6 @@ int dense_decode_step_impl(const void* q, const void* k, const void* v, int64_t 
                            const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B,
                            int Hq, int Hkv, int d, int dtype, float* out, float* alpha_out, float* a_doc,
                            float* alpha_doc, void* ws, size_t ws_bytes, unsigned long long* ctr, void* stream);
-int set_error(int code, const char* fmt, ...);
 
 namespace {
 

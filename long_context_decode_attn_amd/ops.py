@@ -1,7 +1,8 @@
-"""Python binding of liblcda (ctypes): the four C-ABI calls under the same names.
+"""Python binding of liblcda (ctypes): every C-ABI call of include/lcda.h under the same name.
 
-Only argument marshalling happens here: shapes and dtypes are checked, outputs
-and the workspace are allocated with torch on the tensors' device, and the
+Only argument marshalling happens here: every tensor is checked (device,
+contiguity, dtype, shape; ValueError before any launch), outputs and the
+workspace are allocated with torch on the tensors' device unless given, and the
 call is enqueued on torch's current HIP stream.  Every step of the path runs in
 the HIP kernels of liblcda.so; there is no fallback of any kind: if the library
 is missing or a call fails, an exception is raised.
@@ -26,7 +27,8 @@ EXPORTS = ("cached_attn_lse", "lse_merge_local", "sig_score_topk", "gather_attn"
            "lcda_last_error", "lcda_version", "lcda_set_tuning", "lcda_get_tuning",
            "dense_decode_step", "lcda_ws_bytes_dense_decode_step", "sig_encode", "sig_score_topk_q",
            "sig_score_topk_w", "lcda_ws_bytes_sig_score_topk_w", "dense_decode_step_noalloc",
-           "lcda_noalloc_scratch_bytes", "sparse_decode_step", "lcda_ws_bytes_sparse_decode_step")
+           "lcda_noalloc_scratch_bytes", "sparse_decode_step", "lcda_ws_bytes_sparse_decode_step",
+           "lcda_stream_read")
 
 _lib = None
 
@@ -82,6 +84,8 @@ def load(path: str = LIB_PATH):
     lib.sparse_decode_step.restype = ctypes.c_int
     lib.lcda_ws_bytes_sparse_decode_step.argtypes = [i32, i32, i32, i32, i64, i64]
     lib.lcda_ws_bytes_sparse_decode_step.restype = ctypes.c_size_t
+    lib.lcda_stream_read.argtypes = [P, sz, i32, P, ctypes.c_uint32, P]
+    lib.lcda_stream_read.restype = ctypes.c_int
     lib.lcda_set_tuning.argtypes = [ctypes.c_char_p, i64]
     lib.lcda_set_tuning.restype = ctypes.c_int
     lib.lcda_get_tuning.argtypes = [ctypes.c_char_p]
@@ -117,23 +121,82 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+# Every tensor that reaches a kernel is checked here first (device, contiguity,
+# dtype, shape): a host tensor or a short buffer must never become a device
+# pointer.  Failures raise ValueError before any launch.
+_CODES = (torch.int32, torch.uint32)
+
+
+def _tensor(t, name: str, dev, dtypes=None, shape=None):
+    _need(isinstance(t, torch.Tensor), "%s must be a tensor" % name)
+    _need(t.device == dev, "%s must be on %s, got %s" % (name, dev, t.device))
+    _need(t.is_contiguous(), "%s must be contiguous" % name)
+    if dtypes is not None:
+        _need(t.dtype in dtypes, "%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _out(t, name: str, shape, dev, dtype=torch.float32):
+    """A caller-provided output (checked) or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _tensor(t, name, dev, (dtype,), shape)
+
+
+def _gpu(t, name: str):
+    _need(isinstance(t, torch.Tensor), "%s must be a tensor" % name)
+    _need(t.is_cuda, "%s must be on a GPU, got %s" % (name, t.device))
+    return t.device
+
+
 def _ws(nbytes: int, device, ws):
     if ws is not None:
+        _tensor(ws, "ws", device)
         _need(ws.numel() * ws.element_size() >= nbytes, "workspace too small: need %d bytes" % nbytes)
         return ws
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def _as_kv(k: torch.Tensor, B: int):
+def _as_kv(k: torch.Tensor, B: int, dev=None, name="K/V"):
     """K/V as [Bkv, Hkv, n, d]; returns (tensor4d, kv_batch_stride in elements)."""
+    _need(isinstance(k, torch.Tensor), "%s must be a tensor" % name)
     if k.dim() == 3:
         k = k.unsqueeze(0)
-    _need(k.dim() == 4, "K/V must be [B, Hkv, n, d] or [Hkv, n, d]")
-    _need(k.is_contiguous(), "K/V must be contiguous")
+    _need(k.dim() == 4, "%s must be [B, Hkv, n, d] or [Hkv, n, d]" % name)
+    if dev is not None:
+        _tensor(k, name, dev)
+    _need(k.is_contiguous(), "%s must be contiguous" % name)
     Bk = k.shape[0]
-    _need(Bk in (1, B), "K/V batch %d must be 1 (shared document) or B = %d" % (Bk, B))
+    _need(Bk in (1, B), "%s batch %d must be 1 (shared document) or B = %d" % (name, Bk, B))
     stride = 0 if (Bk == 1 and B != 1) else k.shape[1] * k.shape[2] * k.shape[3]
     return k, stride
+
+
+def _query(q, name="q"):
+    """q [B, Hq, d] on a GPU, float32 or bfloat16, contiguous; returns (device, B, Hq, d)."""
+    dev = _gpu(q, name)
+    _need(q.dim() == 3, "%s must be [B, Hq, d]" % name)
+    _tensor(q, name, dev, (torch.float32, torch.bfloat16))
+    return (dev,) + tuple(q.shape)
+
+
+def _kv_pair(k, v, B, dev, dtype):
+    k, stride = _as_kv(k, B, dev, "K")
+    v, _ = _as_kv(v, B, dev, "V")
+    _need(v.shape == k.shape, "K and V shapes differ")
+    _need(k.dtype == dtype and v.dtype == dtype, "q, K, V must share a dtype")
+    return k, v, stride
+
+
+def _locals(k_loc, v_loc, n_loc, B, dev, dtype):
+    _tensor(k_loc, "k_loc", dev, (dtype,))
+    _tensor(v_loc, "v_loc", dev, (dtype,))
+    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
+    if n_loc is not None:
+        _tensor(n_loc, "n_loc", dev, (torch.int32,))
+        _need(n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
 
 
 def ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride) -> int:
@@ -158,16 +221,11 @@ def cached_attn_lse(q, k, v, out=None, alpha=None, ws=None):
     K, V: [B, Hkv, n, d] (one cache per batch item) or [1, Hkv, n, d] (one
     document shared by all B items)."""
     lib = load()
-    B, Hq, d = q.shape
-    k, stride = _as_kv(k, B)
-    v, _ = _as_kv(v, B)
-    _need(v.shape == k.shape, "K and V shapes differ")
-    _need(q.is_contiguous() and q.is_cuda and k.device == q.device and v.device == q.device,
-          "q, K, V must be contiguous tensors on one GPU")
-    _need(q.dtype == k.dtype == v.dtype, "q, K, V must share a dtype")
+    dev, B, Hq, d = _query(q)
+    k, v, stride = _kv_pair(k, v, B, dev, q.dtype)
     Hkv, n = k.shape[1], k.shape[2]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
-    alpha = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if alpha is None else alpha
+    out = _out(out, "out", (B, Hq, d), dev)
+    alpha = _out(alpha, "alpha", (B, Hq), dev)
     nb = lib.lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, stride)
     w = _ws(nb, q.device, ws)
     st = lib.cached_attn_lse(_p(q), _p(k), _p(v), B, Hq, Hkv, d, n, stride, _dtype_code(q),
@@ -182,17 +240,14 @@ def lse_merge_local(q, a_in, alpha_in, k_loc, v_loc, n_loc=None, out=None, alpha
 
     n_loc: int32 tensor [B] on the GPU (None: all n_loc_max tokens visible)."""
     lib = load()
-    B, Hq, d = q.shape
-    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
-    _need(k_loc.is_contiguous() and v_loc.is_contiguous() and q.is_contiguous(), "inputs must be contiguous")
-    _need(a_in.dtype == torch.float32 and alpha_in.dtype == torch.float32, "a_in, alpha_in must be fp32")
-    _need(q.dtype == k_loc.dtype == v_loc.dtype, "q, k_loc, v_loc must share a dtype")
-    if n_loc is not None:
-        _need(n_loc.dtype == torch.int32 and n_loc.is_cuda and n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
+    dev, B, Hq, d = _query(q)
+    _tensor(a_in, "a_in", dev, (torch.float32,), (B, Hq, d))
+    _tensor(alpha_in, "alpha_in", dev, (torch.float32,), (B, Hq))
+    _locals(k_loc, v_loc, n_loc, B, dev, q.dtype)
     Hkv, nmax = k_loc.shape[1], k_loc.shape[2]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
-    if want_alpha and alpha_out is None:
-        alpha_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", (B, Hq, d), dev)
+    if want_alpha or alpha_out is not None:
+        alpha_out = _out(alpha_out, "alpha_out", (B, Hq), dev)
     nb = lib.lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, nmax)
     w = _ws(nb, q.device, ws)
     st = lib.lse_merge_local(_p(q), _p(a_in), _p(alpha_in), _p(k_loc), _p(v_loc), _p(n_loc), nmax, B, Hq, Hkv, d,
@@ -212,19 +267,18 @@ def dense_decode_step(q, k, v, k_loc, v_loc, n_loc=None, out=None, alpha_out=Non
 
     Returns (out, alpha_out); a_doc / alpha_doc (both or neither) receive the cached-only (A, alpha)."""
     lib = load()
-    B, Hq, d = q.shape
-    k, stride = _as_kv(k, B)
-    v, _ = _as_kv(v, B)
-    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
-    _need(q.is_contiguous() and k_loc.is_contiguous() and v_loc.is_contiguous(), "inputs must be contiguous")
-    _need(q.dtype == k.dtype == v.dtype == k_loc.dtype == v_loc.dtype, "q, K, V, k_loc, v_loc must share a dtype")
-    if n_loc is not None:
-        _need(n_loc.dtype == torch.int32 and n_loc.is_cuda and n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
+    dev, B, Hq, d = _query(q)
+    k, v, stride = _kv_pair(k, v, B, dev, q.dtype)
+    _locals(k_loc, v_loc, n_loc, B, dev, q.dtype)
     Hkv, n = k.shape[1], k.shape[2]
     nmax = k_loc.shape[2]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
-    if want_alpha and alpha_out is None:
-        alpha_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", (B, Hq, d), dev)
+    if want_alpha or alpha_out is not None:
+        alpha_out = _out(alpha_out, "alpha_out", (B, Hq), dev)
+    _need((a_doc is None) == (alpha_doc is None), "a_doc and alpha_doc go together")
+    if a_doc is not None:
+        _tensor(a_doc, "a_doc", dev, (torch.float32,), (B, Hq, d))
+        _tensor(alpha_doc, "alpha_doc", dev, (torch.float32,), (B, Hq))
     nb = lib.lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, stride, nmax)
     w = _ws(nb, q.device, ws)
     st = lib.dense_decode_step(_p(q), _p(k), _p(v), stride, n, _p(k_loc), _p(v_loc), _p(n_loc), nmax, B, Hq, Hkv, d,
@@ -238,19 +292,14 @@ def dense_decode_step_noalloc(q, k, v, k_loc, v_loc, n_loc=None, out=None, alpha
     """dense_decode_step with the library's static scratch array instead of a workspace (the call itself
     allocates nothing; outputs are allocated here unless given).  Returns (out, alpha_out)."""
     lib = load()
-    B, Hq, d = q.shape
-    k, stride = _as_kv(k, B)
-    v, _ = _as_kv(v, B)
-    _need(k_loc.dim() == 4 and k_loc.shape[0] == B and k_loc.shape == v_loc.shape, "k_loc/v_loc must be [B, Hkv, n, d]")
-    _need(q.is_contiguous() and k_loc.is_contiguous() and v_loc.is_contiguous(), "inputs must be contiguous")
-    _need(q.dtype == k.dtype == v.dtype == k_loc.dtype == v_loc.dtype, "q, K, V, k_loc, v_loc must share a dtype")
-    if n_loc is not None:
-        _need(n_loc.dtype == torch.int32 and n_loc.is_cuda and n_loc.numel() == B, "n_loc must be int32 [B] on the GPU")
+    dev, B, Hq, d = _query(q)
+    k, v, stride = _kv_pair(k, v, B, dev, q.dtype)
+    _locals(k_loc, v_loc, n_loc, B, dev, q.dtype)
     Hkv, n = k.shape[1], k.shape[2]
     nmax = k_loc.shape[2]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
-    if want_alpha and alpha_out is None:
-        alpha_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", (B, Hq, d), dev)
+    if want_alpha or alpha_out is not None:
+        alpha_out = _out(alpha_out, "alpha_out", (B, Hq), dev)
     st = lib.dense_decode_step_noalloc(_p(q), _p(k), _p(v), stride, n, _p(k_loc), _p(v_loc), _p(n_loc), nmax, B, Hq,
                                        Hkv, d, _dtype_code(q), _p(out), _p(alpha_out), _stream(q.device))
     _check("dense_decode_step_noalloc", st)
@@ -271,14 +320,16 @@ def sig_score_topk(key_sigs, q_sigs, m, n_sink, n_recent, cap=None, want_scores=
 
     Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, scores [B, Hq, n] int8 or None)."""
     lib = load()
-    _need(key_sigs.dtype in (torch.int32, torch.uint32) and q_sigs.dtype == key_sigs.dtype, "signatures must be 32-bit")
-    _need(key_sigs.is_contiguous() and q_sigs.is_contiguous(), "signatures must be contiguous")
+    dev = _gpu(key_sigs, "key_sigs")
+    _need(key_sigs.dim() == 3, "key_sigs must be [B, Hkv, n]")
+    _tensor(key_sigs, "key_sigs", dev, _CODES)
     B, Hkv, n = key_sigs.shape
+    _need(isinstance(q_sigs, torch.Tensor) and q_sigs.dim() == 2 and q_sigs.shape[0] == B, "q_sigs must be [B, Hq]")
+    _tensor(q_sigs, "q_sigs", dev, (key_sigs.dtype,))
     Hq = q_sigs.shape[1]
     cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
-    dev = key_sigs.device
-    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
-    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
+    idx = _out(idx, "idx", (B, Hq, cap), dev, torch.int32)
+    count = _out(count, "count", (B, Hq), dev, torch.int32)
     scores = torch.empty((B, Hq, n), dtype=torch.int8, device=dev) if want_scores else None
     nb = lib.lcda_ws_bytes_sig_score_topk(B, Hq, Hkv, n)
     w = _ws(nb, dev, ws)
@@ -293,16 +344,20 @@ def sig_score_topk_q(key_sigs, q, R, m, n_sink, n_recent, cap=None, want_scores=
     """SCORE + TOPK with the query codes encoded at the head of the scan from q [B, Hq, 128] and R [128, bits]
     (fp32).  Returns (idx, count, scores or None, q_sigs [B, Hq] int32 storage of uint32 codes)."""
     lib = load()
-    _need(key_sigs.dtype in (torch.int32, torch.uint32) and key_sigs.is_contiguous(), "key codes: contiguous 32-bit")
-    _need(q.is_contiguous() and q.shape[-1] == 128, "q must be contiguous [B, Hq, 128]")
-    _need(R.dtype == torch.float32 and R.is_contiguous() and R.shape[0] == 128 and R.dim() == 2, "R: [128, bits] fp32")
+    dev = _gpu(key_sigs, "key_sigs")
+    _need(key_sigs.dim() == 3, "key_sigs must be [B, Hkv, n]")
+    _tensor(key_sigs, "key_sigs", dev, _CODES)
     B, Hkv, n = key_sigs.shape
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3 and q.shape[0] == B and q.shape[2] == 128,
+          "q must be [B, Hq, 128]")
+    _tensor(q, "q", dev, (torch.float32, torch.bfloat16))
+    _need(isinstance(R, torch.Tensor) and R.dim() == 2 and R.shape[0] == 128, "R: [128, bits] fp32")
+    _tensor(R, "R", dev, (torch.float32,))
     Hq = q.shape[1]
     cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
-    dev = key_sigs.device
-    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
-    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
-    q_sigs = torch.empty((B, Hq), dtype=torch.int32, device=dev) if q_sigs is None else q_sigs
+    idx = _out(idx, "idx", (B, Hq, cap), dev, torch.int32)
+    count = _out(count, "count", (B, Hq), dev, torch.int32)
+    q_sigs = _out(q_sigs, "q_sigs", (B, Hq), dev, torch.int32)
     scores = torch.empty((B, Hq, n), dtype=torch.int8, device=dev) if want_scores else None
     nb = lib.lcda_ws_bytes_sig_score_topk(B, Hq, Hkv, n)
     w = _ws(nb, dev, ws)
@@ -319,15 +374,16 @@ def sig_score_topk_w(key_sigs, q_sigs, m, n_sink, n_recent, cap=None, want_score
 
     Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, scores [B, Hq, n] int16 or None)."""
     lib = load()
-    _need(key_sigs.dtype in (torch.int32, torch.uint32) and q_sigs.dtype == key_sigs.dtype, "codes must be 32-bit")
-    _need(key_sigs.is_contiguous() and q_sigs.is_contiguous(), "codes must be contiguous")
+    dev = _gpu(key_sigs, "key_sigs")
+    _need(key_sigs.dim() == 4, "key_sigs must be [B, Hkv, n, W]")
+    _tensor(key_sigs, "key_sigs", dev, _CODES)
     B, Hkv, n, W = key_sigs.shape
+    _need(isinstance(q_sigs, torch.Tensor) and q_sigs.dim() == 3, "q_sigs must be [B, Hq, W]")
     Hq = q_sigs.shape[1]
-    _need(tuple(q_sigs.shape) == (B, Hq, W), "q_sigs must be [B, Hq, W]")
+    _tensor(q_sigs, "q_sigs", dev, (key_sigs.dtype,), (B, Hq, W))
     cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
-    dev = key_sigs.device
-    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
-    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
+    idx = _out(idx, "idx", (B, Hq, cap), dev, torch.int32)
+    count = _out(count, "count", (B, Hq), dev, torch.int32)
     scores = torch.empty((B, Hq, n), dtype=torch.int16, device=dev) if want_scores else None
     nb = lib.lcda_ws_bytes_sig_score_topk_w(B, Hq, n)
     w = _ws(nb, dev, ws)
@@ -344,12 +400,18 @@ def sig_encode(x, R, codes=None):
     [B, H, r, 128] view into a cache (rows contiguous, heads evenly strided, e.g. K[:, :, n_old:n_old + r]); codes
     must then be the matching [B, H, r] view into the key codes (e.g. key_sigs[:, :, n_old:n_old + r])."""
     lib = load()
-    _need(R.dtype == torch.float32 and R.is_contiguous() and R.dim() == 2 and R.shape[0] == 128, "R: [128, bits] fp32")
+    dev = _gpu(x, "x")
+    _need(x.dtype in (torch.float32, torch.bfloat16), "x must be float32 or bfloat16")
+    _need(isinstance(R, torch.Tensor) and R.dim() == 2 and R.shape[0] == 128, "R: [128, bits] fp32")
+    _tensor(R, "R", dev, (torch.float32,))
     _need(x.shape[-1] == 128 and x.stride(-1) == 1, "rows of x must hold 128 contiguous values")
+    if codes is not None:
+        _need(isinstance(codes, torch.Tensor) and codes.device == dev and codes.dtype in _CODES,
+              "codes must be 32-bit on %s" % dev)
     if x.is_contiguous():
         lead = x.shape[:-1]
         rows = x.numel() // 128
-        codes = torch.empty(lead, dtype=torch.int32, device=x.device) if codes is None else codes
+        codes = torch.empty(lead, dtype=torch.int32, device=dev) if codes is None else codes
         _need(codes.is_contiguous() and codes.numel() == rows, "codes must be contiguous, one per row")
         g, rpg, xs, cs = 1, rows, 0, 0
     else:
@@ -366,17 +428,17 @@ def sig_encode(x, R, codes=None):
 def gather_attn(q, k, v, idx, count, out=None, alpha=None, ws=None, want_alpha=True):
     """Attention of each query head over its selected positions idx[:, :, :count] only."""
     lib = load()
-    B, Hq, d = q.shape
-    k, stride = _as_kv(k, B)
-    v, _ = _as_kv(v, B)
-    _need(idx.dtype == torch.int32 and count.dtype == torch.int32, "idx and count must be int32")
-    _need(idx.is_contiguous() and count.is_contiguous() and q.is_contiguous(), "inputs must be contiguous")
-    _need(q.dtype == k.dtype == v.dtype, "q, K, V must share a dtype")
+    dev, B, Hq, d = _query(q)
+    k, v, stride = _kv_pair(k, v, B, dev, q.dtype)
+    _need(isinstance(idx, torch.Tensor) and idx.dim() == 3 and tuple(idx.shape[:2]) == (B, Hq),
+          "idx must be [B, Hq, cap]")
+    _tensor(idx, "idx", dev, (torch.int32,))
+    _tensor(count, "count", dev, (torch.int32,), (B, Hq))
     Hkv, n = k.shape[1], k.shape[2]
     cap = idx.shape[2]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
-    if want_alpha and alpha is None:
-        alpha = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", (B, Hq, d), dev)
+    if want_alpha or alpha is not None:
+        alpha = _out(alpha, "alpha", (B, Hq), dev)
     nb = lib.lcda_ws_bytes_gather_attn(B, Hq, Hkv, d, cap)
     w = _ws(nb, q.device, ws)
     st = lib.gather_attn(_p(q), _p(k), _p(v), stride, _p(idx), _p(count), cap, B, Hq, Hkv, d, n, _dtype_code(q),
@@ -396,22 +458,17 @@ def sparse_decode_step(key_sigs, q_sigs, q, k, v, m, n_sink, n_recent, cap=None,
 
     Returns (idx [B, Hq, cap] int32, count [B, Hq] int32, out [B, Hq, 128] fp32, alpha [B, Hq] fp32)."""
     lib = load()
-    B, Hq, d = q.shape
-    k, stride = _as_kv(k, B)
-    v, _ = _as_kv(v, B)
-    _need(key_sigs.dtype in (torch.int32, torch.uint32) and q_sigs.dtype == key_sigs.dtype, "signatures must be 32-bit")
-    _need(key_sigs.is_contiguous() and q_sigs.is_contiguous() and q.is_contiguous(), "inputs must be contiguous")
-    _need(q.dtype == k.dtype == v.dtype, "q, K, V must share a dtype")
+    dev, B, Hq, d = _query(q)
+    k, v, stride = _kv_pair(k, v, B, dev, q.dtype)
     Hkv, n = k.shape[1], k.shape[2]
-    _need(tuple(key_sigs.shape) == (B, Hkv, n), "key_sigs must be [B, Hkv, n]")
-    _need(tuple(q_sigs.shape) == (B, Hq), "q_sigs must be [B, Hq]")
+    _tensor(key_sigs, "key_sigs", dev, _CODES, (B, Hkv, n))
+    _tensor(q_sigs, "q_sigs", dev, (key_sigs.dtype,), (B, Hq))
     cap = capacity(n, m, n_sink, n_recent) if cap is None else int(cap)
-    dev = q.device
-    idx = torch.empty((B, Hq, cap), dtype=torch.int32, device=dev) if idx is None else idx
-    count = torch.empty((B, Hq), dtype=torch.int32, device=dev) if count is None else count
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
-    if want_alpha and alpha is None:
-        alpha = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    idx = _out(idx, "idx", (B, Hq, cap), dev, torch.int32)
+    count = _out(count, "count", (B, Hq), dev, torch.int32)
+    out = _out(out, "out", (B, Hq, d), dev)
+    if want_alpha or alpha is not None:
+        alpha = _out(alpha, "alpha", (B, Hq), dev)
     nb = lib.lcda_ws_bytes_sparse_decode_step(B, Hq, Hkv, d, n, cap)
     w = _ws(nb, dev, ws)
     st = lib.sparse_decode_step(_p(key_sigs), _p(q_sigs), _p(q), _p(k), _p(v), stride, B, Hq, Hkv, d, n, _dtype_code(q),
@@ -419,6 +476,18 @@ def sparse_decode_step(key_sigs, q_sigs, q, k, v, m, n_sink, n_recent, cap=None,
                                 w.numel() * w.element_size(), _stream(dev))
     _check("sparse_decode_step", st)
     return idx, count, out, alpha
+
+
+def stream_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor = None) -> None:
+    """The streaming-read probe (lcda_stream_read) over all of buf (a contiguous GPU tensor whose size in bytes is
+    a multiple of 16): enqueued on torch's current stream; time it with events."""
+    dev = _gpu(buf, "buf")
+    _tensor(buf, "buf", dev)
+    nbytes = buf.numel() * buf.element_size()
+    _need(nbytes % 16 == 0, "buf must hold a multiple of 16 bytes")
+    sink = _out(sink, "sink", (1,), dev, torch.int32)
+    _check("lcda_stream_read", load().lcda_stream_read(_p(buf), nbytes, int(workgroups), _p(sink), 0x9E3779B9,
+                                                       _stream(dev)))
 
 
 def set_tuning(key: str, value: int) -> None:

@@ -157,3 +157,31 @@ def test_workspace_sizes_of_an_empty_batch(lib):
     for stride in (0, 2 * 1000 * 128):
         assert lib.lcda_ws_bytes_cached_attn_lse(0, 8, 2, 128, 1000, stride) >= 0
         assert lib.lcda_ws_bytes_dense_decode_step(0, 8, 2, 128, 1000, stride, 64) >= 0
+
+
+@pytest.mark.parametrize("which", ["m", "n_sink", "n_recent"])
+def test_topk_rejects_huge_counts_before_summing(lib, which):
+    """m, n_sink and n_recent beyond INT32_MAX are refused before they are added up (a sum of huge int64 values
+    would overflow and could pass the capacity check)."""
+    big = (1 << 63) - 1
+    kw = dict(m=10, n_sink=2, n_recent=2)
+    kw[which] = big
+    st = lib.sig_score_topk(fake(), fake(), 1, 4, 1, 1000, kw["m"], kw["n_sink"], kw["n_recent"], fake(), 14, fake(),
+                            None, fake(), 1 << 30, None)
+    assert st == 1 and b"INT32_MAX" in lib.lcda_last_error()
+    st = lib.sig_score_topk_w(fake(), fake(), 2, 1, 4, 1, 1000, kw["m"], kw["n_sink"], kw["n_recent"], fake(), 14,
+                              fake(), None, fake(), 1 << 30, None)
+    assert st == 1 and b"INT32_MAX" in lib.lcda_last_error()
+    st = lib.sparse_decode_step(fake(), fake(), fake(), fake(), fake(), 0, 1, 4, 1, 128, 1000, 1, kw["m"],
+                                kw["n_sink"], kw["n_recent"], fake(), 14, fake(), fake(), None, fake(), 1 << 30, None)
+    assert st == 1 and b"INT32_MAX" in lib.lcda_last_error()
+
+
+def test_stream_read_rejects(lib):
+    """The streaming-read probe refuses null or misaligned buffers and bad grids before any launch."""
+    assert lib.lcda_stream_read(None, 1 << 20, 256, fake(), 0, None) == 1
+    assert lib.lcda_stream_read(fake(0x10008), 1 << 20, 256, fake(), 0, None) == 1
+    assert lib.lcda_stream_read(fake(), (1 << 20) + 4, 256, fake(), 0, None) == 1
+    assert lib.lcda_stream_read(fake(), 1 << 20, 0, fake(), 0, None) == 1
+    assert lib.lcda_stream_read(fake(), 1 << 20, 256, None, 0, None) == 1
+    assert lib.lcda_stream_read(None, 0, 256, None, 0, None) == 0   # nothing to read
