@@ -415,6 +415,8 @@ def bench_sparse(args, cfg, rot=None):
         "topk_sig_tbps": sig_bytes / (ms_t * 1e-3) / 1e12,
         "gather_tbps": gather_bytes / (ms_g * 1e-3) / 1e12,
         "gather_bytes": gather_bytes,
+        "topk_traffic": traffic_from_profile("topk_unit_sparse128k", sig_bytes, "topk_unit")
+                        if cfg.n * cfg.B == 8 * 131072 else None,
         "rotations": rot,
         "step_spread": replay_stats(st),
     }

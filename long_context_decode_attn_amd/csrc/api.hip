@@ -11,6 +11,7 @@
 #include "../../include/lcda.h"
 #include "common.h"
 #include "internal.h"
+#include "sparse.h"
 
 namespace lcda {
 

@@ -18,6 +18,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "sparse.h"
 #include "sig_proj.h"
 
 namespace lcda {

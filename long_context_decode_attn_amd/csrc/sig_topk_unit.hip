@@ -67,6 +67,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "sparse.h"
 #include "sig_proj.h"
 
 namespace lcda {

@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "sparse.h"
 
 namespace lcda {
 namespace {

@@ -29,6 +29,7 @@ KERNEL_SOURCES = {
     "split_mfma": (_C + "split_mfma.hip", _C + "mfma_tile.h", _C + "common.h", _C + "internal.h"),
     "split_rows": (_C + "split_rows.hip", _C + "mfma_tile.h", _C + "common.h", _C + "internal.h"),
     "split_valu": (_C + "split_valu.hip", _C + "common.h", _C + "internal.h"),
+    "topk_unit": (_C + "sig_topk_unit.hip", _C + "sparse.h", _C + "sig_proj.h", _C + "common.h", _C + "internal.h"),
 }
 
 
