@@ -254,9 +254,9 @@ int dense_decode_step(const void* q, const void* k, const void* v, int64_t kv_ba
  *
  *   arguments as in dense_decode_step, without a_doc, alpha_doc, ws, ws_bytes;
  *   stream must belong to the current device.
- * Errors: LCDA_EUNSUPPORTED when B*Hq exceeds 8192 query rows, or when
- * lcda_ws_bytes_dense_decode_step for the shapes exceeds
- * lcda_noalloc_scratch_bytes() (16 MiB less the counters: a 61,440-token
+ * Errors: LCDA_EUNSUPPORTED when B*Hq exceeds 8192 query rows, or when the
+ * workspace the call takes (its form, under the current lcda_set_tuning knobs)
+ * exceeds lcda_noalloc_scratch_bytes() (16 MiB less the counters: a 61,440-token
  * shared document read by 16 items of 32 query heads needs 8.5 MB); the other
  * errors of dense_decode_step.  Every call on a GPU uses that GPU's one array:
  * calls that can overlap on one GPU (work on concurrent streams) race and
@@ -287,7 +287,9 @@ const char* lcda_version(void);
 /* Launch-shape knobs, for measurement and tuning (process-wide; set them
  * before enqueuing work, never concurrently with other calls).  They change
  * how work is split over workgroups, never what is computed.  Workspace sizes
- * (lcda_ws_bytes_*) follow the current values.  Keys:
+ * (lcda_ws_bytes_*) do not depend on them: they cover every accepted setting,
+ * so a knob changed after a workspace was sized (on any thread) never makes it
+ * too small.  Keys (the *_wgs keys accept 1 .. 2048):
  *   "dense_wgs"      target workgroups of the MFMA split with 16/32-row tiles (256)
  *   "dense_wgs_nt4"  target workgroups of the MFMA split with 64-row tiles (256)
  *   "valu_wgs"       target workgroups of the fp32 dense split (512)

@@ -217,7 +217,22 @@ Tuning& tuning() {
 // blocks, then the local tokens (so no block spans both).
 int64_t fused_tokens(int64_t n, int64_t n_loc_max) { return (n + 31) / 32 * 32 + n_loc_max; }
 
+namespace {
+
+// The split plan under the knobs in t (plan_split uses the current ones).
+SplitPlan plan_split_t(const Tuning& t, int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens,
+                       bool shared);
+
+}  // namespace
+
 SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared) {
+    return plan_split_t(tuning(), dtype, gather, B, Hq, Hkv, n_tokens, shared);
+}
+
+namespace {
+
+SplitPlan plan_split_t(const Tuning& t, int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens,
+                       bool shared) {
     SplitPlan p{};
     const int G = Hq / Hkv;
     const int rows = shared ? B * G : G;
@@ -231,11 +246,11 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = 1;
         p.block = valu_step_tokens();
         units = B * Hq;
-        p.waves = (int)tuning().gather_waves;
-        target = (int)tuning().gather_wgs;
+        p.waves = (int)t.gather_waves;
+        target = (int)t.gather_wgs;
         p.grid_y = Hq;
         p.grid_z = B;
-    } else if (dtype == LCDA_BF16 && rows > 16 && tuning().rows_kernel) {
+    } else if (dtype == LCDA_BF16 && rows > 16 && t.rows_kernel) {
         // Many rows per KV head (a shared document): 64 rows per workgroup, every block read once.
         p.kernel = kRows;
         p.nt = 1;
@@ -244,7 +259,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = 32;
         units = bkv * Hkv * p.row_groups;
-        target = (int)(p.row_groups == 1 ? tuning().rows_wgs_single : tuning().rows_wgs);
+        target = (int)(p.row_groups == 1 ? t.rows_wgs_single : t.rows_wgs);
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
     } else if (dtype == LCDA_BF16) {
@@ -254,7 +269,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = 32;
         units = bkv * Hkv * p.row_groups;
-        target = (int)(p.nt == 4 ? tuning().dense_wgs_nt4 : tuning().dense_wgs);
+        target = (int)(p.nt == 4 ? t.dense_wgs_nt4 : t.dense_wgs);
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
     } else {
@@ -264,7 +279,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
         p.row_groups = (int)ceil_div(rows, p.rows_per_group);
         p.block = valu_step_tokens();
         units = bkv * Hkv * p.row_groups;
-        target = (int)tuning().valu_wgs;
+        target = (int)t.valu_wgs;
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
     }
@@ -273,7 +288,7 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
     int64_t splits = ceil_div(target, units > 0 ? units : 1);
     // Short ranges run as one split finished in place, unless there are too few
     // units to fill the chip that way.
-    if (nblocks <= tuning().direct_blocks && units >= target) splits = 1;
+    if (nblocks <= t.direct_blocks && units >= target) splits = 1;
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
     const int64_t bps = nblocks > 0 ? ceil_div(nblocks, splits) : 1;
     splits = nblocks > 0 ? ceil_div(nblocks, bps) : 1;
@@ -281,6 +296,61 @@ SplitPlan plan_split(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_t
     p.blocks_per_split = (int)bps;
     p.grid_x = p.splits;
     return p;
+}
+
+// Target workgroups accepted by lcda_set_tuning (its *_wgs keys).
+constexpr int64_t kMaxTargetWgs = 2048;
+
+// The largest split count any accepted knob setting gives a shape: the
+// workspace sizes (lcda_ws_bytes_*) follow it, so that lcda_set_tuning never
+// makes a workspace sized earlier too small.  More target workgroups, fewer
+// GATHER-ATT wavefronts and no direct runs only ever add splits; rows_kernel
+// picks between two kernels, so both are tried.
+int max_plan_splits(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared) {
+    int s = 1;
+    for (int rk = 0; rk <= 1; ++rk) {
+        Tuning t = tuning();
+        t.dense_wgs = t.dense_wgs_nt4 = t.valu_wgs = t.gather_wgs = t.rows_wgs = t.rows_wgs_single = kMaxTargetWgs;
+        t.gather_waves = 4;
+        t.direct_blocks = 0;
+        t.rows_kernel = rk;
+        s = std::max(s, plan_split_t(t, dtype, gather, B, Hq, Hkv, n_tokens, shared).splits);
+    }
+    return s;
+}
+
+// Workspace of one split pass: under the current knobs (any = false) or under
+// any accepted ones (any = true).
+size_t split_ws(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared, bool any) {
+    const int s = any ? max_plan_splits(dtype, gather, B, Hq, Hkv, n_tokens, shared)
+                      : plan_split(dtype, gather, B, Hq, Hkv, n_tokens, shared).splits;
+    return partial_layout(B, Hq, s).bytes;
+}
+
+}  // namespace
+
+// Workspace of dense_decode_step in the form a call with these arguments takes
+// (the 64-row shared-document pass, the two calls, or the fused split), under
+// the current knobs (any = false) or any accepted ones (any = true, where the
+// form a knob could switch to is covered as well).
+size_t dense_step_ws(int dtype, int B, int Hq, int Hkv, int64_t n, int64_t kv_batch_stride, int64_t n_loc_max,
+                     bool a_doc, bool any) {
+    const bool shared = kv_batch_stride == 0 && B > 1;
+    size_t need = 0;
+    if (shared && dtype == LCDA_BF16 && !a_doc && n > 0 && n_loc_max > 0) {
+        const SplitPlan p = plan_split(dtype, false, B, Hq, Hkv, n, true);
+        const size_t rows = split_ws(dtype, false, B, Hq, Hkv, n, true, any);
+        if (p.kernel == kRows && !any) return rows;
+        need = rows;
+    }
+    if (dtype != LCDA_BF16 || shared || a_doc || n == 0 || any) {
+        // the two calls: each one's workspace, then the doc-only (A, alpha)
+        need = std::max(need, split_ws(dtype, false, B, Hq, Hkv, n, kv_batch_stride == 0, any) +
+                                  split_ws(dtype, false, B, Hq, Hkv, n_loc_max, false, any) +
+                                  round_up((size_t)B * Hq * (kD + 1) * sizeof(float)));
+        if (!any) return need;
+    }
+    return std::max(need, split_ws(dtype, false, B, Hq, Hkv, fused_tokens(n, n_loc_max), false, any));
 }
 
 hipError_t launch_split(const SplitPlan& p, const SplitArgs& a, int dtype, hipStream_t st) {
@@ -304,13 +374,14 @@ int lcda_set_tuning(const char* key, int64_t value) {
     if (!key) return fail(LCDA_EINVAL, "lcda_set_tuning: key is NULL");
     if (value < 0) return fail(LCDA_EINVAL, "lcda_set_tuning: %s = %lld < 0", key, (long long)value);
     Tuning& t = tuning();
-    if (!strcmp(key, "dense_wgs") && value > 0) t.dense_wgs = value;
-    else if (!strcmp(key, "dense_wgs_nt4") && value > 0) t.dense_wgs_nt4 = value;
-    else if (!strcmp(key, "valu_wgs") && value > 0) t.valu_wgs = value;
-    else if (!strcmp(key, "gather_wgs") && value > 0) t.gather_wgs = value;
+    const bool wgs_ok = value > 0 && value <= kMaxTargetWgs;   // the workspace sizes assume at most this
+    if (!strcmp(key, "dense_wgs") && wgs_ok) t.dense_wgs = value;
+    else if (!strcmp(key, "dense_wgs_nt4") && wgs_ok) t.dense_wgs_nt4 = value;
+    else if (!strcmp(key, "valu_wgs") && wgs_ok) t.valu_wgs = value;
+    else if (!strcmp(key, "gather_wgs") && wgs_ok) t.gather_wgs = value;
     else if (!strcmp(key, "gather_waves") && (value == 4 || value == 8 || value == 16)) t.gather_waves = value;
-    else if (!strcmp(key, "rows_wgs") && value > 0) t.rows_wgs = value;
-    else if (!strcmp(key, "rows_wgs_single") && value > 0) t.rows_wgs_single = value;
+    else if (!strcmp(key, "rows_wgs") && wgs_ok) t.rows_wgs = value;
+    else if (!strcmp(key, "rows_wgs_single") && wgs_ok) t.rows_wgs_single = value;
     else if (!strcmp(key, "rows_kernel") && value <= 1) t.rows_kernel = value;
     else if (!strcmp(key, "rows_variant") && value <= 8) t.rows_variant = value;
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
@@ -350,10 +421,8 @@ int64_t lcda_get_tuning(const char* key) {
 
 size_t lcda_ws_bytes_cached_attn_lse(int B, int Hq, int Hkv, int d, int64_t n, int64_t kv_batch_stride) {
     if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX) return 0;
-    const SplitPlan p = plan_split(LCDA_BF16, false, B, Hq, Hkv, n, kv_batch_stride == 0);
-    const SplitPlan p32 = plan_split(LCDA_F32, false, B, Hq, Hkv, n, kv_batch_stride == 0);
-    const int s = p.splits > p32.splits ? p.splits : p32.splits;
-    return partial_layout(B, Hq, s).bytes;
+    return std::max(split_ws(LCDA_BF16, false, B, Hq, Hkv, n, kv_batch_stride == 0, true),
+                    split_ws(LCDA_F32, false, B, Hq, Hkv, n, kv_batch_stride == 0, true));
 }
 
 size_t lcda_ws_bytes_lse_merge_local(int B, int Hq, int Hkv, int d, int64_t n_loc_max) {
@@ -367,8 +436,7 @@ size_t lcda_ws_bytes_sig_score_topk(int B, int Hq, int Hkv, int64_t n) {
 
 size_t lcda_ws_bytes_gather_attn(int B, int Hq, int Hkv, int d, int64_t cap) {
     if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || cap < 0 || cap > INT32_MAX) return 0;
-    const SplitPlan p = plan_split(LCDA_BF16, true, B, Hq, Hkv, cap, false);
-    return partial_layout(B, Hq, p.splits).bytes;
+    return split_ws(LCDA_BF16, true, B, Hq, Hkv, cap, false, true);
 }
 
 static int cached_attn_lse_impl(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int d,
@@ -492,13 +560,12 @@ size_t lcda_ws_bytes_dense_decode_step(int B, int Hq, int Hkv, int d, int64_t n,
     if (d != kD || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || n < 0 || n > INT32_MAX || n_loc_max < 0 ||
         fused_tokens(n, n_loc_max) > INT32_MAX)
         return 0;
-    // the two-call form needs its own workspace and the doc-only (A, alpha) buffers
-    const size_t two = lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride) +
-                       lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max) +
-                       round_up((size_t)B * Hq * (kD + 1) * sizeof(float));
-    const SplitPlan p = plan_split(LCDA_BF16, false, B, Hq, Hkv, fused_tokens(n, n_loc_max), false);
-    const size_t fused = partial_layout(B, Hq, p.splits).bytes;
-    return two > fused ? two : fused;
+    // Whichever form a call takes (any dtype, with or without a_doc), under any accepted knobs.
+    size_t need = 0;
+    for (int dt : {LCDA_BF16, LCDA_F32})
+        for (int a_doc = 0; a_doc <= 1; ++a_doc)
+            need = std::max(need, dense_step_ws(dt, B, Hq, Hkv, n, kv_batch_stride, n_loc_max, a_doc != 0, true));
+    return need;
 }
 
 }  // extern "C"
@@ -531,7 +598,7 @@ int dense_decode_step_impl(const void* q, const void* k, const void* v, int64_t 
     RETURN_IF(check_ptr(fn, "ws", ws, false));
     if ((a_doc == nullptr) != (alpha_doc == nullptr))
         return fail(LCDA_EINVAL, "%s: a_doc and alpha_doc must both be given or both be NULL", fn);
-    const size_t need = lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, kv_batch_stride, n_loc_max);
+    const size_t need = dense_step_ws(dtype, B, Hq, Hkv, n, kv_batch_stride, n_loc_max, a_doc != nullptr, false);
     if (!work) return LCDA_OK;
     if (!ws || ws_bytes < need)
         return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, need);
@@ -574,8 +641,8 @@ int dense_decode_step_impl(const void* q, const void* k, const void* v, int64_t 
     if (dtype != LCDA_BF16 || shared || a_doc != nullptr || n == 0) {
         // Two-call form: cached_attn_lse, then lse_merge_local on its result.
         char* w = static_cast<char*>(ws);
-        const size_t w1 = lcda_ws_bytes_cached_attn_lse(B, Hq, Hkv, d, n, kv_batch_stride);
-        const size_t w2 = lcda_ws_bytes_lse_merge_local(B, Hq, Hkv, d, n_loc_max);
+        const size_t w1 = split_ws(dtype, false, B, Hq, Hkv, n, kv_batch_stride == 0, false);
+        const size_t w2 = split_ws(dtype, false, B, Hq, Hkv, n_loc_max, false, false);
         float* A = a_doc;
         float* al = alpha_doc;
         if (!A) {

@@ -27,6 +27,8 @@ int dense_decode_step_impl(const void* q, const void* k, const void* v, int64_t 
                            const void* k_loc, const void* v_loc, const int32_t* n_loc, int64_t n_loc_max, int B,
                            int Hq, int Hkv, int d, int dtype, float* out, float* alpha_out, float* a_doc,
                            float* alpha_doc, void* ws, size_t ws_bytes, unsigned long long* ctr, void* stream);
+size_t dense_step_ws(int dtype, int B, int Hq, int Hkv, int64_t n, int64_t kv_batch_stride, int64_t n_loc_max,
+                     bool a_doc, bool any);
 
 namespace {
 
@@ -74,7 +76,11 @@ int dense_decode_step_noalloc(const void* q, const void* k, const void* v, int64
     if (B > 0 && Hq > 0 && (int64_t)B * Hq > kNoallocMaxRows)
         return set_error(LCDA_EUNSUPPORTED, "%s: B*Hq = %lld query rows exceed the %d supported", fn,
                          (long long)B * Hq, kNoallocMaxRows);
-    const size_t need = lcda_ws_bytes_dense_decode_step(B, Hq, Hkv, d, n, kv_batch_stride, n_loc_max);
+    // The workspace this call takes under the current knobs (the shape checks come below).
+    const bool shapes_ok = d == kD && B >= 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && n >= 0 && n <= INT32_MAX &&
+                           n_loc_max >= 0 && n_loc_max <= INT32_MAX && (dtype == LCDA_F32 || dtype == LCDA_BF16);
+    const size_t need =
+        shapes_ok ? dense_step_ws(dtype, B, Hq, Hkv, n, kv_batch_stride, n_loc_max, false, false) : 0;
     if (need > lcda_noalloc_scratch_bytes())
         return set_error(LCDA_EUNSUPPORTED, "%s: the shapes need %zu bytes of scratch, more than the %zu held", fn,
                          need, lcda_noalloc_scratch_bytes());

@@ -185,3 +185,33 @@ def test_stream_read_rejects(lib):
     assert lib.lcda_stream_read(fake(), 1 << 20, 0, fake(), 0, None) == 1
     assert lib.lcda_stream_read(fake(), 1 << 20, 256, None, 0, None) == 1
     assert lib.lcda_stream_read(None, 0, 256, None, 0, None) == 0   # nothing to read
+
+
+def test_workspace_sizes_do_not_follow_the_knobs(lib):
+    """Workspace sizes cover every accepted knob setting, so a knob changed after a workspace was sized never
+    makes it too small; target-workgroup knobs beyond that range are refused."""
+    shapes = [
+        ("lcda_ws_bytes_cached_attn_lse", (1, 32, 8, 128, 61440, 8 * 61440 * 128)),
+        ("lcda_ws_bytes_cached_attn_lse", (16, 32, 8, 128, 61440, 0)),
+        ("lcda_ws_bytes_gather_attn", (8, 32, 8, 128, 4352)),
+        ("lcda_ws_bytes_dense_decode_step", (1, 32, 8, 128, 61440, 8 * 61440 * 128, 256)),
+        ("lcda_ws_bytes_dense_decode_step", (16, 32, 8, 128, 61440, 0, 512)),
+        ("lcda_ws_bytes_sig_score_topk", (8, 32, 8, 131072)),
+        ("lcda_ws_bytes_sparse_decode_step", (8, 32, 8, 128, 131072, 4352)),
+    ]
+    keys = {"dense_wgs": 2048, "dense_wgs_nt4": 2048, "valu_wgs": 2048, "gather_wgs": 2048, "gather_waves": 4,
+            "rows_wgs": 2048, "rows_wgs_single": 2048, "rows_kernel": 0, "direct_blocks": 0, "topk_kernel": 0,
+            "topk_subs": 1, "topk_wgs": 2048}
+    before = [getattr(lib, f)(*a) for f, a in shapes]
+    saved = {k: lib.lcda_get_tuning(k.encode()) for k in keys}
+    try:
+        for k, v in keys.items():
+            assert lib.lcda_set_tuning(k.encode(), v) == 0, k
+        after = [getattr(lib, f)(*a) for f, a in shapes]
+    finally:
+        for k, v in saved.items():
+            assert lib.lcda_set_tuning(k.encode(), v) == 0
+    assert after == before
+    for k in ("dense_wgs", "dense_wgs_nt4", "valu_wgs", "gather_wgs", "rows_wgs", "rows_wgs_single"):
+        assert lib.lcda_set_tuning(k.encode(), 4096) == 1
+        assert lib.lcda_get_tuning(k.encode()) == saved[k]
