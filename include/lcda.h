@@ -313,7 +313,9 @@ const char* lcda_version(void);
  *   "dense_variant"  MFMA split K/V pipeline (16-row tiles): 0 = nontemporal
  *                    loads one block ahead, 1 = cached loads one block ahead,
  *                    2 = nontemporal two blocks ahead, 3 = as 0 with registers
- *                    capped so two workgroups share a CU (0)
+ *                    capped so two workgroups share a CU; 4 = bf16 on the VALU
+ *                    split instead of MFMA (dense_decode_step then takes the
+ *                    two-call form), for comparison (0)
  *   "gather_variant" GATHER-ATT rows: 0 = nontemporal loads, 1 = cached loads (0)
  *   "topk_subs"      TOPK scans: 4096-position sub-chunks per workgroup (1..64;
  *                    more where a head would otherwise exceed 64 chunks); 0 picks

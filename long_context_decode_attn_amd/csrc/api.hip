@@ -262,7 +262,7 @@ SplitPlan plan_split_t(const Tuning& t, int dtype, bool gather, int B, int Hq, i
         target = (int)(p.row_groups == 1 ? t.rows_wgs_single : t.rows_wgs);
         p.grid_y = Hkv;
         p.grid_z = bkv * p.row_groups;
-    } else if (dtype == LCDA_BF16) {
+    } else if (dtype == LCDA_BF16 && t.dense_variant != 4) {
         p.kernel = kMfma16;
         p.nt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
         p.rows_per_group = 16 * p.nt;
@@ -305,16 +305,20 @@ constexpr int64_t kMaxTargetWgs = 2048;
 // workspace sizes (lcda_ws_bytes_*) follow it, so that lcda_set_tuning never
 // makes a workspace sized earlier too small.  More target workgroups, fewer
 // GATHER-ATT wavefronts and no direct runs only ever add splits; rows_kernel
-// picks between two kernels, so both are tried.
+// and dense_variant 4 pick between kernels, so each choice is tried.
 int max_plan_splits(int dtype, bool gather, int B, int Hq, int Hkv, int64_t n_tokens, bool shared) {
     int s = 1;
     for (int rk = 0; rk <= 1; ++rk) {
-        Tuning t = tuning();
-        t.dense_wgs = t.dense_wgs_nt4 = t.valu_wgs = t.gather_wgs = t.rows_wgs = t.rows_wgs_single = kMaxTargetWgs;
-        t.gather_waves = 4;
-        t.direct_blocks = 0;
-        t.rows_kernel = rk;
-        s = std::max(s, plan_split_t(t, dtype, gather, B, Hq, Hkv, n_tokens, shared).splits);
+        for (int dv : {0, 4}) {   // dense_variant 4 puts bf16 on the VALU split
+            Tuning t = tuning();
+            t.dense_wgs = t.dense_wgs_nt4 = t.valu_wgs = t.gather_wgs = t.rows_wgs = t.rows_wgs_single =
+                kMaxTargetWgs;
+            t.gather_waves = 4;
+            t.direct_blocks = 0;
+            t.rows_kernel = rk;
+            t.dense_variant = dv;
+            s = std::max(s, plan_split_t(t, dtype, gather, B, Hq, Hkv, n_tokens, shared).splits);
+        }
     }
     return s;
 }
@@ -343,7 +347,7 @@ size_t dense_step_ws(int dtype, int B, int Hq, int Hkv, int64_t n, int64_t kv_ba
         if (p.kernel == kRows && !any) return rows;
         need = rows;
     }
-    if (dtype != LCDA_BF16 || shared || a_doc || n == 0 || any) {
+    if (dtype != LCDA_BF16 || shared || a_doc || n == 0 || any || tuning().dense_variant == 4) {
         // the two calls: each one's workspace, then the doc-only (A, alpha)
         need = std::max(need, split_ws(dtype, false, B, Hq, Hkv, n, kv_batch_stride == 0, any) +
                                   split_ws(dtype, false, B, Hq, Hkv, n_loc_max, false, any) +
@@ -385,7 +389,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "rows_kernel") && value <= 1) t.rows_kernel = value;
     else if (!strcmp(key, "rows_variant") && value <= 8) t.rows_variant = value;
     else if (!strcmp(key, "direct_blocks")) t.direct_blocks = value;
-    else if (!strcmp(key, "dense_variant") && value <= 3) t.dense_variant = value;
+    else if (!strcmp(key, "dense_variant") && value <= 4) t.dense_variant = value;
     else if (!strcmp(key, "gather_variant") && value <= 1) t.gather_variant = value;
     else if (!strcmp(key, "topk_subs") && value <= 64) t.topk_subs = value;
     else if (!strcmp(key, "topk_wgs") && value > 0) t.topk_wgs = value;
@@ -638,7 +642,7 @@ int dense_decode_step_impl(const void* q, const void* k, const void* v, int64_t 
                           static_cast<hipStream_t>(stream));
         }
     }
-    if (dtype != LCDA_BF16 || shared || a_doc != nullptr || n == 0) {
+    if (dtype != LCDA_BF16 || shared || a_doc != nullptr || n == 0 || tuning().dense_variant == 4) {
         // Two-call form: cached_attn_lse, then lse_merge_local on its result.
         char* w = static_cast<char*>(ws);
         const size_t w1 = split_ws(dtype, false, B, Hq, Hkv, n, kv_batch_stride == 0, false);

@@ -308,10 +308,11 @@ def test_decode_step_config2_full_size(orc):
 
 
 # ------------------------------------------------------- kernel variants ----
-@pytest.mark.parametrize("variant,wgs", [(0, 256), (1, 256), (2, 256), (3, 256), (3, 512), (3, 1024)])
+@pytest.mark.parametrize("variant,wgs", [(0, 256), (1, 256), (2, 256), (3, 256), (3, 512), (3, 1024), (4, 256)])
 def test_dense_split_variants(orc, variant, wgs):
-    """Every MFMA split variant (nontemporal / cached loads, one or two blocks ahead, two waves per SIMD) and
-    launch width gives the oracle's result, for the plain call and the fused step, ragged and short ranges."""
+    """Every MFMA split variant (nontemporal / cached loads, one or two blocks ahead, two waves per SIMD), the bf16
+    VALU split kept for comparison (variant 4), and launch width give the oracle's result, for the plain call and
+    the fused step, ragged and short ranges."""
     old = ops.get_tuning("dense_variant")
     old_w = ops.get_tuning("dense_wgs")
     ops.set_tuning("dense_variant", variant)
