@@ -65,8 +65,9 @@ struct ValuSmem {
 
 // R: query rows per unit (dense) - 1 in gather mode.  U: rows per lane group per step.
 // NTL: K/V rows are loaded nontemporal.  W: wavefronts per workgroup, which
-// share the split's token range step by step.
-template <typename T, int R, int U, bool GATHER, bool NTL, int W = kWaves>
+// share the split's token range step by step.  RA: steps whose rows are in
+// flight ahead of the step computed (positions one step further).
+template <typename T, int R, int U, bool GATHER, bool NTL, int W = kWaves, int RA = 2>
 __global__ __launch_bounds__(64 * W) void k_split_valu(SplitArgs a) {
     __shared__ ValuSmem<T, R, W> sm;
     const int lane = threadIdx.x & 63;
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(64 * W) void k_split_valu(SplitArgs a) {
     const int64_t stride = (int64_t)W * kStep;
 
     // Software pipeline over steps of kStep tokens: the positions (gather mode:
-    // entries of the index list) are requested three steps ahead and the K/V
-    // rows two steps ahead of the step being computed.  Requests past the end
+    // entries of the index list) are requested RA + 1 steps ahead and the K/V
+    // rows RA steps ahead of the step being computed.  Requests past the end
     // of the range are clamped to its last entry (cache-resident) and ignored.
     struct Step {
         Row8<T> k[U], v[U];
@@ -228,31 +229,30 @@ __global__ __launch_bounds__(64 * W) void k_split_valu(SplitArgs a) {
         }
     };
 
+    // Step i of this wavefront lives in slot i mod NS of the buffers: at step
+    // i the positions of step i + NS replace its own (fetched RA steps ago),
+    // the rows of step i + RA are requested, and step i is computed.
     int64_t t0 = t_begin + (int64_t)w * kStep;
     if (t0 < t_end) {
-        int32_t p0[U], p1[U], p2[U];
-        Step s0, s1, s2;
-        positions(t0, p0);
-        positions(t0 + stride, p1);
-        positions(t0 + 2 * stride, p2);
-        fetch(s0, p0);
-        fetch(s1, p1);
-        while (true) {
-            positions(t0 + 3 * stride, p0);
-            fetch(s2, p2);
-            compute(s0, t0);
-            t0 += stride;
-            if (t0 >= t_end) break;
-            positions(t0 + 3 * stride, p1);
-            fetch(s0, p0);
-            compute(s1, t0);
-            t0 += stride;
-            if (t0 >= t_end) break;
-            positions(t0 + 3 * stride, p2);
-            fetch(s1, p1);
-            compute(s2, t0);
-            t0 += stride;
-            if (t0 >= t_end) break;
+        constexpr int NS = RA + 1;
+        int32_t pp[NS][U];
+        Step ss[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) positions(t0 + k * stride, pp[k]);
+#pragma unroll
+        for (int k = 0; k < RA; ++k) fetch(ss[k], pp[k]);
+        bool done = false;
+        while (!done) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                if (!done) {
+                    positions(t0 + NS * stride, pp[u]);
+                    fetch(ss[(u + RA) % NS], pp[(u + RA) % NS]);
+                    compute(ss[u], t0);
+                    t0 += stride;
+                    done = t0 >= t_end;
+                }
+            }
         }
     }
 

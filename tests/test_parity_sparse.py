@@ -255,13 +255,16 @@ def test_gather_clamps_out_of_range_entries(orc):
     assert torch.all(out[1, 5] == 0) and torch.isneginf(alpha[1, 5])     # a negative count is an empty set
 
 
-@pytest.mark.parametrize("waves,wgs", [(4, 2048), (4, 16), (8, 16), (8, 512), (16, 16), (16, 300)])
-def test_gather_workgroup_shapes(orc, waves, wgs):
+@pytest.mark.parametrize("waves,wgs,variant", [(4, 2048, 0), (4, 16, 0), (8, 16, 0), (8, 512, 0), (16, 16, 0),
+                                               (16, 300, 0), (4, 16, 1), (4, 512, 1)])
+def test_gather_workgroup_shapes(orc, waves, wgs, variant):
     """GATHER-ATT with 4, 8 or 16 wavefronts per workgroup, as one split per row finished in place (few
-    workgroups) and as several splits merged by the combine pass; an empty and a one-row set included."""
-    old = (ops.get_tuning("gather_waves"), ops.get_tuning("gather_wgs"))
+    workgroups) and as several splits merged by the combine pass, with nontemporal or (variant 1, four
+    wavefronts) cached row loads; an empty and a one-row set included."""
+    old = (ops.get_tuning("gather_waves"), ops.get_tuning("gather_wgs"), ops.get_tuning("gather_variant"))
     ops.set_tuning("gather_waves", waves)
     ops.set_tuning("gather_wgs", wgs)
+    ops.set_tuning("gather_variant", variant)
     try:
         B, Hq, Hkv, n = 2, 8, 2, 9000
         q, k, v = _kv(B, Hq, Hkv, n, torch.bfloat16, 81)
@@ -270,7 +273,7 @@ def test_gather_workgroup_shapes(orc, waves, wgs):
         ri, rc, _ = orc.sig_score_topk(sig_np(ks), sig_np(qs), 700, 64, 64)
         rc[0, 1] = 0
         rc[1, 2] = 1
-        print("case gather waves=%d wgs=%d" % (waves, wgs), flush=True)
+        print("case gather waves=%d wgs=%d variant=%d" % (waves, wgs, variant), flush=True)
         out, alpha = ops.gather_attn(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(ri).to(DEV),
                                      torch.from_numpy(rc).to(DEV))
         torch.cuda.synchronize()
@@ -283,3 +286,4 @@ def test_gather_workgroup_shapes(orc, waves, wgs):
     finally:
         ops.set_tuning("gather_waves", old[0])
         ops.set_tuning("gather_wgs", old[1])
+        ops.set_tuning("gather_variant", old[2])
