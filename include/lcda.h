@@ -331,8 +331,12 @@ const char* lcda_version(void);
  *   "sparse_fused"   sparse_decode_step: 1 = SCORE + TOPK + GATHER-ATT in the one
  *                    TOPK launch where that form applies; 0 = sig_score_topk then
  *                    gather_attn (0)
+ *   "wide_chunk"     sig_score_topk_w: positions per chunk, a multiple of 4096 up
+ *                    to 32768 (raised where the workspace bound n / 2048 chunks
+ *                    asks); 0 picks the length whose grid fills the device's
+ *                    workgroup slots (0)
  * Returns LCDA_EINVAL for an unknown key or a negative (or, except
- * direct_blocks, zero) value.  lcda_get_tuning returns -1 for an unknown key. */
+ * direct_blocks and wide_chunk, zero) value.  lcda_get_tuning returns -1 for an unknown key. */
 int lcda_set_tuning(const char* key, int64_t value);
 int64_t lcda_get_tuning(const char* key);
 

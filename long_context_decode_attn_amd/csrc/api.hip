@@ -12,6 +12,7 @@
 #include "common.h"
 #include "internal.h"
 #include "sparse.h"
+#include "wide.h"
 
 namespace lcda {
 
@@ -45,6 +46,11 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// lcda_set_tuning "wide_chunk": positions per chunk of sig_score_topk_w (0:
+// from the device's workgroup slots).  Kept here, not in Tuning: the split
+// kernels' sources do not change with the wide path's knobs.
+int64_t g_wide_chunk = 0;
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t elem_bytes(int dtype) { return dtype == LCDA_F32 ? 4 : 2; }
 
@@ -396,6 +402,7 @@ int lcda_set_tuning(const char* key, int64_t value) {
     else if (!strcmp(key, "topk_kernel") && value <= 1) t.topk_kernel = value;
     else if (!strcmp(key, "topk_spin") && value <= (1 << 20)) t.topk_spin = value;
     else if (!strcmp(key, "sparse_fused") && value <= 1) t.sparse_fused = value;
+    else if (!strcmp(key, "wide_chunk") && (value == 0 || (value % 4096 == 0 && value <= kWideMaxL))) g_wide_chunk = value;
     else return fail(LCDA_EINVAL, "lcda_set_tuning: unknown key or value for '%s'", key);
     return LCDA_OK;
 }
@@ -420,6 +427,7 @@ int64_t lcda_get_tuning(const char* key) {
     if (!strcmp(key, "topk_kernel")) return t.topk_kernel;
     if (!strcmp(key, "topk_spin")) return t.topk_spin;
     if (!strcmp(key, "sparse_fused")) return t.sparse_fused;
+    if (!strcmp(key, "wide_chunk")) return g_wide_chunk;
     return -1;
 }
 
@@ -803,9 +811,33 @@ int sig_score_topk_q(const uint32_t* key_sigs, const void* q, int q_dtype, const
                      n_recent, idx, cap, count, scores, ws, ws_bytes, stream);
 }
 
+// Workspace of sig_score_topk_w: distance bytes ([B, Hkv, groups][n][HG]: at
+// most 2 B Hq n bytes, as HG <= 2G - 1 for G <= 8 and groups * 8 < 2G above),
+// per-chunk histograms (rows padded to 16 bytes, sized for the widest code),
+// per-chunk offsets and per-row thresholds.  W = 1 may run the one-word kernel
+// instead, in the same workspace, which is sized for that too (its layout only
+// grows with Hkv, so Hkv = Hq bounds it).
+struct WideLayout {
+    size_t dist, hist, rec, rowrec, bytes;
+    int64_t n16, nc_max;
+};
+constexpr int kWideBinsP = 520;   // 513 bins padded to a multiple of 8
+WideLayout wide_layout(int B, int Hq, int64_t n) {
+    WideLayout l{};
+    const size_t rows = (size_t)B * Hq;
+    l.n16 = (n + 15) / 16 * 16;
+    l.nc_max = std::max<int64_t>(1, ceil_div(n, kWideMinL));
+    l.dist = 0;
+    l.hist = l.dist + round_up(2 * rows * (size_t)l.n16);
+    l.rec = l.hist + round_up(3 * rows * (size_t)l.nc_max * kWideBinsP * sizeof(uint16_t));
+    l.rowrec = l.rec + round_up(rows * (size_t)l.nc_max * 2 * sizeof(uint32_t));
+    l.bytes = l.rowrec + round_up(rows * 2 * sizeof(int32_t));
+    return l;
+}
+
 size_t lcda_ws_bytes_sig_score_topk_w(int B, int Hq, int64_t n) {
     if (B < 0 || Hq <= 0 || n < 0 || n > INT32_MAX) return 0;
-    return round_up((size_t)B * Hq * (size_t)n * sizeof(uint16_t)) + 256;
+    return std::max(wide_layout(B, Hq, n).bytes, topk_layout(B, Hq, Hq, n).bytes);
 }
 
 int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, int B, int Hq, int Hkv, int64_t n,
@@ -838,6 +870,10 @@ int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, in
     const size_t need_ws = lcda_ws_bytes_sig_score_topk_w(B, Hq, n);
     if (!ws || ws_bytes < need_ws)
         return fail(LCDA_EWORKSPACE, "%s: workspace %zu bytes < %zu required", fn, ws_bytes, need_ws);
+    // One word without scores: the one-word kernel computes this very selection.
+    if (W == 1 && !scores && Hq / Hkv <= 8)
+        return topk_impl(fn, key_sigs, const_cast<uint32_t*>(q_sigs), nullptr, 0, nullptr, 0, false, B, Hq, Hkv, n, m,
+                         n_sink, n_recent, idx, cap, count, nullptr, ws, ws_bytes, stream);
     WideArgs a{};
     a.key_sigs = key_sigs;
     a.q_sigs = q_sigs;
@@ -854,7 +890,36 @@ int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, in
     a.idx = idx;
     a.count = count;
     a.scores = scores;
-    a.dist = static_cast<uint16_t*>(ws);
+    a.HG = wide_group(a.G);
+    a.ng = (a.G + a.HG - 1) / a.HG;
+    const WideLayout l = wide_layout(B, Hq, n);
+    // Chunks: as many as make the histogram and compaction grids fill the
+    // workgroup slots of the device in whole rounds (one round where the
+    // chunk length allows), at most 32 per head where that suffices (the
+    // select pass stages 32 chunks at a time), never more than the workspace
+    // holds (n / kWideMinL) nor longer than kWideMaxL positions; the length
+    // is a whole number of histogram-loop turns and compaction tiles.
+    const int64_t units = (int64_t)B * Hkv * a.ng;
+    const int64_t slots = (int64_t)std::max(1, wide_slots_per_cu(W, a.HG)) * std::max(1, device_cus());
+    const int64_t nc_min = ceil_div(n, kWideMaxL);
+    int64_t want = 1;
+    for (int64_t k = 1;; ++k) {
+        want = std::max<int64_t>(1, k * slots / units);
+        if (want >= nc_min) break;
+    }
+    if (want > 32) want = std::max<int64_t>(32, nc_min);
+    want = std::min(want, l.nc_max);
+    const int64_t gran = wide_granule(W);   // divides kWideMaxL
+    a.L = n > 0 ? ceil_div(ceil_div(n, want), gran) * gran : gran;
+    if (g_wide_chunk > 0) a.L = std::max(g_wide_chunk, ceil_div(ceil_div(n, l.nc_max), gran) * gran);
+    a.nc = ceil_div(n, a.L);
+    a.dstride = l.n16 * a.HG;
+    a.vec = (n * W) % 4 == 0;   // key_sigs is 16-byte aligned (checked above)
+    char* base = static_cast<char*>(ws);
+    a.dist = reinterpret_cast<uint8_t*>(base + l.dist);
+    a.hist = reinterpret_cast<uint16_t*>(base + l.hist);
+    a.rec = reinterpret_cast<uint32_t*>(base + l.rec);
+    a.rowrec = reinterpret_cast<int32_t*>(base + l.rowrec);
     return hip_status(fn, launch_topk_wide(a, static_cast<hipStream_t>(stream)));
 }
 

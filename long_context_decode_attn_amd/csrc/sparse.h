@@ -1,24 +1,11 @@
 // sparse.h - host-side launch interfaces of the sparse path's kernels: the
-// signature encoder (T_map), SCORE + TOPK (one-word and wide codes) and the
+// signature encoder (T_map), SCORE + TOPK over one-word codes and the
 // one-launch SCORE + TOPK (+ GATHER-ATT) form.
 #pragma once
 
 #include "internal.h"
 
 namespace lcda {
-
-// Signature top-k over codes of W words (one workgroup per query head).
-struct WideArgs {
-    const uint32_t* key_sigs;   // [B, Hkv, n, W]
-    const uint32_t* q_sigs;     // [B, Hq, W]
-    int W, B, Hq, Hkv, G;
-    int64_t n, m, n_sink, n_recent, cap;
-    int32_t* idx;               // [B, Hq, cap]
-    int32_t* count;             // [B, Hq]
-    int16_t* scores;            // [B, Hq, n] or null
-    uint16_t* dist;             // ws: [B, Hq, n] distances
-};
-hipError_t launch_topk_wide(const WideArgs& a, hipStream_t st);
 
 // Random-projection codes (T_map).
 struct EncodeArgs {

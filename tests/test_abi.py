@@ -198,10 +198,11 @@ def test_workspace_sizes_do_not_follow_the_knobs(lib):
         ("lcda_ws_bytes_dense_decode_step", (16, 32, 8, 128, 61440, 0, 512)),
         ("lcda_ws_bytes_sig_score_topk", (8, 32, 8, 131072)),
         ("lcda_ws_bytes_sparse_decode_step", (8, 32, 8, 128, 131072, 4352)),
+        ("lcda_ws_bytes_sig_score_topk_w", (8, 32, 131072)),
     ]
     keys = {"dense_wgs": 2048, "dense_wgs_nt4": 2048, "valu_wgs": 2048, "gather_wgs": 2048, "gather_waves": 4,
             "rows_wgs": 2048, "rows_wgs_single": 2048, "rows_kernel": 0, "direct_blocks": 0, "topk_kernel": 0,
-            "topk_subs": 1, "topk_wgs": 2048}
+            "topk_subs": 1, "topk_wgs": 2048, "wide_chunk": 4096}
     before = [getattr(lib, f)(*a) for f, a in shapes]
     saved = {k: lib.lcda_get_tuning(k.encode()) for k in keys}
     try:

@@ -52,3 +52,62 @@ def test_wide_massive_ties(orc, W, pool):
 def test_wide_large_and_empty(orc):
     _case(orc, 8, 1, 8, 2, 131072, 4096, 128, 128, 970, scores=False)
     _case(orc, 4, 2, 4, 1, 0, 10, 2, 2, 971)
+
+
+@pytest.mark.parametrize("W", [1, 4, 16])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (6, 2), (24, 2), (16, 2)])
+def test_wide_head_groups(orc, W, Hq, Hkv):
+    """G = 1, 3, 12 and 8 query heads per KV head: one workgroup takes up to 8 of a KV head's query heads (a
+    partial group when G is not 1, 2, 4 or 8); chunks and windows as in the main shape."""
+    _case(orc, W, 1, Hq, Hkv, 9000, 300, 40, 70, 980 + W + Hq)
+
+
+@pytest.mark.parametrize("W", [1, 2, 8])
+def test_wide_long_chunks(orc, W):
+    """n > 131,072 takes chunks of 8,192 positions (two compaction tiles each); a sink window over several
+    chunks and a recent window that starts inside a chunk."""
+    _case(orc, W, 1, 4, 2, 140001, 4000, 20000, 300, 990 + W, scores=False)
+
+
+@pytest.mark.parametrize("W", [8, 16])
+def test_wide_distances_past_255(orc, W):
+    """Keys near the complement of the query: distances 32W - 3 .. 32W, so t >= 255 and the stored byte (the
+    distance clamped to 255) must be resolved from the codes."""
+    g = np.random.default_rng(995 + W)
+    n = 7000
+    qs = g.integers(0, 2 ** 32, (1, 2, W), dtype=np.uint64).astype(np.uint32)
+    ks = np.repeat(~qs[:, :1, None, :], n, axis=2)
+    for i in range(n):
+        for f in g.integers(0, 32 * W, i % 4):
+            ks[0, 0, i, f // 32] ^= np.uint32(1 << int(f % 32))
+    ks = np.ascontiguousarray(ks)
+    for m in (10, 3000, 6999):
+        print("case wide topk past 255 W=%d m=%d" % (W, m), flush=True)
+        kt = torch.from_numpy(ks.view(np.int32)).to(DEV)
+        qt = torch.from_numpy(qs.view(np.int32)).to(DEV)
+        idx, cnt, sc = ops.sig_score_topk_w(kt, qt, m, 5, 5, want_scores=True)
+        torch.cuda.synchronize()
+        ri, rc, rs = orc.sig_score_topk_w(ks, qs, m, 5, 5, want_scores=True)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+        np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+
+
+def test_wide_one_word_matches_32bit(orc):
+    """W = 1 through sig_score_topk_w and the one-word path sig_score_topk select the same positions."""
+    g = np.random.default_rng(999)
+    ks = g.integers(0, 2 ** 32, (2, 2, 20000), dtype=np.uint64).astype(np.uint32)
+    qs = g.integers(0, 2 ** 32, (2, 8), dtype=np.uint64).astype(np.uint32)
+    kt = torch.from_numpy(ks.view(np.int32)).to(DEV)
+    qt = torch.from_numpy(qs.view(np.int32)).to(DEV)
+    iw, cw, _ = ops.sig_score_topk_w(kt.unsqueeze(-1).contiguous(), qt.unsqueeze(-1).contiguous(), 625, 128, 128)
+    i1, c1, _ = ops.sig_score_topk(kt, qt, 625, 128, 128)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cw.cpu().numpy(), c1.cpu().numpy())
+    np.testing.assert_array_equal(iw.cpu().numpy(), i1.cpu().numpy())
+
+
+def test_wide_many_chunks(orc):
+    """n = 1,100,001: more than 32 chunks per head, so the select pass stages the chunks' histograms block by
+    block (all positions first, then each block again with its window parts)."""
+    _case(orc, 2, 1, 2, 1, 1100001, 30000, 40000, 5000, 1001, scores=False)
