@@ -795,7 +795,12 @@ def main():
         line.update({"value": w8["queries_per_s"], "steps": max(20, args.steps // 2), "ms_per_step": w8["us"] / 1e3})
         line["roofline"] = {"bound": "hbm", "achieved": w8["code_tbps"] * 1e3, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                             "frac": w8["code_tbps"] * 1e12 / HBM_PEAK, "traffic": None,
-                            "kernel": "k_topk_wide<8> (256-bit codes; achieved on the key-code bytes)"}
+                            "kernel": "sig_score_topk_w at 256 bits, the whole call (k_wide_hist + k_wide_select + "
+                                      "k_wide_compact); achieved on the key-code bytes"}
+        # HBM bytes per launch of the histogram pass (key codes read once per KV head, distance bytes written)
+        hist_alg = cfg.B * cfg.Hkv * cfg.n * 4 * 8 + cfg.B * cfg.Hq * cfg.n
+        line["hist_pass"] = {"algorithmic_bytes": hist_alg,
+                             "traffic": traffic_from_profile("wide_hist_sigwidth256", hist_alg, "wide")}
         line["config"] = {"workload": "sigwidth: sig_score_topk_w on " + cfg.name + ", random codes of 32-512 bits",
                           "launch": launch}
         line["step"] = "sig_score_topk_w at 256 bits (value); every width in detail"

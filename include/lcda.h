@@ -137,8 +137,11 @@ int sig_score_topk_q(const uint32_t* key_sigs, const void* q, int q_dtype, const
  * 16): the distance popcount(h_i XOR h_q) of sig_score_topk summed over the
  * words, from 0 to b; the same selection, windows, order and padding.  These
  * are the code widths of HashAttention's scoring-cost sweep (64 to 512 bits;
- * slide with Table 6).  One workgroup per query head: the plain form, in which
- * each of a group's G query heads reads its KV head's codes.
+ * slide with Table 6).  Three launches over chunks of each head: distances and
+ * per-chunk histograms (a KV head's codes read once for up to 8 of its query
+ * heads), the per-row threshold and chunk offsets, then ordered compaction.
+ * W = 1 without scores (and at most 8 query heads per KV head) runs
+ * sig_score_topk's kernel, which makes the same selection.
  *
  *   key_sigs  [B, Hkv, n, W] uint32 (word w of position i's code at i*W + w)
  *   q_sigs    [B, Hq, W]     uint32

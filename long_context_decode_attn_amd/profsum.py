@@ -30,6 +30,7 @@ KERNEL_SOURCES = {
     "split_rows": (_C + "split_rows.hip", _C + "mfma_tile.h", _C + "common.h", _C + "internal.h"),
     "split_valu": (_C + "split_valu.hip", _C + "common.h", _C + "internal.h"),
     "topk_unit": (_C + "sig_topk_unit.hip", _C + "sparse.h", _C + "sig_proj.h", _C + "common.h", _C + "internal.h"),
+    "wide": (_C + "sig_topk_wide.hip", _C + "wide.h", _C + "common.h", _C + "internal.h"),
 }
 
 
