@@ -9,10 +9,12 @@
 // m = alpha_in * log2(e), l = 1, acc = A_in: the "virtual logit/value pair"
 // of Eq. (3.4), which makes the same kernel the local-token merge.
 //
-// One workgroup of 256 threads per query row: the slot weights are computed
-// once into LDS (maxima and sums reduced in each wavefront, then across the
-// four through LDS), then 8 slot groups x 32 threads x 4 columns read the partial
-// vectors with independent 16-byte loads and are summed through LDS.
+// k_combine, for many slots: one workgroup of 256 threads per query row; the
+// slot weights are computed once into LDS (maxima and sums reduced in each
+// wavefront, then across the four through LDS), then 8 slot groups x 32
+// threads x 4 columns read the partial vectors with independent 16-byte loads
+// and are summed through LDS.  k_combine_small, for at most 64 slots: one
+// wavefront per row.
 
 #include "common.h"
 #include "internal.h"
@@ -133,10 +135,58 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
     }
 }
 
+// Rows of at most SM slots (1 <= slots <= SM): one wavefront per row, four
+// rows per workgroup.  Every load of a row is requested at once (the slot
+// states one per lane, the partial vectors of all slots, two columns per
+// lane), so the merge waits for one memory round trip; then the same
+// arithmetic as above, the slots summed in order.
+template <int SM>
+__global__ __launch_bounds__(kThreads) void k_combine_small(CombineArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (row >= a.rows) return;   // a whole wavefront; no barrier follows
+    const int S = a.slots;
+    const float2 x = a.ml[row * S + min(lane, S - 1)];   // lanes at or past S are ignored
+    const float* acc = a.acc + row * S * kD + 2 * lane;
+    f32x2 v[SM];
+#pragma unroll
+    for (int s = 0; s < SM; ++s) v[s] = *reinterpret_cast<const f32x2*>(acc + (int64_t)min(s, S - 1) * kD);
+    const float al_in = a.alpha_in != nullptr ? a.alpha_in[row] : -INFINITY;
+    const bool virt = al_in > -INFINITY;
+    const f32x2 a_in = virt ? *reinterpret_cast<const f32x2*>(a.a_in + row * kD + 2 * lane) : f32x2{0.f, 0.f};
+    const bool has = lane < S && x.y > 0.f;
+    if (!__any(has) && !virt) {
+        *reinterpret_cast<f32x2*>(a.out + row * kD + 2 * lane) = f32x2{0.f, 0.f};
+        if (a.alpha && lane == 0) a.alpha[row] = -INFINITY;
+        return;
+    }
+    const float mv = virt ? al_in * kLog2e : kNoMax;
+    const float M = fmaxf(wave_max(has ? x.x : kNoMax), mv);
+    const float w = has ? fast_exp2(x.x - M) : 0.f;
+    f32x2 o = {0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+        if (s < S) o += __shfl(w, s, 64) * v[s];   // s < S is the same in every lane
+    const float wv = virt ? fast_exp2(mv - M) : 0.f;
+    const float L = wave_sum(w * x.y) + wv;
+    if (virt) o += wv * a_in;
+    *reinterpret_cast<f32x2*>(a.out + row * kD + 2 * lane) = o * (1.f / L);
+    if (a.alpha && lane == 0) a.alpha[row] = (M + log2f(L)) * kLn2;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.slots >= 1 && a.slots <= 64) {   // few slots per row: a wavefront per row
+        const dim3 grid((unsigned)((a.rows + kThreads / 64 - 1) / (kThreads / 64)));
+        if (a.slots <= 4) hipLaunchKernelGGL(k_combine_small<4>, grid, dim3(kThreads), 0, st, a);
+        else if (a.slots <= 8) hipLaunchKernelGGL(k_combine_small<8>, grid, dim3(kThreads), 0, st, a);
+        else if (a.slots <= 16) hipLaunchKernelGGL(k_combine_small<16>, grid, dim3(kThreads), 0, st, a);
+        else if (a.slots <= 32) hipLaunchKernelGGL(k_combine_small<32>, grid, dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL(k_combine_small<64>, grid, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_combine, dim3(a.rows), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
