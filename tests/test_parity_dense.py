@@ -325,3 +325,20 @@ def test_dense_split_variants(orc, variant, wgs):
     finally:
         ops.set_tuning("dense_variant", old)
         ops.set_tuning("dense_wgs", old_w)
+
+
+# -------------------------------------------------------- combine slots ----
+@pytest.mark.parametrize("wgs,n", [(2, 20800), (4, 20800), (5, 20800), (8, 20800), (9, 20800), (16, 20800),
+                                   (17, 20800), (32, 20800), (33, 20800), (64, 20480), (65, 20800), (200, 20800)])
+def test_combine_slot_counts(orc, wgs, n):
+    """fp32 split over one KV head with valu_wgs target workgroups: 2, 4, 5, 8, 9, 16, 17, 32, 33, 64, 65 and 186
+    slots per row (16-token blocks, 1,300 or 1,280 of them), on both sides of each slot bound of the
+    one-wavefront-per-row combine and of the switch to a workgroup per row past 64 slots; cached_attn_lse, and the
+    fused step whose merge with local tokens enters as the virtual pair."""
+    old = ops.get_tuning("valu_wgs")
+    ops.set_tuning("valu_wgs", wgs)
+    try:
+        _dense_case(1, 4, 1, n, torch.float32, 1500 + wgs, orc=orc)
+        _step_case(orc, 1, 4, 1, n, 100, [100], torch.float32, 1600 + wgs)
+    finally:
+        ops.set_tuning("valu_wgs", old)
