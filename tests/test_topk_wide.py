@@ -111,3 +111,11 @@ def test_wide_many_chunks(orc):
     """n = 1,100,001: more than 32 chunks per head, so the select pass stages the chunks' histograms block by
     block (all positions first, then each block again with its window parts)."""
     _case(orc, 2, 1, 2, 1, 1100001, 30000, 40000, 5000, 1001, scores=False)
+
+
+@pytest.mark.parametrize("W", [8, 16])
+def test_wide_bench_shape_every_row(orc, W):
+    """The shape the code-width sweep times (B = 8, Hkv = 8, Hq = 32, n = 131,072, m = n/32, 128 + 128 window
+    positions; random codes): every row's indices and count, bit-exact."""
+    n = 131072
+    _case(orc, W, 8, 32, 8, n, n // 32, 128, 128, 1100 + W, scores=False)
