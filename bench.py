@@ -207,7 +207,7 @@ def bench_dense(args, cfg, layers=1):
                                 traffic_from_profile("split_rows_shared36", layer_bytes, "split_rows"),
                      "kernel": ("k_split_mfma (dense_decode_step: cache + local tokens, LSE combine in-kernel; "
                                 "one launch per layer)") if fused else
-                               ("k_split_rows_pair + k_combine per layer (dense_decode_step on a shared document: "
+                               ("k_split_rows_pair + k_combine_small per layer (dense_decode_step on a shared document: "
                                 "64-row document pass that also takes each row's local tokens, then the combine; "
                                 "avg_launch_us is the per-layer time of the pair)"),
                      "bytes_per_launch": layer_bytes, "avg_launch_us": launch_us},
@@ -811,7 +811,7 @@ def main():
         line.update({"value": res["value"], "steps": res["steps"], "ms_per_step": res["ms_per_step"]})
         line["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_BF16_PEAK / 1e12,
                             "unit": "TFLOP/s", "frac": res["tflops"] * 1e12 / MFMA_BF16_PEAK, "traffic": None,
-                            "kernel": "k_split_rows_pair (64-row MFMA pass over the shared module) + k_combine"}
+                            "kernel": "k_split_rows_pair (64-row MFMA pass over the shared module) + k_combine_small"}
         line["config"] = {"workload": "quadrature: " + cfg.name, "launch": launch}
         line["step"] = "cached_attn_lse of 256 queries against p = 6,144 shared (W, Z) pairs per KV head"
         line["detail"] = res
@@ -824,7 +824,8 @@ def main():
         ach = res["gather_tbps"] * 1e12
         line["roofline"] = {"bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                             "frac": ach / HBM_PEAK, "traffic": None,
-                            "kernel": "gather_attn (k_split_valu gather + k_combine; achieved on unique rows)"}
+                            "kernel": "gather_attn (k_split_valu gather + the combine where a row is split; achieved on "
+                                      "unique rows)"}
         line["config"] = {"workload": "needles512k: " + cfg.name, "launch": launch}
         line["step"] = "sig_score_topk + gather_attn (value); cached_attn_lse on the same inputs (dense_*)"
         line["detail"] = res
