@@ -86,6 +86,43 @@ def test_topk_unit_exchange_fallback(orc):
         ops.set_tuning("topk_spin", old)
 
 
+def test_topk_unit_skewed_parts(orc):
+    """Workgroups of one (b, KV head) whose own steps would put t far apart: every fourth step of 4,096 positions
+    holds near copies of the first query head's code (0 to 2 bits off), the others random codes, so the steps held
+    by some workgroups take all of the top m and the others none (their own histograms alone would give t ~10).
+    The other heads see random codes everywhere.  Indices bit-exact, also with a zero wait (every workgroup that
+    does not arrive last counts its partners' parts itself)."""
+    B, Hq, Hkv, n, m = 2, 8, 2, 131072, 4096
+    G = Hq // Hkv
+    g = np.random.default_rng(777)
+    ks = g.integers(0, 2 ** 32, (B, Hkv, n), dtype=np.uint64).astype(np.uint32)
+    qs = g.integers(0, 2 ** 32, (B, Hq), dtype=np.uint64).astype(np.uint32)
+    for b in range(B):
+        for h in range(Hkv):
+            for s in range(0, n // 4096, 4):
+                pos = np.arange(s * 4096, (s + 1) * 4096)
+                flips = np.zeros(len(pos), np.uint32)
+                for k in range(2):
+                    bit = g.integers(0, 32, len(pos)).astype(np.uint32)
+                    on = g.integers(0, 2, len(pos)).astype(bool)
+                    flips ^= np.where(on, np.left_shift(np.uint32(1), bit), np.uint32(0)).astype(np.uint32)
+                ks[b, h, pos] = qs[b, h * G] ^ flips
+    kt = torch.from_numpy(ks.view(np.int32).copy()).to(DEV)
+    qt = torch.from_numpy(qs.view(np.int32).copy()).to(DEV)
+    ri, rc, _ = orc.sig_score_topk(ks, qs, m, 128, 128)
+    old = ops.get_tuning("topk_spin")
+    try:
+        for spin in (old, 0):
+            ops.set_tuning("topk_spin", spin)
+            print("case topk skewed parts spin=%d" % spin, flush=True)
+            idx, cnt, _ = ops.sig_score_topk(kt, qt, m, 128, 128)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+            np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    finally:
+        ops.set_tuning("topk_spin", old)
+
+
 @pytest.mark.parametrize("n,m,s,r", [(300001, 5000, 5000, 3000), (270000, 4096, 128, 128), (524288, 8192, 128, 128),
                                      (524288, 100, 9000, 70000)])
 def test_topk_long(orc, n, m, s, r):
