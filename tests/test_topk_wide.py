@@ -119,3 +119,16 @@ def test_wide_bench_shape_every_row(orc, W):
     positions; random codes): every row's indices and count, bit-exact."""
     n = 131072
     _case(orc, W, 8, 32, 8, n, n // 32, 128, 128, 1100 + W, scores=False)
+
+
+@pytest.mark.parametrize("chunk", [4096, 32768])
+def test_wide_chunk_knob(orc, chunk):
+    """The chunk length knob at both ends of its range: 25 chunks of 4,096 positions or 4 of 32,768 (one
+    workspace serves both), windows over several chunks, ragged last chunk; 1, 4 and 16 words."""
+    old = ops.get_tuning("wide_chunk")
+    ops.set_tuning("wide_chunk", chunk)
+    try:
+        for W in (1, 4, 16):
+            _case(orc, W, 2, 8, 2, 100003, 3000, 9000, 5000, 1200 + W, scores=(W == 1))
+    finally:
+        ops.set_tuning("wide_chunk", old)
