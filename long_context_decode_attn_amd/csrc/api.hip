@@ -955,6 +955,7 @@ int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group,
     e.bits = bits;
     e.codes = codes;
     e.codes_group_stride = codes_group_stride;
+    e.cus = device_cus();
     return hip_status(fn, launch_sig_encode(e, static_cast<hipStream_t>(stream)));
 }
 

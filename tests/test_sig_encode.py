@@ -111,3 +111,73 @@ def test_config4_reduced_from_queries(orc):
     np.testing.assert_array_equal(sig_np(qs), rqs)
     ri, rc, _ = orc.sig_score_topk(sig_np(x["key_sigs"]), rqs, m, 128, 128)
     np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+
+
+# Many rows (16,384 and more) take the blocked path: persistent workgroups, a lane owning 8 rows x 8 bits.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,bits", [(16384, 32), (16805, 32), (40000, 13), (70001, 32), (20000, 1)])
+def test_encode_many_rows(orc, dtype, rows, bits):
+    g = torch.Generator().manual_seed(700 + rows + bits)
+    x = torch.randn((rows, 128), generator=g).to(dtype)
+    R = _proj(bits, 701 + bits)
+    print("case encode many rows=%d bits=%d %s" % (rows, bits, dtype), flush=True)
+    got = ops.sig_encode(x.to(DEV), R.to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sig_np(got), orc.sig_encode(to_np(x), R.numpy()))
+
+
+def test_encode_many_near_zero_projections(orc):
+    """The blocked path on rows built so that every projection of a row lands within rounding of zero, plus
+    all-zero rows: the sign of each chain's sum decides, bit for bit."""
+    rows = 20000
+    rng = np.random.default_rng(710)
+    R = _proj(32, 711)
+    v = rng.standard_normal((rows, 128))
+    Rd = R.double().numpy()
+    b = np.arange(rows) % 32
+    rb = Rd[:, b].T                                   # the column each row is made orthogonal to
+    v -= ((v * rb).sum(1) / (rb * rb).sum(1))[:, None] * rb
+    x = torch.from_numpy(v.astype(np.float32))
+    x[::97] = 0.0
+    print("case encode many near-zero projections", flush=True)
+    got = ops.sig_encode(x.to(DEV), R.to(DEV))
+    torch.cuda.synchronize()
+    want = orc.sig_encode(x.numpy(), R.numpy())
+    np.testing.assert_array_equal(sig_np(got), want)
+    assert np.all(sig_np(got)[::97] == 0)
+
+
+def test_encode_many_into_cache_layout(orc):
+    """24,000 new keys of a [B, Hkv, n_cap, 128] cache (1,500 per head, so wavefront row blocks straddle heads)
+    encoded into the matching positions of a [B, Hkv, n] code array; every other code is untouched."""
+    B, Hkv, n_cap, n, n_old, r = 2, 8, 3000, 2800, 1100, 1500
+    g = torch.Generator().manual_seed(720)
+    K = torch.randn((B, Hkv, n_cap, 128), generator=g).to(torch.bfloat16).to(DEV)
+    R = _proj(32, 721).to(DEV)
+    codes = torch.full((B, Hkv, n), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    print("case encode many into cache layout", flush=True)
+    ops.sig_encode(K[:, :, n_old:n_old + r], R, codes=codes[:, :, n_old:n_old + r])
+    torch.cuda.synchronize()
+    c = sig_np(codes)
+    want = orc.sig_encode(to_np(K[:, :, n_old:n_old + r].contiguous()), R.cpu().numpy())
+    np.testing.assert_array_equal(c[:, :, n_old:n_old + r], want)
+    assert np.all(c[:, :, :n_old] == 0x5A5A5A5A) and np.all(c[:, :, n_old + r:] == 0x5A5A5A5A)
+
+
+def test_encode_whole_cache_sampled(orc):
+    """A whole cache of 8 x 8 heads x 131,072 positions (8.4 M rows, bf16), the timed whole-cache encode's
+    shape; 8,192 sampled rows and the last row against the oracle."""
+    B, Hkv, n = 8, 8, 131072
+    gen = torch.Generator(device=DEV).manual_seed(730)
+    K = torch.randn((B, Hkv, n, 128), generator=gen, device=DEV, dtype=torch.bfloat16)
+    R = _proj(32, 731).to(DEV)
+    print("case encode whole cache %dx%dx%d" % (B, Hkv, n), flush=True)
+    codes = ops.sig_encode(K, R)
+    torch.cuda.synchronize()
+    rows = B * Hkv * n
+    pick = np.random.default_rng(732).choice(rows, 8192, replace=False)
+    pick = np.append(pick, rows - 1)
+    pt = torch.from_numpy(pick).to(DEV)
+    want = orc.sig_encode(to_np(K.reshape(rows, 128)[pt]), R.cpu().numpy())
+    np.testing.assert_array_equal(sig_np(codes.reshape(rows)[pt]), want)
+    del K
