@@ -147,15 +147,20 @@ def test_encode_many_near_zero_projections(orc):
     assert np.all(sig_np(got)[::97] == 0)
 
 
-def test_encode_many_into_cache_layout(orc):
-    """24,000 new keys of a [B, Hkv, n_cap, 128] cache (1,500 per head, so wavefront row blocks straddle heads)
-    encoded into the matching positions of a [B, Hkv, n] code array; every other code is untouched."""
-    B, Hkv, n_cap, n, n_old, r = 2, 8, 3000, 2800, 1100, 1500
-    g = torch.Generator().manual_seed(720)
-    K = torch.randn((B, Hkv, n_cap, 128), generator=g).to(torch.bfloat16).to(DEV)
+@pytest.mark.parametrize("B,Hkv,n_cap,n,n_old,r,dtype", [
+    (2, 8, 3000, 2800, 1100, 1500, torch.bfloat16),   # 1,500 rows per head: a 256-row turn straddles heads
+    (8, 64, 300, 260, 200, 37, torch.bfloat16),       # 37 rows per head: a turn spans seven or eight heads
+    (4, 8, 1200, 1100, 500, 600, torch.float32),
+])
+def test_encode_many_into_cache_layout(orc, B, Hkv, n_cap, n, n_old, r, dtype):
+    """16,384 or more new keys of a [B, Hkv, n_cap, 128] cache encoded into the matching positions of a
+    [B, Hkv, n] code array; every other code is untouched."""
+    g = torch.Generator().manual_seed(720 + r)
+    K = torch.randn((B, Hkv, n_cap, 128), generator=g).to(dtype).to(DEV)
     R = _proj(32, 721).to(DEV)
     codes = torch.full((B, Hkv, n), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
-    print("case encode many into cache layout", flush=True)
+    assert B * Hkv * r >= 16384
+    print("case encode many into cache layout B=%d Hkv=%d r=%d %s" % (B, Hkv, r, dtype), flush=True)
     ops.sig_encode(K[:, :, n_old:n_old + r], R, codes=codes[:, :, n_old:n_old + r])
     torch.cuda.synchronize()
     c = sig_np(codes)
