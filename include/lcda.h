@@ -162,8 +162,10 @@ int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, in
  * merely hashing"; the learned map needs trained weights).  Each projection is
  * a chain of fp64 fused multiply-adds over the 128 values in order, from 0:
  * codes are exact and reproducible, including the sign of a projection near
- * zero.  One call encodes queries (groups = 1, rows_per_group = B*Hq) or
- * appends new keys' codes (groups = B*Hkv, one group per cached head).
+ * zero.  One call encodes queries (groups = 1, rows_per_group = B*Hq),
+ * appends new keys' codes (groups = B*Hkv, one group per cached head), or
+ * encodes a whole cache; from 16,384 rows a blocked kernel takes over (same
+ * chains, same codes).
  *
  *   x      row (g, i), g < groups, i < rows_per_group, at
  *          x + g*x_group_stride + i*128 elements, dtype (fp32 or bf16);
