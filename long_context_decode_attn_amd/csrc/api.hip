@@ -10,6 +10,7 @@
 
 #include "../../include/lcda.h"
 #include "common.h"
+#include "device.h"
 #include "internal.h"
 #include "sparse.h"
 #include "wide.h"
@@ -197,19 +198,6 @@ void set_unit_ws(TopkArgs& a, char* w, const TopkLayout& l) {
     a.rbar = reinterpret_cast<unsigned long long*>(w + l.rbar_off);
     a.repoch = reinterpret_cast<uint32_t*>(w + l.repoch_off);
     a.srec = reinterpret_cast<uint32_t*>(w + l.srec_off);
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] == 0) {
-        int c = 0;
-        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev] = c;
-    }
-    return cache[dev];
 }
 
 }  // namespace
@@ -955,7 +943,6 @@ int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group,
     e.bits = bits;
     e.codes = codes;
     e.codes_group_stride = codes_group_stride;
-    e.cus = device_cus();
     return hip_status(fn, launch_sig_encode(e, static_cast<hipStream_t>(stream)));
 }
 

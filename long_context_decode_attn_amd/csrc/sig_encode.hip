@@ -31,6 +31,7 @@
 // into the turn's codes in LDS.
 
 #include "common.h"
+#include "device.h"
 #include "internal.h"
 #include "sparse.h"
 #include "sig_proj.h"
@@ -175,7 +176,7 @@ int many_slots_per_cu() {
 template <typename T>
 hipError_t launch_many(const EncodeArgs& a, int64_t rows, hipStream_t st) {
     const int64_t turns = (rows + kManyRows - 1) / kManyRows;
-    const int64_t slots = (int64_t)std::max(1, many_slots_per_cu<T>()) * std::max(1, a.cus);
+    const int64_t slots = (int64_t)std::max(1, many_slots_per_cu<T>()) * std::max(1, device_cus());
     const dim3 grid((unsigned)std::min(turns, slots)), block(256);
     hipLaunchKernelGGL(k_sig_encode_many<T>, grid, block, 0, st, a);
     return hipGetLastError();

@@ -16,7 +16,6 @@ struct EncodeArgs {
     int bits;                  // 1 .. 32
     uint32_t* codes;           // row (g, i) at codes[g * codes_group_stride + i]
     int64_t codes_group_stride;
-    int cus;                   // compute units of the device (sizes the many-rows grid; 0: one)
 };
 hipError_t launch_sig_encode(const EncodeArgs& a, hipStream_t st);
 
