@@ -38,6 +38,7 @@ from long_context_decode_attn_amd import ops, synth, traffic  # noqa: E402
 from long_context_decode_attn_amd.profsum import kernel_source_digest  # noqa: E402
 
 HBM_PEAK = 8.0e12   # B/s, MI355X published peak
+FP64_PEAK = 78.6e12  # FLOP/s, MI355X published fp64 vector peak
 MFMA_BF16_PEAK = 2.5e15   # FLOP/s, MI355X published dense bf16 matrix peak
 METRIC = "decode-attention queries/sec + achieved HBM TB/s (KV+sig bytes) vs ~8 TB/s peak"
 
@@ -379,7 +380,8 @@ def bench_tmap(args, sets, cfg):
             "sig_score_topk_q_us": us([s.topk_q for s in sets]),
             "encode_whole_cache_us": t_cache,
             "encode_whole_cache_rows_per_s": rows / (t_cache * 1e-6),
-            "encode_whole_cache_fp64_tflops": rows * 32 * 128 * 2 / (t_cache * 1e-6) / 1e12}
+            "encode_whole_cache_fp64_tflops": rows * 32 * 128 * 2 / (t_cache * 1e-6) / 1e12,
+            "encode_whole_cache_frac_of_fp64_peak": rows * 32 * 128 * 2 / (t_cache * 1e-6) / FP64_PEAK}
 
 
 def bench_sparse(args, cfg, rot=None):
