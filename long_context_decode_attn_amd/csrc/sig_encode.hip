@@ -24,11 +24,11 @@
 // row, so its projection values are the same for all its lanes (broadcast LDS
 // reads); lane l owns rows 4l .. 4l + 3, 32 independent chains, each still in
 // order from 0.  The rows come through LDS in 64-byte chunks stored
-// [dword][row]: the global reads take whole 64-byte pieces of each row (scattered
-// 8-byte reads, one row per lane, made the L2 deliver a line per 8 bytes used),
-// and a lane then reads its four rows' dword with one 16-byte LDS read.  The
-// next chunk loads while this one is computed.  The four waves OR their bytes
-// into the turn's codes in LDS.
+// [dword][row]: the global reads take whole 64-byte pieces of each row (a lane
+// reading its own rows a few bytes at a time would make the L2 deliver a cache
+// line per few bytes used), and a lane then reads its four rows' dword with one
+// 16-byte LDS read.  The next chunk loads while this one is computed.  The four
+// waves OR their bytes into the turn's codes in LDS.
 
 #include "common.h"
 #include "device.h"
