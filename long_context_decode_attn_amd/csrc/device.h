@@ -3,19 +3,22 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 namespace lcda {
 
-// Compute units of the current device (cached per device; 0 if the query fails).
+// Compute units of the current device (cached per device, safe to call from
+// several host threads; 0 if the query fails).
 inline int device_cus() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] == 0) {
-        int c = 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev] = c;
+        cache[dev].store(c, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return c;
 }
 
 }  // namespace lcda

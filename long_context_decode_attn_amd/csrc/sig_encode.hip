@@ -30,6 +30,8 @@
 // 16-byte LDS read.  The next chunk loads while this one is computed.  The four
 // waves OR their bytes into the turn's codes in LDS.
 
+#include <atomic>
+
 #include "common.h"
 #include "device.h"
 #include "internal.h"
@@ -160,17 +162,17 @@ __global__ __launch_bounds__(256, 2) void k_sig_encode_many(EncodeArgs a) {
     }
 }
 
-// Workgroups of the many-rows kernel one CU holds at once.
+// Workgroups of the many-rows kernel one CU holds at once (cached; safe to
+// call from several host threads).
 template <typename T>
 int many_slots_per_cu() {
-    static int slots = -1;
-    if (slots < 0) {
-        int s = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&s, k_sig_encode_many<T>, 256, 0) != hipSuccess)
-            s = 0;
-        slots = s;
+    static std::atomic<int> slots{-1};
+    int s = slots.load(std::memory_order_relaxed);
+    if (s < 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&s, k_sig_encode_many<T>, 256, 0) != hipSuccess) s = 0;
+        slots.store(s, std::memory_order_relaxed);
     }
-    return slots;
+    return s;
 }
 
 template <typename T>
