@@ -284,6 +284,7 @@ SplitPlan plan_split_t(const Tuning& t, int dtype, bool gather, int B, int Hq, i
     // units to fill the chip that way.
     if (nblocks <= t.direct_blocks && units >= target) splits = 1;
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+    splits = std::min<int64_t>(splits, kCtrMaxTarget);   // an arrival counter counts at most this many
     const int64_t bps = nblocks > 0 ? ceil_div(nblocks, splits) : 1;
     splits = nblocks > 0 ? ceil_div(nblocks, bps) : 1;
     p.splits = (int)splits;

@@ -154,17 +154,25 @@ __device__ __forceinline__ f32x2 load_dev2(const float* p) {   // two adjacent f
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Tag of the arrival counter at address c: a hash of the address, so that a
-// counter word is recognised as one this library left (tag, 0) and anything
-// else (a fresh workspace, other data) is not.
-__device__ __forceinline__ uint32_t ctr_tag(const unsigned long long* c) {
-    uint32_t x = (uint32_t)((uintptr_t)c >> 3) ^ 0x6C8E9CF5u;   // MurmurHash3's 32-bit finalizer
-    x ^= x >> 16;
-    x *= 0x85EBCA6Bu;
-    x ^= x >> 13;
-    x *= 0xC2B2AE35u;
-    x ^= x >> 16;
-    return x;
+// Arrival counter words hold a 52-bit tag above a 12-bit count of arrivals
+// (targets up to 4,095; the launchers never exceed 2,048).
+constexpr int kCtrCountBits = 12;
+constexpr unsigned long long kCtrCountMask = (1ull << kCtrCountBits) - 1ull;
+constexpr int kCtrMaxTarget = (int)kCtrCountMask;
+
+// Tag of the arrival counter at address c, in the word's upper 52 bits: a hash
+// of the address (the SplitMix64 finalizer), so that a counter word is
+// recognised as one this library left (tag, 0) and anything else (a fresh
+// workspace, other data) is not.  Bytes that were never a counter hold a given
+// tag with probability 2^-52.
+__device__ __forceinline__ unsigned long long ctr_tag(const unsigned long long* c) {
+    unsigned long long x = (unsigned long long)(uintptr_t)c;
+    x ^= x >> 30;
+    x *= 0xBF58476D1CE4E5B9ull;
+    x ^= x >> 27;
+    x *= 0x94D049BB133111EBull;
+    x ^= x >> 31;
+    return x & ~kCtrCountMask;
 }
 
 // One arrival at counter c, made by one thread once the workgroup's published
@@ -175,18 +183,17 @@ __device__ __forceinline__ uint32_t ctr_tag(const unsigned long long* c) {
 // so, and the others then count on the valid word (the exchange loop ends once
 // any of them has installed it).
 __device__ __forceinline__ uint32_t arrive_one(unsigned long long* c, uint32_t target) {
-    const uint32_t tag = ctr_tag(c);
-    const unsigned long long valid0 = (unsigned long long)tag << 32;
+    const unsigned long long valid0 = ctr_tag(c);
     unsigned long long old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t count;
-    if ((uint32_t)(old >> 32) == tag) {
-        count = (uint32_t)old + 1u;
+    if ((old & ~kCtrCountMask) == valid0) {
+        count = (uint32_t)(old & kCtrCountMask) + 1u;
     } else {
         unsigned long long cur = old + 1ull;
         while (true) {
-            if ((uint32_t)(cur >> 32) == tag) {
+            if ((cur & ~kCtrCountMask) == valid0) {
                 old = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                count = (uint32_t)old + 1u;
+                count = (uint32_t)(old & kCtrCountMask) + 1u;
                 break;
             }
             if (__hip_atomic_compare_exchange_strong(c, &cur, valid0 | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -202,9 +209,9 @@ __device__ __forceinline__ uint32_t arrive_one(unsigned long long* c, uint32_t t
 
 // Arrival of one workgroup at counter c, after every thread wrote what it
 // publishes with device-scope stores: returns true, in every thread, in the
-// last of `target` workgroups to arrive.  The counter holds
-// (tag << 32 | arrivals); between calls it is (tag, 0), which the last arrival
-// restores (see arrive_one).
+// last of `target` workgroups to arrive.  The counter holds (tag, arrivals);
+// between calls it is (tag, 0), which the last arrival restores (see
+// arrive_one).
 __device__ __forceinline__ bool arrive_count(unsigned long long* c, uint32_t target, int* s_flag) {
     wait_vm_all();    // this thread's device-scope stores are acknowledged
     __syncthreads();  // ... in every thread of the workgroup

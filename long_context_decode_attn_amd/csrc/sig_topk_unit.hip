@@ -59,7 +59,7 @@
 //   6. the last workgroup of the unit to publish its partial states merges the
 //      parts exactly through their maxima (the split identity of the dense path).
 // The workspace holds the counters, epochs, histograms and step records; the
-// counter words are (tag << 32 | arrivals) as for the split pass (see
+// counter words are (tag, arrivals) as for the split pass (see
 // arrive_one), so no call needs them cleared, and every call leaves them at
 // (tag, 0).
 
