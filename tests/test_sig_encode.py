@@ -151,6 +151,7 @@ def test_encode_many_near_zero_projections(orc):
     (2, 8, 3000, 2800, 1100, 1500, torch.bfloat16),   # 1,500 rows per head: a 256-row turn straddles heads
     (8, 64, 300, 260, 200, 37, torch.bfloat16),       # 37 rows per head: a turn spans seven or eight heads
     (4, 8, 1200, 1100, 500, 600, torch.float32),
+    (64, 256, 3, 2, 1, 1, torch.bfloat16),            # one new key in each of 16,384 heads
 ])
 def test_encode_many_into_cache_layout(orc, B, Hkv, n_cap, n, n_old, r, dtype):
     """16,384 or more new keys of a [B, Hkv, n_cap, 128] cache encoded into the matching positions of a
