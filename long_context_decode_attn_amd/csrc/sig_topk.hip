@@ -121,11 +121,11 @@ struct __align__(16) HistSmem {
 // has been counted, so that a group's loads are in flight at once.
 constexpr int kGrp = 4;
 
-template <bool VEC>
-__device__ __forceinline__ void load_group(uint32_t (&xr)[kGrp][16], const uint32_t* ks, int64_t gb, int64_t end,
+template <bool VEC, int NG>
+__device__ __forceinline__ void load_group(uint32_t (&xr)[NG][16], const uint32_t* ks, int64_t gb, int64_t end,
                                            int tid) {
 #pragma unroll
-    for (int u = 0; u < kGrp; ++u)
+    for (int u = 0; u < NG; ++u)
         if (gb + (int64_t)u * kSub < end) load_sub<VEC>(xr[u], ks, gb + (int64_t)u * kSub, end, tid);
 }
 
@@ -133,19 +133,19 @@ __device__ __forceinline__ void load_group(uint32_t (&xr)[kGrp][16], const uint3
 // into counters that all lanes share: positions below s_cut (the sink part;
 // s_cut = beg when the chunk is not cut there) and from r_cut (the recent part;
 // r_cut = end when not cut).  Only the sub-chunks that meet a part do this.
-template <int MAXG, bool VEC, bool FULL, bool SCORES>
+template <int MAXG, bool VEC, bool FULL, bool SCORES, int NG>
 __device__ __forceinline__ void hist_chunk(const TopkArgs& a, uint32_t* my, uint32_t* part, const uint32_t* ks,
-                                           const uint32_t (&qs)[MAXG], uint32_t (&xr)[kGrp][16], int64_t beg,
+                                           const uint32_t (&qs)[MAXG], uint32_t (&xr)[NG][16], int64_t beg,
                                            int64_t end, int64_t s_cut, int64_t r_cut, int tid, int64_t row0) {
-    for (int64_t gb = beg; gb < end; gb += (int64_t)kGrp * kSub) {
+    for (int64_t gb = beg; gb < end; gb += (int64_t)NG * kSub) {
 #pragma unroll
-        for (int u = 0; u < kGrp; ++u) {
+        for (int u = 0; u < NG; ++u) {
             const int64_t sb = gb + (int64_t)u * kSub;
             if (sb < end) {   // uniform
                 uint32_t x[16];
 #pragma unroll
                 for (int k = 0; k < 16; ++k) x[k] = xr[u][k];
-                const int64_t nb = sb + (int64_t)kGrp * kSub;
+                const int64_t nb = sb + (int64_t)NG * kSub;
                 if (nb < end) load_sub<VEC>(xr[u], ks, nb, end, tid);
                 const int rem = FULL ? kSub : (int)min(end - sb, (int64_t)kSub);
                 if (sb < s_cut || min(sb + (int64_t)kSub, end) > r_cut) {   // uniform
@@ -226,7 +226,10 @@ __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
     const int64_t end = min(a.n, beg + a.chunk_len);
     const int64_t row0 = (int64_t)b * a.Hq + h * G;
 
-    uint32_t xr[kGrp][16];
+    // With the score stores and four heads, a ring of four sub-chunks went to scratch memory; two stay in
+    // registers (the compiler keeps the ring of four in registers for eight heads).
+    constexpr int NG = (SCORES && MAXG == 4) ? 2 : kGrp;
+    uint32_t xr[NG][16];
     load_group<VEC>(xr, ks, beg, end, tid);
     uint32_t qs[MAXG];
     __shared__ uint32_t s_qc[8];
@@ -252,9 +255,9 @@ __global__ __launch_bounds__(256) void k_topk_hist(TopkArgs a) {
     const int64_t r_cut = (beg < r_beg && r_beg < end) ? r_beg : end;
     uint32_t* my = sm.cnt + lane;
     if (end - beg == a.chunk_len)
-        hist_chunk<MAXG, VEC, true, SCORES>(a, my, sm.part, ks, qs, xr, beg, end, s_cut, r_cut, tid, row0);
+        hist_chunk<MAXG, VEC, true, SCORES, NG>(a, my, sm.part, ks, qs, xr, beg, end, s_cut, r_cut, tid, row0);
     else
-        hist_chunk<MAXG, VEC, false, SCORES>(a, my, sm.part, ks, qs, xr, beg, end, s_cut, r_cut, tid, row0);
+        hist_chunk<MAXG, VEC, false, SCORES, NG>(a, my, sm.part, ks, qs, xr, beg, end, s_cut, r_cut, tid, row0);
     __syncthreads();
     store_rows(sm, a, row0, c, tid);
 
