@@ -308,7 +308,14 @@ hipError_t launch_t(const SplitPlan& p, const SplitArgs& a, hipStream_t st) {
         const dim3 gblock(64 * p.waves);
         // 16 wavefronts (1,024 threads) leave 128 VGPRs a lane: rows one step ahead instead of two fit them.
         if (p.waves == 16) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true, 16, 1>), grid, gblock, 0, st, a);
-        else if (p.waves == 8) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true, 8>), grid, gblock, 0, st, a);
+        else if (p.waves == 8) {
+            // fp32 rows take twice the registers: at 8 wavefronts (256 VGPRs a lane) rows two steps ahead
+            // spilled one VGPR, so they go one step ahead.
+            if constexpr (sizeof(T) == 4)
+                hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true, 8, 1>), grid, gblock, 0, st, a);
+            else
+                hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true, 8>), grid, gblock, 0, st, a);
+        }
         else if (tuning().gather_variant == 1) hipLaunchKernelGGL((k_split_valu<T, 1, U, true, false>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_split_valu<T, 1, U, true, true>), grid, block, 0, st, a);
     } else {
