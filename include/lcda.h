@@ -173,7 +173,8 @@ int sig_score_topk_w(const uint32_t* key_sigs, const uint32_t* q_sigs, int W, in
  *   R      [128, bits] fp32, 1 <= bits <= 32 (code bits at or past bits are 0)
  *   codes  row (g, i)'s code at codes[g*codes_group_stride + i] (uint32,
  *          4-byte aligned: e.g. key_sigs + n_old with codes_group_stride = n)
- * With groups > 1 the strides must not make rows overlap.  No workspace.
+ * With groups > 1 the strides must not make rows overlap.  At most INT32_MAX
+ * rows in all (LCDA_EUNSUPPORTED beyond).  No workspace.
  */
 int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group, int64_t x_group_stride,
                const float* R, int bits, uint32_t* codes, int64_t codes_group_stride, void* stream);

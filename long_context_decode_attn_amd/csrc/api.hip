@@ -921,6 +921,9 @@ int sig_encode(const void* x, int dtype, int64_t groups, int64_t rows_per_group,
                     (long long)rows_per_group);
     if (bits < 1 || bits > 32) return fail(LCDA_EINVAL, "%s: bits = %d outside 1 .. 32", fn, bits);
     const bool work = groups > 0 && rows_per_group > 0;
+    if (work && rows_per_group > INT32_MAX / groups)   // rows above INT32_MAX: beyond any grid here
+        return fail(LCDA_EUNSUPPORTED, "%s: groups * rows_per_group = %lld * %lld exceeds INT32_MAX rows", fn,
+                    (long long)groups, (long long)rows_per_group);
     if (work && groups > 1 && (x_group_stride < rows_per_group * kD || codes_group_stride < rows_per_group))
         return fail(LCDA_EINVAL, "%s: group strides overlap the rows (x %lld < %lld or codes %lld < %lld)", fn,
                     (long long)x_group_stride, (long long)(rows_per_group * kD), (long long)codes_group_stride,

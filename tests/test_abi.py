@@ -119,6 +119,8 @@ def test_sig_encode_rejects(lib):
     assert call(xs=4 * 128 + 4) == 1 and b"multiple of 8" in lib.lcda_last_error()
     assert call(codes=ctypes.c_void_p(0x10002)) == 1 and b"4-byte" in lib.lcda_last_error()
     assert call(x=None) == 1
+    assert call(groups=1 << 20, rpg=1 << 12, xs=(1 << 12) * 128, cs=1 << 12) == 2   # 2^32 rows
+    assert b"INT32_MAX" in lib.lcda_last_error()
     assert call(groups=0, x=None, R=None, codes=None) == 0   # nothing to do
 
 
